@@ -1,0 +1,210 @@
+"""Pins for the oracle's GEMMs, SiLU*up, scatter, fold and whole layer (CPU only).
+
+Pinned by a float64 triple loop over operands decoded nibble by nibble from
+their bits, the dense-FFN special case (one expert, top-1, weight 1), the
+pages' gate/up split, the fold's identity and error bound, and the layer
+cosine of the pages' layer test.
+"""
+import numpy as np
+import pytest
+
+import oracle as O
+import workloads as W
+
+E2M1 = [0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0]
+
+
+def _decode_bits_loop(q, sf):
+    """Decode packed E2M1 x E4M3 element by element from the bit patterns."""
+    R, Kh = q.shape
+    out = np.zeros((R, 2 * Kh))
+    for r in range(R):
+        for kk in range(2 * Kh):
+            byte = int(q[r, kk // 2])
+            nib = (byte >> 4) if kk % 2 else (byte & 0xF)
+            mag = E2M1[nib & 7] * (-1.0 if nib & 8 else 1.0)
+            c = int(sf[r, kk // 16])
+            e, m = (c >> 3) & 0xF, c & 7
+            s = (m / 8.0) * 2.0 ** -6 if e == 0 else (1 + m / 8.0) * 2.0 ** (e - 7)
+            out[r, kk] = mag * s
+    return out
+
+
+def test_grouped_gemm_brute_force():
+    rng = np.random.default_rng(0)
+    L, N, K, T = 3, 8, 64, 10
+    a_q, a_sf = W.random_fp4_operands(1, T, K)
+    b_q, b_sf = W.random_fp4_operands(2, L * N, K)
+    b_q, b_sf = b_q.reshape(L, N, K // 2), b_sf.reshape(L, N, K // 16)
+    counts = np.array([4, 0, 9])
+    offsets = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    row_index = rng.integers(0, T, counts.sum()).astype(np.int32)
+    a_gs = np.float32(0.37)
+    b_gs = np.array([1.5, 2.0, 0.01], np.float32)
+    got = O.grouped_gemm(a_q, a_sf, row_index, a_gs, b_q, b_sf, b_gs, offsets)
+    A = _decode_bits_loop(a_q, a_sf)
+    want = np.zeros_like(got, dtype=np.float64)
+    for e in range(L):
+        Bm = _decode_bits_loop(b_q[e], b_sf[e])
+        for s in range(offsets[e], offsets[e + 1]):
+            for n in range(N):
+                acc = 0.0
+                for kk in range(K):
+                    acc += A[row_index[s], kk] * Bm[n, kk]
+                want[s, n] = float(np.float32(a_gs) * np.float32(b_gs[e])) * acc
+    scale = np.abs(want).max()
+    assert np.max(np.abs(got - want)) <= 1e-5 * scale
+    # without a row index, rows are read in slot order
+    got2 = O.grouped_gemm(a_q, a_sf, None, a_gs, b_q, b_sf, b_gs, np.array([0, 2, 2, 5], np.int32))
+    assert np.allclose(got2[0], (A[0] @ _decode_bits_loop(b_q[0], b_sf[0]).T) * float(a_gs * b_gs[0]),
+                       rtol=1e-5, atol=1e-6 * scale)
+
+
+def test_scatter_brute_force():
+    rng = np.random.default_rng(1)
+    T, k, H, S = 7, 3, 16, 9
+    y = W.bf16_bits(rng.standard_normal((S, H)).astype(np.float32))
+    ts = np.full(T * k, -1, np.int32)
+    ts[rng.choice(T * k, S, replace=False)] = rng.permutation(S)
+    w = rng.random((T, k)).astype(np.float32)
+    got = O.bf16_to_f32(O.scatter(y, ts, w))
+    Y = O.bf16_to_f64(y)
+    for t in range(T):
+        acc = np.zeros(H)
+        for j in range(k):
+            s = ts[t * k + j]
+            if s >= 0:
+                acc += float(w[t, j]) * Y[s]
+        assert np.allclose(got[t], acc, rtol=2 ** -7, atol=0)
+    assert not got[[t for t in range(T) if (ts[t * k:(t + 1) * k] < 0).all()]].any()
+
+
+def _layer(cfg_name):
+    cfg = W.get_config(cfg_name)
+    ids, w = W.make_router(cfg)
+    x = W.make_activations(cfg)
+    wg, wu, wd = W.make_weights(cfg)
+    return cfg, ids, w, x, wg, wu, wd
+
+
+def test_dense_ffn_special_case():
+    # one expert, top-1, weight 1: the layer is a dense SwiGLU FFN on the
+    # quantized operands
+    rng = np.random.default_rng(2)
+    T, H, I = 24, 128, 64
+    x = W.bf16_bits(rng.standard_normal((T, H)).astype(np.float32))
+    wg = W.bf16_bits(rng.standard_normal((1, I, H)).astype(np.float32) * 0.05)
+    wu = W.bf16_bits(rng.standard_normal((1, I, H)).astype(np.float32) * 0.05)
+    wd = W.bf16_bits(rng.standard_normal((1, H, I)).astype(np.float32) * 0.05)
+    ids = np.zeros((T, 1), np.int32)
+    w = np.ones((T, 1), np.float32)
+    P = O.prepare_weights(wg, wu, wd)
+    tr = O.moe_forward(x, ids, w, 0, P)
+    xh = O.dequantize(tr.x_q, tr.x_sf, tr.gs_x)
+    W1 = O.dequantize(P["w1_q"][0], P["w1_sf"][0], P["w1_gs"][0])
+    gate, up = xh @ W1[:I].T, xh @ W1[I:].T
+    h = gate / (1 + np.exp(-gate)) * up
+    assert np.allclose(O.bf16_to_f64(tr.h), h, rtol=2 ** -6, atol=1e-3 * np.abs(h).max())
+    hh = O.dequantize(tr.h_q, tr.h_sf, tr.gs_h)
+    y = hh @ O.dequantize(P["w2_q"][0], P["w2_sf"][0], P["w2_gs"][0]).T
+    out = O.bf16_to_f64(tr.out)
+    assert np.max(np.abs(out - y)) <= 1e-2 * np.abs(y).max()
+    assert np.array_equal(tr.routing["slot_token"], np.arange(T))
+
+
+def test_gate_up_split_at_intermediate_size():
+    # pages (intermediate-split commit): gate = L1 out[:, :I], up = L1 out[:, I:]
+    cfg, ids, w, x, wg, wu, wd = _layer("tiny")
+    zero = np.zeros_like(wu)
+    for args in ((wg, zero, wd), (zero, wu, wd)):
+        tr = O.moe_forward(x, ids, w, cfg.expert_start, O.prepare_weights(*args))
+        assert not O.bf16_to_f32(tr.out).any()
+        assert not O.bf16_to_f32(tr.h).any()
+    base = O.moe_forward(x, ids, w, cfg.expert_start, O.prepare_weights(wg, wu, wd))
+    # with gate pre-activations of order 5, silu(g)*u and silu(u)*g differ clearly
+    big = lambda a: W.bf16_bits(O.bf16_to_f32(a) * np.float32(20.0))
+    b1 = O.moe_forward(x, ids, w, cfg.expert_start, O.prepare_weights(big(wg), big(wu), wd))
+    b2 = O.moe_forward(x, ids, w, cfg.expert_start, O.prepare_weights(big(wu), big(wg), wd))
+    assert O.cosine(O.bf16_to_f32(b1.out), O.bf16_to_f32(b2.out)) < 0.8
+    # the split follows the intermediate size: h has I columns
+    assert base.h.shape == (base.routing["S"], cfg.inter)
+
+
+def test_fold_identity_and_error_bound():
+    rng = np.random.default_rng(4)
+    L, I, K = 4, 32, 64
+    sf = rng.integers(0, 0x7F, (L, 2 * I, K // 16)).astype(np.uint8)
+    g = np.array([1.0, 0.5, 3e-4, 2.0], np.float32)
+    u = np.array([1.0, 0.7, 9e-3, 0.06], np.float32)
+    out, gs1 = O.fold_gate_up(sf, g, u, I)
+    assert np.array_equal(gs1, np.maximum(g, u))
+    assert np.array_equal(out[0], sf[0])                    # equal scales: unchanged
+    for e in range(L):
+        for lo, hi, gp in ((0, I, g[e]), (I, 2 * I, u[e])):
+            if gp == gs1[e]:
+                assert np.array_equal(out[e, lo:hi], sf[e, lo:hi])
+                continue
+            before = O.e4m3_decode(sf[e, lo:hi]) * float(gp)
+            after = O.e4m3_decode(out[e, lo:hi]) * float(gs1[e])
+            # within half an E4M3 step of the folded value (plus float32 rounding)
+            c = out[e, lo:hi].astype(int)
+            up_ = O.e4m3_decode(np.minimum(c + 1, 0x7E).astype(np.uint8))
+            dn_ = O.e4m3_decode(np.maximum(c - 1, 0).astype(np.uint8))
+            half = np.maximum(up_ - O.e4m3_decode(out[e, lo:hi]), O.e4m3_decode(out[e, lo:hi]) - dn_) / 2
+            assert np.all(np.abs(after - before) <= (half * 1.0001 + 2 ** -30) * float(gs1[e]))
+
+
+def test_fold_targets_the_smaller_scale_half():
+    cfg, ids, w, x, wg, wu, wd = _layer("mid_skew")
+    P = O.prepare_weights(wg, wu, wd)
+    assert np.all(P["gs_up"] > 20 * P["gs_gate"])          # W_up is 30x larger
+    I = cfg.inter
+    for e in range(2):
+        gq, gsf, _ = O.quantize(wg[e])
+        uq, usf, _ = O.quantize(wu[e])
+        assert np.array_equal(P["w1_sf"][e, I:], usf)      # larger-gs half untouched
+        assert not np.array_equal(P["w1_sf"][e, :I], gsf)  # gate scales folded
+        deq = O.dequantize(P["w1_q"][e, :I], P["w1_sf"][e, :I], P["w1_gs"][e])
+        assert O.cosine(deq, O.bf16_to_f64(wg[e])) > 0.99
+
+
+@pytest.mark.parametrize("name", ["tiny", "mid", "mid_skew"])
+def test_layer_cosine(name):
+    # pages (layer-test commits): the full NVFP4 pipeline against a BF16 layer whose
+    # weights are the NVFP4 weights dequantized to BF16 reaches cosine 0.989-0.995.
+    cfg, ids, w, x, wg, wu, wd = _layer(name)
+    P = O.prepare_weights(wg, wu, wd)
+    tr = O.moe_forward(x, ids, w, cfg.expert_start, P)
+    out = O.bf16_to_f32(tr.out)
+    L, I = cfg.num_local, cfg.inter
+
+    def deq_bf16(q, sf, gs):
+        return O.f32_to_bf16(O.dequantize(q, sf, gs, np.float32))
+    dg = np.stack([deq_bf16(P["w1_q"][e, :I], P["w1_sf"][e, :I], P["w1_gs"][e]) for e in range(L)])
+    du = np.stack([deq_bf16(P["w1_q"][e, I:], P["w1_sf"][e, I:], P["w1_gs"][e]) for e in range(L)])
+    dd = np.stack([deq_bf16(P["w2_q"][e], P["w2_sf"][e], P["w2_gs"][e]) for e in range(L)])
+    ref_deq = O.bf16_reference_layer(x, ids, w, cfg.expert_start, dg, du, dd)
+    assert O.cosine(out, ref_deq) >= 0.98
+    # against the original BF16 weights the four FP4 roundings (x, W1, h, W2;
+    # ~9.5% RMS each on Gaussian data) cap the cosine near 0.973
+    ref = O.bf16_reference_layer(x, ids, w, cfg.expert_start, wg, wu, wd)
+    assert 0.96 <= O.cosine(out, ref) < 0.99
+
+
+def test_bf16_reference_layer_dense_case():
+    # the cosine reference itself: one expert, top-1, weight 0.5 -> 0.5 * SwiGLU FFN
+    rng = np.random.default_rng(8)
+    T, H, I = 12, 64, 32
+    x = W.bf16_bits(rng.standard_normal((T, H)).astype(np.float32))
+    wg, wu = (W.bf16_bits(rng.standard_normal((1, I, H)).astype(np.float32) * 0.2) for _ in range(2))
+    wd = W.bf16_bits(rng.standard_normal((1, H, I)).astype(np.float32) * 0.2)
+    ids = np.full((T, 1), 5, np.int32)
+    w = np.full((T, 1), 0.5, np.float32)
+    got = O.bf16_reference_layer(x, ids, w, 5, wg, wu, wd)
+    X = O.bf16_to_f64(x)
+    g = X @ O.bf16_to_f64(wg[0]).T
+    u = X @ O.bf16_to_f64(wu[0]).T
+    want = 0.5 * ((g / (1 + np.exp(-g)) * u) @ O.bf16_to_f64(wd[0]).T)
+    assert np.allclose(got, want, rtol=1e-4, atol=1e-5 * np.abs(want).max())
+    # ids outside the local range contribute nothing
+    assert not O.bf16_reference_layer(x, ids, w, 6, wg, wu, wd).any()
