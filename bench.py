@@ -1,0 +1,218 @@
+"""Benchmark of the NVFP4 MoE expert-FFN layer on one MI355X.
+
+One step = one full layer forward (quantize x, route, L1 grouped GEMM with the
+SiLU*up epilogue, re-quantize h, L2 grouped GEMM, weighted scatter) over one
+batch of synthetic input already resident in HBM.
+
+Default workload: the prefill-shaped shard (8192 tokens, top-8 of 384 experts,
+this GPU's 48 local experts 96..143, hidden 7168, intermediate 3072, uniform
+router logits). The decode-shaped shard (64 tokens, same weights) is measured
+alongside. Prints one JSON line.
+
+    python bench.py [--steps K] [--warmup W] [--gpus 1] [--config prefill|decode|skewed]
+                    [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+from concurrent.futures import ThreadPoolExecutor
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "MoE layer tokens/s + grouped-GEMM TFLOPS & HBM GB/s (% of roofline), 1 GPU"
+PEAK_FP16_TFLOPS = 2500.0     # MI355X dense fp16/bf16 MFMA
+PEAK_FP4_TFLOPS = 10100.0     # MI355X dense fp4 MFMA (not usable for block-16 E4M3 scales)
+PEAK_HBM_GBS = 8000.0
+PROFILE_DIR = os.path.join(ROOT, "profiles")
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def kernel_source_sha() -> str:
+    p = os.path.join(ROOT, "nvfp4_quantized_moe_amd", "csrc", "grouped_gemm.hip")
+    return hashlib.sha256(open(p, "rb").read()).hexdigest()[:16]
+
+
+def read_traffic(workload: str):
+    """Per-launch HBM bytes of the L1 GEMM from the committed counter summary,
+    or None when absent or taken on a different kernel source."""
+    p = os.path.join(PROFILE_DIR, f"l1_gemm_{workload}_traffic.txt")
+    if not os.path.exists(p):
+        return None
+    kv = {}
+    for line in open(p):
+        if "=" in line and not line.lstrip().startswith("#"):
+            k, v = line.split("=", 1)
+            kv[k.strip()] = v.strip()
+    if kv.get("kernel_source_sha") != kernel_source_sha():
+        return None
+    return float(kv["hbm_bytes_per_launch"])
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--config", default="prefill", choices=["prefill", "decode", "skewed"])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-decode", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU; --gpus {args.gpus} is not supported "
+              f"(expert-parallel sharding across GPUs is described in DESIGN.md, not built)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import nvfp4_quantized_moe_amd as nv
+    import workloads as W
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    cfg = W.get_config(args.config)
+    t0 = time.time()
+    ids, w = W.make_router(cfg)
+    x = W.make_activations(cfg)
+    wg, wu, wd = W.make_weights(cfg)
+    log(f"generated {cfg.name} inputs in {time.time() - t0:.1f}s")
+
+    def bf16(a):
+        return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev)
+
+    weights = nv.prepare_weights(bf16(wg), bf16(wu), bf16(wd))
+    torch.cuda.synchronize()
+
+    def run_layer(cfg_, ids_, w_, x_, steps, warmup):
+        T, k = ids_.shape
+        d_x, d_ids, d_w = bf16(x_), torch.from_numpy(ids_).to(dev), torch.from_numpy(w_).to(dev)
+        out = torch.empty((T, cfg_.hidden), dtype=torch.bfloat16, device=dev)
+        lay = nv.nvfp4_moe_ws_layout(T, k, cfg_.hidden, cfg_.inter, cfg_.num_local)
+        ws = torch.empty(lay["end"], dtype=torch.uint8, device=dev)
+
+        def step():
+            nv.nvfp4_moe_forward(weights, d_x, d_ids, d_w, cfg_.expert_start, out=out, ws=ws)
+
+        for _ in range(warmup):
+            step()
+        torch.cuda.synchronize()
+        t = time.perf_counter()
+        for _ in range(steps):
+            step()
+        torch.cuda.synchronize()
+        ms = (time.perf_counter() - t) * 1e3 / steps
+        # the dominant kernel, L1 grouped GEMM, timed alone on the stream it is launched on
+        cap = T * k
+        S = int(nv.ws_view(ws, lay, "offsets", torch.int32, (cfg_.num_local + 1,))[-1].item())
+        counts = nv.ws_view(ws, lay, "counts", torch.int32, (cfg_.num_local,)).cpu().numpy()
+        tile_m = nv.nvfp4_moe_tile_m(T, k, cfg_.num_local)
+        gargs = (nv.ws_view(ws, lay, "x_q", torch.uint8, (T, cfg_.hidden // 2)),
+                 nv.ws_view(ws, lay, "x_sf", torch.uint8, (T, cfg_.hidden // 16)),
+                 nv.ws_view(ws, lay, "slot_token", torch.int32, (cap,)),
+                 nv.ws_view(ws, lay, "scalars", torch.float32, (4,))[0:1],
+                 weights.w1_q, weights.w1_sf, weights.w1_gs,
+                 nv.ws_view(ws, lay, "offsets", torch.int32, (cfg_.num_local + 1,)),
+                 nv.ws_view(ws, lay, "tiles", torch.int32, (nv.nvfp4_tile_table_len(cap, cfg_.num_local, tile_m),)))
+        h = torch.empty((cap, cfg_.inter), dtype=torch.bfloat16, device=dev)
+        amax = torch.zeros(1, dtype=torch.float32, device=dev)
+        stream = torch.cuda.current_stream()
+        ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        n_l1 = max(steps, 5)
+        for _ in range(2):
+            nv.nvfp4_grouped_gemm(*gargs, cap, tile_m, nv.EPI_SILU_MUL, d=h, amax_out=amax)
+        ev0.record(stream)
+        for _ in range(n_l1):
+            nv.nvfp4_grouped_gemm(*gargs, cap, tile_m, nv.EPI_SILU_MUL, d=h, amax_out=amax)
+        ev1.record(stream)
+        torch.cuda.synchronize()
+        l1_ms = ev0.elapsed_time(ev1) / n_l1
+        return dict(ms=ms, S=S, touched=int((counts > 0).sum()), l1_ms=l1_ms, tile_m=tile_m, out=out)
+
+    log(f"timing {cfg.name}: {args.warmup} warmup + {args.steps} steps")
+    r = run_layer(cfg, ids, w, x, args.steps, args.warmup)
+    T, k, H, I = cfg.tokens, cfg.top_k, cfg.hidden, cfg.inter
+    S = r["S"]
+    tok_s = T / (r["ms"] * 1e-3)
+    l1_flop = S * 2.0 * (2 * I) * H                       # per slot: 2 * 2I * H (88.08 MFLOP)
+    layer_flop = S * 2.0 * (2 * I * H + H * I)            # per slot: 132.12 MFLOP
+    l1_tflops = l1_flop / (r["l1_ms"] * 1e-3) / 1e12
+    l1_w_bytes = r["touched"] * 2 * I * (H // 2 + H // 16)  # FP4 weights + scales of touched experts
+    traffic = read_traffic(cfg.name)
+    roofline = {
+        "kernel": "grouped_gemm L1 (gate+up, SiLU*up epilogue)",
+        "bound": "mfma", "achieved": round(l1_tflops, 2), "peak": PEAK_FP16_TFLOPS, "unit": "TFLOP/s",
+        "frac": round(l1_tflops / PEAK_FP16_TFLOPS, 4), "traffic": traffic,
+        "avg_launch_ms": round(r["l1_ms"], 4), "flop_per_launch": l1_flop,
+        "frac_of_fp4_peak": round(l1_tflops / PEAK_FP4_TFLOPS, 4),
+    }
+    if cfg.name == "decode":
+        gbs = l1_w_bytes / (r["l1_ms"] * 1e-3) / 1e9
+        roofline.update(bound="hbm", achieved=round(gbs, 1), peak=PEAK_HBM_GBS, unit="GB/s",
+                        frac=round(gbs / PEAK_HBM_GBS, 4), bytes_per_launch=l1_w_bytes)
+    result = {
+        "metric": METRIC, "value": round(tok_s, 1), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(r["ms"], 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "fp16", "data": "synthetic (seeded NumPy draws, random-init weights)",
+        "config": {"workload": f"{cfg.name} shard: T={T}, top-{k} of {cfg.num_global} experts, local "
+                               f"{cfg.expert_start}..{cfg.expert_start + cfg.num_local - 1}, H={H}, I={I}",
+                   "tokens": T, "top_k": k, "local_experts": cfg.num_local, "hidden": H, "inter": I,
+                   "slots": S, "touched_experts": r["touched"], "tile_m": r["tile_m"]},
+        "layer_tflops": round(layer_flop / (r["ms"] * 1e-3) / 1e12, 2),
+        "roofline": roofline,
+    }
+    if cfg.name == "prefill" and not args.no_decode:
+        dcfg = W.get_config("decode")
+        dids, dw = W.make_router(dcfg)
+        dx = W.make_activations(dcfg)
+        rd = run_layer(dcfg, dids, dw, dx, max(args.steps, 50), args.warmup)
+        bytes_w = rd["touched"] * (2 * I * (H // 2 + H // 16) + H * (I // 2 + I // 16))
+        gbs = bytes_w / (rd["ms"] * 1e-3) / 1e9
+        l1b = rd["touched"] * 2 * I * (H // 2 + H // 16)
+        l1g = l1b / (rd["l1_ms"] * 1e-3) / 1e9
+        result["decode"] = {
+            "workload": "decode shard: T=64, top-8 of 384, local 96..143, same weights",
+            "tokens_per_s": round(dcfg.tokens / (rd["ms"] * 1e-3), 1), "ms_per_step": round(rd["ms"], 4),
+            "touched_experts": rd["touched"], "slots": rd["S"],
+            "layer_weight_GBs": round(gbs, 1), "layer_hbm_frac": round(gbs / PEAK_HBM_GBS, 4),
+            "l1_gemm_ms": round(rd["l1_ms"], 4), "l1_gemm_GBs": round(l1g, 1),
+            "l1_gemm_hbm_frac": round(l1g / PEAK_HBM_GBS, 4),
+        }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(cfg, ids, w, x, wg, wu, wd, T)
+    print(json.dumps(result), flush=True)
+
+
+def cpu_baseline(cfg, ids, w, x, wg, wu, wd, T):
+    """The CPU oracle timed on a bounded sample of the same workload: the
+    first n tokens (all of their local slots) through a1..a8. Weight
+    preparation (offline) is not timed."""
+    import oracle as O
+    n = min(T, int(os.environ.get("NVFP4_BENCH_ORACLE_TOKENS", "1024")))
+    cores = len(os.sched_getaffinity(0))
+    threads = min(16, cores)
+    t0 = time.time()
+    with ThreadPoolExecutor(max_workers=threads) as ex:
+        P = O.prepare_weights(wg, wu, wd, map_fn=ex.map)
+    log(f"oracle weight preparation (untimed) {time.time() - t0:.1f}s")
+    t = time.perf_counter()
+    with ThreadPoolExecutor(max_workers=threads) as ex:
+        O.moe_forward(x[:n], ids[:n], w[:n], cfg.expert_start, P, map_fn=ex.map)
+    dt = time.perf_counter() - t
+    log(f"oracle forward on {n} tokens: {dt:.1f}s")
+    return {"value": round(n / dt, 2), "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"first {n} of {T} tokens of the {cfg.name} shard (all their local slots), "
+                      f"steps a1-a8; experts on {threads} threads, BLAS threads inside each; "
+                      f"{cores} host cores visible; {dt:.1f}s"}
+
+
+if __name__ == "__main__":
+    main()

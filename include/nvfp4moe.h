@@ -1,0 +1,213 @@
+/*
+ * nvfp4moe — NVFP4 mixture-of-experts expert FFN on AMD Instinct MI355X (gfx950).
+ *
+ * C ABI of libnvfp4moe.so. The layer runs in six steps (tests history of the
+ * nvfp4-megamoe-kernel project, moe_pipeline commit): quantize the BF16
+ * activation to NVFP4; L1 grouped GEMM (gate+up); SiLU(gate)*up, re-quantized;
+ * L2 grouped GEMM (down_proj); weighted scatter back to token rows.
+ *
+ * NVFP4 storage used throughout:
+ *   - values: E2M1 nibbles, bit 3 = sign, bits 2:0 index {0,0.5,1,1.5,2,3,4,6};
+ *     two per byte along K, element 2j in the low nibble of byte j;
+ *     a [rows, K] tensor is stored as uint8 [rows, K/2], row-major;
+ *   - block scales: one E4M3 (float8_e4m3fn) bit pattern per 16 consecutive
+ *     K elements, uint8 [rows, K/16], row-major, never negative, at most 448;
+ *   - global scale: float32 gs = amax / 2688 (= 6 * 448) per tensor;
+ *     value = E2M1(nibble) * E4M3(scale) * gs.
+ * BF16 tensors are passed as raw 16-bit patterns (void*).
+ *
+ * Conventions for every entry point:
+ *   - Pointers are device pointers unless marked (host). The caller owns all
+ *     memory; the library never allocates, frees, caches or keeps state, and
+ *     reads no environment variables.
+ *   - Calls are asynchronous on `stream` (a hipStream_t; NULL = the default
+ *     stream) and never synchronize with the host.
+ *   - Arguments are validated on the host before anything is launched; a
+ *     rejected call returns a nonzero status and launches nothing. A launch
+ *     failure returns NVFP4_ERR_HIP (the error is taken with hipGetLastError,
+ *     without synchronizing).
+ *   - Data-dependent conditions are not errors: expert ids outside this
+ *     rank's range are dropped, and zero local slots give a zero output.
+ *   - Device pointers must be 16-byte aligned; floating-point inputs finite.
+ *   - Calls that share no output buffers may run concurrently.
+ */
+#ifndef NVFP4MOE_H
+#define NVFP4MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  NVFP4_OK = 0,
+  NVFP4_ERR_NULL = 1,       /* a required pointer is NULL */
+  NVFP4_ERR_SHAPE = 2,      /* a size is negative, zero where it must not be, or not a multiple it must be */
+  NVFP4_ERR_ALIGN = 3,      /* a device pointer is not 16-byte aligned */
+  NVFP4_ERR_WORKSPACE = 4,  /* workspace smaller than the matching *_ws_bytes() */
+  NVFP4_ERR_HIP = 5,        /* a kernel launch failed */
+  NVFP4_ERR_ARG = 6         /* an enum or option value is unknown */
+} nvfp4_status;
+
+/* Static description of a status code (host). */
+const char* nvfp4_status_string(int status);
+
+/* Library version as major*10000 + minor*100 + patch (host). */
+int nvfp4moe_version(void);
+
+/* ---------------------------------------------------------------- quantize
+ * Activation/weight quantizer (nvfp4_mega_moe.py history: overflow-fix commit,
+ * alpha commit and three-quantizer-bugs commit; tests history: packing along K).
+ *
+ * x_bf16 holds B independent tensors, each [M, K] BF16 row-major
+ * (B*M*K elements). Tensor b gets its own global scale:
+ *   amax_b = max |x_b|   (or amax_in[b] when amax_in != NULL)
+ *   gs_b   = RN_f32(amax_b / 2688)                         -> gs_out[b]
+ * and for every row and 16-element block with bmax = max |x| in the block:
+ *   sf     = nearest E4M3 to bmax / (6 gs_b), ties to even, saturating at 448
+ *   nibble = sign bit of x | nearest E2M1 magnitude index of |x| / (E4M3(sf) gs_b),
+ *            ties to the even index, saturating at 6; magnitude 0 where sf == 0
+ * Both roundings are decided exactly (as on the real quotient). amax == 0 gives
+ * gs = 0, sf = 0 and magnitude 0.
+ *   q  : uint8 [B, M, K/2]    sf : uint8 [B, M, K/16]    gs_out : float [B]
+ *   amax_in : float [B] or NULL (device; the h path passes the L1 epilogue's amax)
+ *   ws : scratch of at least nvfp4_quantize_ws_bytes(B, M, K) bytes
+ * Requires B >= 1, M >= 0, K > 0, K % 32 == 0.
+ */
+size_t nvfp4_quantize_ws_bytes(int64_t B, int64_t M, int64_t K);
+int nvfp4_quantize(const void* x_bf16, int64_t B, int64_t M, int64_t K, const float* amax_in,
+                   uint8_t* q, uint8_t* sf, float* gs_out, void* ws, size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------------- route
+ * Slot routing for one rank's share of experts (nvfp4_mega_moe.py history:
+ * local-expert-id commit; src history: one 1-D slot order for both GEMMs;
+ * nvfp4_cutedsl.py history: bincount/cumsum int32 offsets and sort by expert).
+ *
+ * topk_ids int32 [T, k] are global expert ids; local = id - expert_start is
+ * kept when 0 <= local < num_local and dropped otherwise. S = number of kept
+ * (t, j) pairs. Slots are ordered by (local expert, t*k + j):
+ *   counts      int32 [num_local]     kept pairs per local expert
+ *   offsets     int32 [num_local + 1] exclusive prefix sum; offsets[num_local] = S
+ *   slot_token  int32 [T*k]  token of slot s, -1 for s >= S
+ *   slot_expert int32 [T*k]  local expert of slot s, -1 for s >= S
+ *   slot_weight float [T*k]  topk_w of slot s, 0 for s >= S
+ *   token_slot  int32 [T*k]  slot of pair t*k + j, -1 when dropped
+ *   tile_table  int32 [nvfp4_tile_table_len(T*k, num_local, tile_m)]
+ *               [0] = n tiles; then n pairs (expert, first slot): expert e
+ *               contributes ceil(counts[e] / tile_m) tiles starting at
+ *               offsets[e], offsets[e] + tile_m, ... in expert order.
+ * ws: at least moe_route_ws_bytes(T, k, num_local) bytes.
+ * Requires T >= 0, 1 <= k <= 64, 1 <= num_local <= 4096, tile_m in {16, 32, 64, 128, 256},
+ * T*k < 2^30.
+ */
+size_t moe_route_ws_bytes(int32_t T, int32_t k, int32_t num_local);
+int64_t nvfp4_tile_table_len(int64_t slot_capacity, int32_t num_local, int32_t tile_m);
+int moe_route_slots(const int32_t* topk_ids, const float* topk_w, int32_t T, int32_t k,
+                    int32_t expert_start, int32_t num_local, int32_t tile_m,
+                    int32_t* counts, int32_t* offsets, int32_t* slot_token, int32_t* slot_expert,
+                    float* slot_weight, int32_t* token_slot, int32_t* tile_table,
+                    void* ws, size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------ grouped GEMM
+ * NVFP4 x NVFP4 grouped GEMM over slot rows (nvfp4_mega_moe.py history: alpha
+ * commit; src history: 1-D slot ids, gather only for L1; tests history:
+ * [expert0 | expert1 | ...] row layout for the 2-D x 3-D grouped GEMM).
+ *
+ * For every tile (e, r0) of tile_table and every slot row s in
+ * [r0, min(r0 + tile_m, offsets[e+1])):
+ *   a = a_row_index ? a_row_index[s] : s          (L1 gathers token rows)
+ *   G[s, n] = alpha_e * sum_k A_hat[a, k] * W_hat_e[n, k],  alpha_e = RN_f32(a_gs[0] * b_gs[e])
+ * with A_hat, W_hat the exact dequantized values without global scale and the
+ * sum in float32.
+ *   a_q uint8 [*, K/2], a_sf uint8 [*, K/16]; b_q uint8 [L, N, K/2]; b_sf uint8 [L, N, K/16];
+ *   a_gs float [1]; b_gs float [L]; offsets int32 [L+1]; tile_table as from moe_route_slots
+ *   with the same tile_m; rows_cap = capacity of the row arrays (tile_table holds at
+ *   most nvfp4_tile_table_len(rows_cap, L, tile_m) entries).
+ * epilogue NVFP4_EPI_BF16:        d = BF16 [rows_cap, N], d[s, n] = RN_bf16(G[s, n]).
+ * epilogue NVFP4_EPI_SILU_MUL:    N = 2*I (gate rows [0, I), up rows [I, 2I) of b;
+ *   nvfp4_cutedsl.py history, intermediate-split commit), d = BF16 [rows_cap, I],
+ *   g = RN_bf16(G[s, n]), u = RN_bf16(G[s, I + n]), d[s, n] = RN_bf16(silu(g) * u)
+ *   with silu(g) = g / (1 + exp(-g)) in float32; amax_out[0] is raised (atomic max)
+ *   to max |d| over the rows written, so the caller sets it to 0 first.
+ * Only rows of listed tiles are written. Requires K % 128 == 0, N % 64 == 0
+ * (N % 128 == 0 for NVFP4_EPI_SILU_MUL), 1 <= L, tile_m 32 (decode-shaped
+ * batches) or 128 (prefill-shaped).
+ */
+enum { NVFP4_EPI_BF16 = 0, NVFP4_EPI_SILU_MUL = 1 };
+int nvfp4_grouped_gemm(const uint8_t* a_q, const uint8_t* a_sf, const int32_t* a_row_index,
+                       const float* a_gs, const uint8_t* b_q, const uint8_t* b_sf, const float* b_gs,
+                       const int32_t* offsets, const int32_t* tile_table, int32_t num_local,
+                       int32_t rows_cap, int32_t N, int32_t K, int32_t tile_m, int32_t epilogue,
+                       void* d, float* amax_out, void* stream);
+
+/* ------------------------------------------------------- weighted scatter
+ * out[t, :] = RN_bf16( sum over j = 0..k-1 with token_slot[t*k+j] >= 0 of
+ *                      topk_w[t, j] * y[token_slot[t*k+j], :] ), float32, increasing j;
+ * 0 for tokens with no local pair (nvfp4_cutedsl.py history: scatter with routing
+ * weights; made order-fixed). y BF16 [*, H]; out BF16 [T, H]; H % 8 == 0.
+ */
+int moe_weighted_scatter(const void* y_bf16, const int32_t* token_slot, const float* topk_w,
+                         int32_t T, int32_t k, int32_t H, void* out_bf16, void* stream);
+
+/* ---------------------------------------------------------- scale folding
+ * Offline weight preparation (nvfp4_cutedsl.py history, finalize_weights commit):
+ * gate and up carry their own global scales; both are brought to
+ * gs1[e] = max(gs_gate[e], gs_up[e]) by rewriting the block scales of the half
+ * with the smaller scale: ratio = RN_f32(gs_p / gs1), sf' = E4M3 nearest-even,
+ * saturating, of RN_f32(E4M3(sf) * ratio). Equal scales leave sf unchanged.
+ *   w1_sf uint8 [L, 2I, K/16] in place; gs_gate, gs_up float [L]; gs1 float [L] out.
+ */
+int nvfp4_fold_scales(uint8_t* w1_sf, const float* gs_gate, const float* gs_up, float* gs1,
+                      int32_t num_local, int32_t inter, int32_t K, void* stream);
+
+/* ------------------------------------------------------------ whole layer
+ * One rank's share of the MoE expert FFN (nvfp4_mega_moe.py history:
+ * expert-parallel note — the layer writes a local partial output and the
+ * caller reduces across ranks). Steps, all on `stream`, no host sync:
+ *   quantize x (own gs) -> route -> L1 grouped GEMM with the SiLU*up epilogue
+ *   (alpha = gs_x * w1_gs[e]) -> re-quantize h (gs_h from the epilogue's amax)
+ *   -> L2 grouped GEMM (alpha = gs_h * w2_gs[e]) -> weighted scatter.
+ * Weights (host struct of device pointers), L = num_local:
+ *   w1_q [L, 2I, H/2], w1_sf [L, 2I, H/16], w1_gs [L]   gate rows [0,I), up rows [I,2I),
+ *                                                         gate/up scales folded to one gs
+ *   w2_q [L, H, I/2],  w2_sf [L, H, I/16],  w2_gs [L]
+ * x_bf16 [T, H]; topk_ids int32 [T, k] global ids; topk_w float [T, k];
+ * out_bf16 [T, H] (tokens with no local expert get zeros).
+ * ws: at least nvfp4_moe_ws_bytes(...) bytes; its regions (nvfp4_moe_ws_layout)
+ * hold the intermediates after the call. Requires H % 128 == 0, I % 64 == 0.
+ */
+typedef struct {
+  int32_t num_local, hidden, inter;
+  const uint8_t* w1_q;
+  const uint8_t* w1_sf;
+  const float* w1_gs;
+  const uint8_t* w2_q;
+  const uint8_t* w2_sf;
+  const float* w2_gs;
+} nvfp4_moe_weights;
+
+enum {
+  NVFP4_WS_X_Q = 0, NVFP4_WS_X_SF, NVFP4_WS_SCALARS, NVFP4_WS_COUNTS, NVFP4_WS_OFFSETS,
+  NVFP4_WS_SLOT_TOKEN, NVFP4_WS_SLOT_EXPERT, NVFP4_WS_SLOT_WEIGHT, NVFP4_WS_TOKEN_SLOT,
+  NVFP4_WS_TILES, NVFP4_WS_ROUTE_SCRATCH, NVFP4_WS_H, NVFP4_WS_H_Q, NVFP4_WS_H_SF, NVFP4_WS_Y,
+  NVFP4_WS_QUANT_SCRATCH, NVFP4_WS_END, NVFP4_WS_NREGIONS
+};
+/* Scalars region (float[4]): [0] gs_x, [1] amax_h, [2] gs_h, [3] reserved. */
+
+/* Byte offset of every workspace region (host array of NVFP4_WS_NREGIONS entries;
+ * entry NVFP4_WS_END is the total size). Returns the total size. */
+size_t nvfp4_moe_ws_layout(int32_t T, int32_t k, int32_t hidden, int32_t inter, int32_t num_local,
+                           int32_t tile_m, size_t* offsets_out);
+size_t nvfp4_moe_ws_bytes(int32_t T, int32_t k, int32_t hidden, int32_t inter, int32_t num_local);
+/* GEMM row-tile height the layer uses for a given batch (decode- or prefill-shaped). */
+int32_t nvfp4_moe_tile_m(int32_t T, int32_t k, int32_t num_local);
+int nvfp4_moe_forward(const nvfp4_moe_weights* w, const void* x_bf16, int32_t T,
+                      const int32_t* topk_ids, const float* topk_w, int32_t k, int32_t expert_start,
+                      void* out_bf16, void* ws, size_t ws_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* NVFP4MOE_H */

@@ -1,0 +1,264 @@
+"""Python binding of libnvfp4moe.so — NVFP4 MoE expert FFN on MI355X (gfx950).
+
+Argument marshalling only: every step runs in the library's HIP kernels;
+torch provides device memory and the current stream. The functions carry the
+names of the C entry points declared in include/nvfp4moe.h.
+
+Importing this module loads the built library and fails loudly when it is
+missing; there is no CPU fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+__all__ = [
+    "lib", "LIB_PATH", "NVFP4Error", "EPI_BF16", "EPI_SILU_MUL", "WS_REGIONS", "nvfp4_quantize",
+    "nvfp4_quantize_ws_bytes", "moe_route_slots", "moe_route_ws_bytes", "nvfp4_tile_table_len",
+    "nvfp4_grouped_gemm", "moe_weighted_scatter", "nvfp4_fold_scales", "nvfp4_moe_forward",
+    "nvfp4_moe_ws_bytes", "nvfp4_moe_ws_layout", "nvfp4_moe_tile_m", "MoEWeights", "prepare_weights",
+    "ws_view",
+]
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libnvfp4moe.so")
+if not os.path.exists(LIB_PATH):
+    raise ImportError(f"{LIB_PATH} is not built; run `python __graft_entry__.py` (build()) first")
+lib = ctypes.CDLL(LIB_PATH)
+
+EPI_BF16, EPI_SILU_MUL = 0, 1
+WS_REGIONS = ["x_q", "x_sf", "scalars", "counts", "offsets", "slot_token", "slot_expert", "slot_weight",
+              "token_slot", "tiles", "route_scratch", "h", "h_q", "h_sf", "y", "quant_scratch", "end"]
+
+_vp, _i32, _i64, _sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
+
+
+class _Weights(ctypes.Structure):
+    _fields_ = [("num_local", _i32), ("hidden", _i32), ("inter", _i32),
+                ("w1_q", _vp), ("w1_sf", _vp), ("w1_gs", _vp),
+                ("w2_q", _vp), ("w2_sf", _vp), ("w2_gs", _vp)]
+
+
+def _sig(name, res, *args):
+    f = getattr(lib, name)
+    f.restype = res
+    f.argtypes = list(args)
+    return f
+
+
+_status_string = _sig("nvfp4_status_string", ctypes.c_char_p, ctypes.c_int)
+_version = _sig("nvfp4moe_version", ctypes.c_int)
+_quantize_ws = _sig("nvfp4_quantize_ws_bytes", _sz, _i64, _i64, _i64)
+_quantize = _sig("nvfp4_quantize", ctypes.c_int, _vp, _i64, _i64, _i64, _vp, _vp, _vp, _vp, _vp, _sz, _vp)
+_route_ws = _sig("moe_route_ws_bytes", _sz, _i32, _i32, _i32)
+_tile_len = _sig("nvfp4_tile_table_len", _i64, _i64, _i32, _i32)
+_route = _sig("moe_route_slots", ctypes.c_int, _vp, _vp, _i32, _i32, _i32, _i32, _i32,
+              _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp)
+_gemm = _sig("nvfp4_grouped_gemm", ctypes.c_int, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+             _i32, _i32, _i32, _i32, _i32, _i32, _vp, _vp, _vp)
+_scatter = _sig("moe_weighted_scatter", ctypes.c_int, _vp, _vp, _vp, _i32, _i32, _i32, _vp, _vp)
+_fold = _sig("nvfp4_fold_scales", ctypes.c_int, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _vp)
+_moe_ws_layout = _sig("nvfp4_moe_ws_layout", _sz, _i32, _i32, _i32, _i32, _i32, _i32,
+                      ctypes.POINTER(_sz))
+_moe_ws = _sig("nvfp4_moe_ws_bytes", _sz, _i32, _i32, _i32, _i32, _i32)
+_moe_tile_m = _sig("nvfp4_moe_tile_m", _i32, _i32, _i32, _i32)
+_forward = _sig("nvfp4_moe_forward", ctypes.c_int, ctypes.POINTER(_Weights), _vp, _i32, _vp, _vp,
+                _i32, _i32, _vp, _vp, _sz, _vp)
+
+
+class NVFP4Error(RuntimeError):
+    def __init__(self, status: int, call: str):
+        super().__init__(f"{call}: status {status} ({_status_string(status).decode()})")
+        self.status = status
+
+
+def _check(status: int, call: str):
+    if status != 0:
+        raise NVFP4Error(status, call)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream():
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _dev(t, dtype, name):
+    if not (t.is_cuda and t.dtype == dtype and t.is_contiguous()):
+        raise ValueError(f"{name}: expected a contiguous CUDA {dtype} tensor, got {t.dtype} on {t.device}")
+    return t
+
+
+def version() -> int:
+    return _version()
+
+
+def _alloc_ws(nbytes, device):
+    return torch.empty(max(int(nbytes), 256), dtype=torch.uint8, device=device)
+
+
+# ---------------------------------------------------------------------- quantize
+
+def nvfp4_quantize_ws_bytes(B, M, K) -> int:
+    return int(_quantize_ws(B, M, K))
+
+
+def nvfp4_quantize(x, amax_in=None, q=None, sf=None, gs=None, ws=None):
+    """x: BF16 [M, K] or [B, M, K] -> (q uint8 [..., K/2], sf uint8 [..., K/16], gs float32 [B])."""
+    _dev(x, torch.bfloat16, "x")
+    batched = x.dim() == 3
+    B, M, K = (x.shape if batched else (1, *x.shape))
+    dev = x.device
+    q = torch.empty((B, M, K // 2), dtype=torch.uint8, device=dev) if q is None else q
+    sf = torch.empty((B, M, K // 16), dtype=torch.uint8, device=dev) if sf is None else sf
+    gs = torch.empty((B,), dtype=torch.float32, device=dev) if gs is None else gs
+    ws = _alloc_ws(nvfp4_quantize_ws_bytes(B, M, K), dev) if ws is None else ws
+    if amax_in is not None:
+        _dev(amax_in, torch.float32, "amax_in")
+    _check(_quantize(_ptr(x), B, M, K, _ptr(amax_in), _ptr(q), _ptr(sf), _ptr(gs), _ptr(ws),
+                     ws.numel(), _stream()), "nvfp4_quantize")
+    if not batched:
+        return q[0], sf[0], gs
+    return q, sf, gs
+
+
+# ------------------------------------------------------------------------- route
+
+def moe_route_ws_bytes(T, k, num_local) -> int:
+    return int(_route_ws(T, k, num_local))
+
+
+def nvfp4_tile_table_len(cap, num_local, tile_m) -> int:
+    return int(_tile_len(cap, num_local, tile_m))
+
+
+def moe_route_slots(topk_ids, topk_w, expert_start, num_local, tile_m):
+    _dev(topk_ids, torch.int32, "topk_ids")
+    _dev(topk_w, torch.float32, "topk_w")
+    T, k = topk_ids.shape
+    dev = topk_ids.device
+    cap = T * k
+    i32 = dict(dtype=torch.int32, device=dev)
+    out = dict(
+        counts=torch.empty(num_local, **i32), offsets=torch.empty(num_local + 1, **i32),
+        slot_token=torch.empty(cap, **i32), slot_expert=torch.empty(cap, **i32),
+        slot_weight=torch.empty(cap, dtype=torch.float32, device=dev), token_slot=torch.empty(cap, **i32),
+        tile_table=torch.empty(nvfp4_tile_table_len(cap, num_local, tile_m), **i32),
+    )
+    ws = _alloc_ws(moe_route_ws_bytes(T, k, num_local), dev)
+    _check(_route(_ptr(topk_ids), _ptr(topk_w), T, k, expert_start, num_local, tile_m,
+                  _ptr(out["counts"]), _ptr(out["offsets"]), _ptr(out["slot_token"]), _ptr(out["slot_expert"]),
+                  _ptr(out["slot_weight"]), _ptr(out["token_slot"]), _ptr(out["tile_table"]),
+                  _ptr(ws), ws.numel(), _stream()), "moe_route_slots")
+    return out
+
+
+# ------------------------------------------------------------------ grouped GEMM
+
+def nvfp4_grouped_gemm(a_q, a_sf, a_row_index, a_gs, b_q, b_sf, b_gs, offsets, tile_table, rows_cap,
+                       tile_m, epilogue=EPI_BF16, d=None, amax_out=None):
+    L, N, Kh = b_q.shape
+    K = Kh * 2
+    dev = b_q.device
+    n_out = N // 2 if epilogue == EPI_SILU_MUL else N
+    d = torch.empty((rows_cap, n_out), dtype=torch.bfloat16, device=dev) if d is None else d
+    _check(_gemm(_ptr(a_q), _ptr(a_sf), _ptr(a_row_index), _ptr(a_gs), _ptr(b_q), _ptr(b_sf), _ptr(b_gs),
+                 _ptr(offsets), _ptr(tile_table), L, rows_cap, N, K, tile_m, epilogue, _ptr(d), _ptr(amax_out),
+                 _stream()), "nvfp4_grouped_gemm")
+    return d
+
+
+def moe_weighted_scatter(y, token_slot, topk_w, out=None):
+    T, k = topk_w.shape
+    H = y.shape[1]
+    out = torch.empty((T, H), dtype=torch.bfloat16, device=y.device) if out is None else out
+    _check(_scatter(_ptr(y), _ptr(token_slot), _ptr(topk_w), T, k, H, _ptr(out), _stream()),
+           "moe_weighted_scatter")
+    return out
+
+
+def nvfp4_fold_scales(w1_sf, gs_gate, gs_up, gs1=None):
+    """In place on w1_sf [L, 2I, K/16]; returns gs1 [L]."""
+    L, two_i, k16 = w1_sf.shape
+    gs1 = torch.empty(L, dtype=torch.float32, device=w1_sf.device) if gs1 is None else gs1
+    _check(_fold(_ptr(w1_sf), _ptr(gs_gate), _ptr(gs_up), _ptr(gs1), L, two_i // 2, k16 * 16, _stream()),
+           "nvfp4_fold_scales")
+    return gs1
+
+
+# --------------------------------------------------------------------- the layer
+
+def nvfp4_moe_ws_layout(T, k, hidden, inter, num_local) -> dict:
+    offs = (_sz * len(WS_REGIONS))()
+    tile_m = nvfp4_moe_tile_m(T, k, num_local)
+    _moe_ws_layout(T, k, hidden, inter, num_local, tile_m, offs)
+    return {name: int(offs[i]) for i, name in enumerate(WS_REGIONS)}
+
+
+def nvfp4_moe_ws_bytes(T, k, hidden, inter, num_local) -> int:
+    return int(_moe_ws(T, k, hidden, inter, num_local))
+
+
+def nvfp4_moe_tile_m(T, k, num_local) -> int:
+    return int(_moe_tile_m(T, k, num_local))
+
+
+def ws_view(ws, layout, region, dtype, shape):
+    """A typed view of one workspace region (for reading intermediates)."""
+    off = layout[region]
+    n = 1
+    for s in shape:
+        n *= s
+    nbytes = n * torch.empty((), dtype=dtype).element_size()
+    return ws[off:off + nbytes].view(dtype).view(*shape)
+
+
+class MoEWeights:
+    """Device NVFP4 layer weights for one rank (L local experts)."""
+
+    def __init__(self, w1_q, w1_sf, w1_gs, w2_q, w2_sf, w2_gs):
+        self.w1_q, self.w1_sf, self.w1_gs = w1_q, w1_sf, w1_gs
+        self.w2_q, self.w2_sf, self.w2_gs = w2_q, w2_sf, w2_gs
+        self.num_local, two_i, hh = w1_q.shape
+        self.hidden, self.inter = hh * 2, two_i // 2
+        self._c = _Weights(self.num_local, self.hidden, self.inter, w1_q.data_ptr(), w1_sf.data_ptr(),
+                           w1_gs.data_ptr(), w2_q.data_ptr(), w2_sf.data_ptr(), w2_gs.data_ptr())
+
+
+def prepare_weights(w_gate, w_up, w_down) -> MoEWeights:
+    """Offline weight preparation on the GPU: quantize each (expert, projection)
+    with its own global scale, then fold the gate/up scale ratio.
+
+    w_gate, w_up: BF16 [L, I, H]; w_down: BF16 [L, H, I].
+    """
+    L, I, H = w_gate.shape
+    gate_up = torch.cat([w_gate, w_up], dim=1).contiguous()          # [L, 2I, H]: tensor b = 2e + p
+    q1, sf1, gs_pair = nvfp4_quantize(gate_up.view(2 * L, I, H))
+    w1_q = q1.view(L, 2 * I, H // 2)
+    w1_sf = sf1.view(L, 2 * I, H // 16)
+    gs_pair = gs_pair.view(L, 2)
+    gs_gate, gs_up = gs_pair[:, 0].contiguous(), gs_pair[:, 1].contiguous()
+    w1_gs = nvfp4_fold_scales(w1_sf, gs_gate, gs_up)
+    w2_q, w2_sf, w2_gs = nvfp4_quantize(w_down.contiguous())
+    w = MoEWeights(w1_q, w1_sf, w1_gs, w2_q, w2_sf, w2_gs)
+    w.gs_gate, w.gs_up = gs_gate, gs_up
+    return w
+
+
+def nvfp4_moe_forward(weights: MoEWeights, x, topk_ids, topk_w, expert_start, out=None, ws=None):
+    """One rank's partial output BF16 [T, H] of the expert FFN."""
+    _dev(x, torch.bfloat16, "x")
+    _dev(topk_ids, torch.int32, "topk_ids")
+    _dev(topk_w, torch.float32, "topk_w")
+    T, k = topk_ids.shape
+    H = weights.hidden
+    dev = x.device
+    out = torch.empty((T, H), dtype=torch.bfloat16, device=dev) if out is None else out
+    need = nvfp4_moe_ws_bytes(T, k, H, weights.inter, weights.num_local)
+    ws = _alloc_ws(need, dev) if ws is None else ws
+    _check(_forward(ctypes.byref(weights._c), _ptr(x), T, _ptr(topk_ids), _ptr(topk_w), k, expert_start,
+                    _ptr(out), _ptr(ws), ws.numel(), _stream()), "nvfp4_moe_forward")
+    return out

@@ -1,0 +1,142 @@
+// The whole expert-FFN layer on one rank's share of experts, workspace
+// layout, and the small host entry points.
+//
+// tests history, moe_pipeline commit: quantize -> L1 (gate+up) -> SiLU*up ->
+//   re-quantize -> L2 (down) -> weighted scatter.
+// nvfp4_mega_moe.py history, alpha commit: L1 uses the activation
+//   quantizer's gs, L2 the gs returned by re-quantizing h.
+// nvfp4_cutedsl.py history, graph-compatibility commits: no host
+//   synchronisation, buffers sized for the worst case, device-side offsets,
+//   no early return when there are zero slots.
+// nvfp4_mega_moe.py history, expert-parallel note: the layer writes a local
+//   partial output; the caller reduces across ranks.
+#include "common.h"
+#include "internal.h"
+
+using namespace nvfp4;
+
+extern "C" const char* nvfp4_status_string(int status) {
+  switch (status) {
+    case NVFP4_OK: return "ok";
+    case NVFP4_ERR_NULL: return "a required pointer is NULL";
+    case NVFP4_ERR_SHAPE: return "invalid size or shape";
+    case NVFP4_ERR_ALIGN: return "a device pointer is not 16-byte aligned";
+    case NVFP4_ERR_WORKSPACE: return "workspace too small";
+    case NVFP4_ERR_HIP: return "kernel launch failed";
+    case NVFP4_ERR_ARG: return "unknown option value";
+    default: return "unknown status";
+  }
+}
+
+extern "C" int nvfp4moe_version(void) { return 100; }
+
+extern "C" int32_t nvfp4_moe_tile_m(int32_t T, int32_t k, int32_t num_local) {
+  // prefill-shaped when the slot capacity averages >= 64 rows per local expert
+  return ((int64_t)T * k >= (int64_t)64 * num_local) ? 128 : 32;
+}
+
+extern "C" size_t nvfp4_moe_ws_layout(int32_t T, int32_t k, int32_t hidden, int32_t inter, int32_t num_local,
+                                      int32_t tile_m, size_t* off) {
+  size_t o[NVFP4_WS_NREGIONS];
+  const size_t cap = (size_t)T * k;
+  size_t p = 0;
+  auto put = [&](int r, size_t bytes) {
+    o[r] = p;
+    p += nvfp4_align256(bytes);
+  };
+  put(NVFP4_WS_X_Q, (size_t)T * hidden / 2);
+  put(NVFP4_WS_X_SF, (size_t)T * hidden / 16);
+  put(NVFP4_WS_SCALARS, 16);
+  put(NVFP4_WS_COUNTS, (size_t)num_local * 4);
+  put(NVFP4_WS_OFFSETS, (size_t)(num_local + 1) * 4);
+  put(NVFP4_WS_SLOT_TOKEN, cap * 4);
+  put(NVFP4_WS_SLOT_EXPERT, cap * 4);
+  put(NVFP4_WS_SLOT_WEIGHT, cap * 4);
+  put(NVFP4_WS_TOKEN_SLOT, cap * 4);
+  put(NVFP4_WS_TILES, (size_t)nvfp4_tile_table_len((int64_t)cap, num_local, tile_m) * 4);
+  put(NVFP4_WS_ROUTE_SCRATCH, nvfp4_route_ws(T, k, num_local));
+  put(NVFP4_WS_H, cap * inter * 2);
+  put(NVFP4_WS_H_Q, cap * inter / 2);
+  put(NVFP4_WS_H_SF, cap * inter / 16);
+  put(NVFP4_WS_Y, cap * hidden * 2);
+  put(NVFP4_WS_QUANT_SCRATCH, nvfp4_quant_ws_layout(1, nullptr));
+  o[NVFP4_WS_END] = p;
+  if (off)
+    for (int r = 0; r < NVFP4_WS_NREGIONS; ++r) off[r] = o[r];
+  return p;
+}
+
+extern "C" size_t nvfp4_moe_ws_bytes(int32_t T, int32_t k, int32_t hidden, int32_t inter, int32_t num_local) {
+  if (T < 0 || k < 1 || hidden < 1 || inter < 1 || num_local < 1) return 0;
+  return nvfp4_moe_ws_layout(T, k, hidden, inter, num_local, nvfp4_moe_tile_m(T, k, num_local), nullptr);
+}
+
+extern "C" int nvfp4_moe_forward(const nvfp4_moe_weights* w, const void* x_bf16, int32_t T, const int32_t* topk_ids,
+                                 const float* topk_w, int32_t k, int32_t expert_start, void* out_bf16, void* ws,
+                                 size_t ws_bytes, void* stream_) {
+  if (!w) return NVFP4_ERR_NULL;
+  const int32_t L = w->num_local, H = w->hidden, I = w->inter;
+  if (T < 0 || k < 1 || k > 64 || L < 1 || L > 4096 || H <= 0 || I <= 0) return NVFP4_ERR_SHAPE;
+  if (H % 128 != 0 || I % 128 != 0) return NVFP4_ERR_SHAPE;
+  if ((int64_t)T * k >= (1ll << 30)) return NVFP4_ERR_SHAPE;
+  if (!w->w1_q || !w->w1_sf || !w->w1_gs || !w->w2_q || !w->w2_sf || !w->w2_gs || !ws) return NVFP4_ERR_NULL;
+  if (T > 0 && (!x_bf16 || !topk_ids || !topk_w || !out_bf16)) return NVFP4_ERR_NULL;
+  if (!nvfp4_aligned16(w->w1_q) || !nvfp4_aligned16(w->w1_sf) || !nvfp4_aligned16(w->w2_q) ||
+      !nvfp4_aligned16(w->w2_sf) || !nvfp4_aligned16(ws))
+    return NVFP4_ERR_ALIGN;
+  if (T > 0 && (!nvfp4_aligned16(x_bf16) || !nvfp4_aligned16(out_bf16))) return NVFP4_ERR_ALIGN;
+  if (ws_bytes < nvfp4_moe_ws_bytes(T, k, H, I, L)) return NVFP4_ERR_WORKSPACE;
+
+  hipStream_t stream = (hipStream_t)stream_;
+  const int32_t tile_m = nvfp4_moe_tile_m(T, k, L);
+  size_t o[NVFP4_WS_NREGIONS];
+  nvfp4_moe_ws_layout(T, k, H, I, L, tile_m, o);
+  char* base = reinterpret_cast<char*>(ws);
+  auto R = [&](int r) { return base + o[r]; };
+  uint8_t* x_q = reinterpret_cast<uint8_t*>(R(NVFP4_WS_X_Q));
+  uint8_t* x_sf = reinterpret_cast<uint8_t*>(R(NVFP4_WS_X_SF));
+  float* scalars = reinterpret_cast<float*>(R(NVFP4_WS_SCALARS));
+  int32_t* counts = reinterpret_cast<int32_t*>(R(NVFP4_WS_COUNTS));
+  int32_t* offsets = reinterpret_cast<int32_t*>(R(NVFP4_WS_OFFSETS));
+  int32_t* slot_token = reinterpret_cast<int32_t*>(R(NVFP4_WS_SLOT_TOKEN));
+  int32_t* slot_expert = reinterpret_cast<int32_t*>(R(NVFP4_WS_SLOT_EXPERT));
+  float* slot_weight = reinterpret_cast<float*>(R(NVFP4_WS_SLOT_WEIGHT));
+  int32_t* token_slot = reinterpret_cast<int32_t*>(R(NVFP4_WS_TOKEN_SLOT));
+  int32_t* tiles = reinterpret_cast<int32_t*>(R(NVFP4_WS_TILES));
+  void* route_ws = R(NVFP4_WS_ROUTE_SCRATCH);
+  uint16_t* h = reinterpret_cast<uint16_t*>(R(NVFP4_WS_H));
+  uint8_t* h_q = reinterpret_cast<uint8_t*>(R(NVFP4_WS_H_Q));
+  uint8_t* h_sf = reinterpret_cast<uint8_t*>(R(NVFP4_WS_H_SF));
+  uint16_t* y = reinterpret_cast<uint16_t*>(R(NVFP4_WS_Y));
+  void* qws = R(NVFP4_WS_QUANT_SCRATCH);
+  const int32_t cap = T * k;
+  int st;
+
+  // scalars: gs_x, amax_h, gs_h, reserved
+  if ((st = nvfp4_launch_fill_u32(reinterpret_cast<uint32_t*>(scalars), 4, 0u, stream))) return st;
+  // a1/a2: quantize x with its own global scale
+  if ((st = nvfp4_launch_quantize(x_bf16, 1, T, H, nullptr, nullptr, x_q, x_sf, &scalars[0], qws, stream)))
+    return st;
+  // a3: route
+  if ((st = nvfp4_launch_route(topk_ids, topk_w, T, k, expert_start, L, tile_m, counts, offsets, slot_token,
+                               slot_expert, slot_weight, token_slot, tiles, route_ws, stream)))
+    return st;
+  if (cap > 0) {
+    // a4/a5: L1 with the fused SiLU*up epilogue and amax of h
+    if ((st = nvfp4_launch_grouped_gemm(x_q, x_sf, slot_token, &scalars[0], w->w1_q, w->w1_sf, w->w1_gs, offsets,
+                                        tiles, L, cap, 2 * I, H, tile_m, NVFP4_EPI_SILU_MUL, h, &scalars[1],
+                                        stream)))
+      return st;
+  }
+  // a6: re-quantize the S valid rows of h with gs_h = amax_h / 2688
+  if ((st = nvfp4_launch_quantize(h, 1, cap, I, &scalars[1], &offsets[L], h_q, h_sf, &scalars[2], qws, stream)))
+    return st;
+  if (cap > 0) {
+    // a7: L2 in slot order
+    if ((st = nvfp4_launch_grouped_gemm(h_q, h_sf, nullptr, &scalars[2], w->w2_q, w->w2_sf, w->w2_gs, offsets,
+                                        tiles, L, cap, H, I, tile_m, NVFP4_EPI_BF16, y, nullptr, stream)))
+      return st;
+  }
+  // a8: weighted scatter back to token rows
+  return nvfp4_launch_scatter(y, token_slot, topk_w, T, k, H, out_bf16, stream);
+}

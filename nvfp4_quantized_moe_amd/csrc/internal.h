@@ -1,0 +1,30 @@
+// Internal launchers shared between the entry points and the layer.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+// Quantizer workspace: amax bits [B] then threshold tables [B][128][8] uint16.
+size_t nvfp4_quant_ws_layout(int64_t B, size_t* table_off);
+// rows_dev (optional, device): the number of valid rows is min(M, rows_dev[0]).
+int nvfp4_launch_quantize(const void* x_bf16, int64_t B, int64_t M, int64_t K, const float* amax_in,
+                          const int32_t* rows_dev, uint8_t* q, uint8_t* sf, float* gs_out, void* ws,
+                          hipStream_t stream);
+
+// Route workspace: per-chunk counts and bases, int32 [nchunks][num_local] each.
+constexpr int kRouteChunk = 1024;
+size_t nvfp4_route_ws(int32_t T, int32_t k, int32_t num_local);
+int nvfp4_launch_route(const int32_t* topk_ids, const float* topk_w, int32_t T, int32_t k, int32_t expert_start,
+                       int32_t num_local, int32_t tile_m, int32_t* counts, int32_t* offsets, int32_t* slot_token,
+                       int32_t* slot_expert, float* slot_weight, int32_t* token_slot, int32_t* tile_table,
+                       void* ws, hipStream_t stream);
+
+int nvfp4_launch_grouped_gemm(const uint8_t* a_q, const uint8_t* a_sf, const int32_t* a_row_index,
+                              const float* a_gs, const uint8_t* b_q, const uint8_t* b_sf, const float* b_gs,
+                              const int32_t* offsets, const int32_t* tile_table, int32_t num_local,
+                              int32_t rows_cap, int32_t N, int32_t K, int32_t tile_m, int32_t epilogue, void* d,
+                              float* amax_out, hipStream_t stream);
+
+int nvfp4_launch_scatter(const void* y_bf16, const int32_t* token_slot, const float* topk_w, int32_t T, int32_t k,
+                         int32_t H, void* out_bf16, hipStream_t stream);
+int nvfp4_launch_fill_u32(uint32_t* p, int n, uint32_t v, hipStream_t stream);

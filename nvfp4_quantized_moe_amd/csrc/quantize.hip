@@ -1,0 +1,222 @@
+// BF16 -> NVFP4 quantizer (steps a1/a2/a6 of the layer).
+//
+// nvfp4_mega_moe.py history:
+//   overflow-fix commit   gs = amax / (6 * 448) keeps every block scale <= 448
+//   alpha commit          gs is returned next to (x_fp4, x_sf), not folded
+//   three-bugs commit     stored scale = block_max / 6, nearest E2M1 magnitude,
+//                         sign kept in bit 3 of the nibble
+// tests history, packing-along-K commit: two nibbles per byte along K.
+//
+// Both roundings are decided exactly, as on the real quotients:
+//   sf  = nearest E4M3 (ties even, saturating) to bmax / (6 gs)
+//   m   = nearest E2M1 index (ties even) to |x| / (E4M3(sf) gs)
+// The scale comes from a float64 quotient (an E4M3 value or midpoint has at
+// most 5 significant bits, so the quotient of a BF16 by 6*gs that is not one
+// of them lies >= 2^-32 away relative; float64 rounding cannot move it across).
+// The magnitude is a count of E2M1 midpoints c*E4M3(sf)*gs passed; each
+// midpoint is exact in float64 (3 x 4 x 24 significant bits) and is turned
+// into a BF16 bit-pattern threshold U such that |x| passes it iff
+// bits(|x|) > U. One table of 7 thresholds per scale code (127 codes) is
+// built per tensor, so the per-element work is seven integer compares.
+//
+// Kernels: fill (clear amax), amax (wave reductions + one atomic max per
+// workgroup on the float bits, order-free), table (gs and thresholds per
+// tensor), quantize (16-element blocks, one block per thread, persistent
+// grid-stride over the tensor).
+#include "common.h"
+#include "internal.h"
+
+namespace nvfp4 {
+
+// E2M1 rounding midpoints and whether an exact tie rounds up (upper code even)
+__constant__ double kMid[7] = {0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0};
+__constant__ int kTieUp[7] = {0, 1, 0, 1, 0, 1, 0};
+
+__global__ void fill_u32_kernel(uint32_t* p, int n, uint32_t v) {
+  int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) p[i] = v;
+}
+
+// amax_bits[b] = max over x[b] of |x| as float32 bits (|x| >= 0, so the
+// unsigned order of the bits is the order of the values).
+__global__ __launch_bounds__(256) void amax_kernel(const uint16_t* __restrict__ x, int64_t per_batch,
+                                                   const int32_t* __restrict__ rows_dev, int64_t K,
+                                                   uint32_t* __restrict__ amax_bits) {
+  const int b = blockIdx.y;
+  int64_t n = per_batch;
+  if (rows_dev) {
+    int64_t r = rows_dev[0];
+    n = min(n, r * K);
+  }
+  const uint4* xv = reinterpret_cast<const uint4*>(x + (int64_t)b * per_batch);
+  int64_t nv = n / 8;
+  uint32_t m = 0;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < nv; i += (int64_t)gridDim.x * blockDim.x) {
+    uint4 v = xv[i];
+    uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      uint32_t lo = w[j] & 0x7FFFu, hi = (w[j] >> 16) & 0x7FFFu;
+      m = max(m, max(lo, hi));
+    }
+  }
+  m = wave_max_u32(m);
+  __shared__ uint32_t red[4];
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    uint32_t r = max(max(red[0], red[1]), max(red[2], red[3]));
+    if (r) atomicMax(&amax_bits[b], r << 16);
+  }
+}
+
+// Per tensor b: gs = RN_f32(amax / 2688) and the threshold table
+// table[b][code][j] (uint16, 8 per code, entry 7 unused).
+__global__ __launch_bounds__(256) void table_kernel(const float* __restrict__ amax_in,
+                                                    const uint32_t* __restrict__ amax_bits,
+                                                    uint16_t* __restrict__ table, float* __restrict__ gs_out) {
+  const int b = blockIdx.x;
+  float amax = amax_in ? amax_in[b] : __uint_as_float(amax_bits[b]);
+  // float64 quotient rounded to float32: 53 >= 2*24 + 2, so this equals one
+  // correctly rounded float32 division
+  float gs = (float)((double)amax / 2688.0);
+  if (threadIdx.x == 0) gs_out[b] = gs;
+  uint16_t* t = table + (size_t)b * 128 * 8;
+  for (int i = threadIdx.x; i < 128 * 8; i += blockDim.x) {
+    int code = i >> 3, j = i & 7;
+    uint32_t u = 0xFFFFu;
+    if (j < 7 && code > 0 && code <= 0x7E && gs > 0.0f) {
+      double step = (double)e4m3_to_f32((uint32_t)code) * (double)gs;  // exact
+      double thr = kMid[j] * step;                                       // exact
+      bool exact;
+      uint32_t rd = bf16_round_down_bits(thr, &exact);
+      // strict midpoint: |x| > thr  <=>  bits > bits(RD(thr))
+      // tie-up midpoint: |x| >= thr <=>  bits > bits(RU(thr)) - 1
+      u = (kTieUp[j] && exact) ? rd - 1u : rd;
+    }
+    t[i] = (uint16_t)u;
+  }
+}
+
+template <bool kRowsDev>
+__global__ __launch_bounds__(256) void quantize_kernel(const uint16_t* __restrict__ x, int64_t M, int64_t K,
+                                                       const int32_t* __restrict__ rows_dev,
+                                                       const uint16_t* __restrict__ table,
+                                                       const float* __restrict__ gs_arr,
+                                                       uint8_t* __restrict__ q, uint8_t* __restrict__ sf) {
+  const int b = blockIdx.y;
+  __shared__ uint4 lut[128];
+  const uint4* tb = reinterpret_cast<const uint4*>(table + (size_t)b * 128 * 8);
+  if (threadIdx.x < 128) lut[threadIdx.x] = tb[threadIdx.x];
+  __syncthreads();
+  const float gs = gs_arr[b];
+  const double six_gs = 6.0 * (double)gs;  // exact
+  int64_t rows = M;
+  if (kRowsDev) rows = min(rows, (int64_t)rows_dev[0]);
+  const int64_t nblk = rows * (K / 16);
+  const uint16_t* xb = x + (size_t)b * M * K;
+  uint8_t* qb = q + (size_t)b * M * (K / 2);
+  uint8_t* sfb = sf + (size_t)b * M * (K / 16);
+  for (int64_t blk = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; blk < nblk;
+       blk += (int64_t)gridDim.x * blockDim.x) {
+    const uint4* src = reinterpret_cast<const uint4*>(xb + blk * 16);
+    uint4 v0 = src[0], v1 = src[1];
+    uint32_t w[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
+    uint32_t bmax = 0;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) bmax = max(bmax, max(w[j] & 0x7FFFu, (w[j] >> 16) & 0x7FFFu));
+    uint32_t code = 0;
+    if (gs > 0.0f) code = e4m3_encode_rne_sat((double)bf16_to_f32(bmax) / six_gs);
+    uint4 tv = lut[code];
+    uint32_t U[7] = {tv.x & 0xFFFFu, tv.x >> 16, tv.y & 0xFFFFu, tv.y >> 16,
+                     tv.z & 0xFFFFu, tv.z >> 16, tv.w & 0xFFFFu};
+    uint32_t packed[2] = {0u, 0u};
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      uint32_t bits = (e & 1) ? (w[e >> 1] >> 16) : (w[e >> 1] & 0xFFFFu);
+      uint32_t a = bits & 0x7FFFu;
+      uint32_t m = 0;
+#pragma unroll
+      for (int j = 0; j < 7; ++j) m += (a > U[j]) ? 1u : 0u;
+      uint32_t nib = ((bits >> 12) & 8u) | m;
+      packed[e >> 3] |= nib << (4 * (e & 7));
+    }
+    *reinterpret_cast<uint2*>(qb + blk * 8) = make_uint2(packed[0], packed[1]);
+    sfb[blk] = (uint8_t)code;
+  }
+}
+
+}  // namespace nvfp4
+
+using namespace nvfp4;
+
+static int quant_grid(int64_t nblk) {
+  int64_t g = (nblk + 255) / 256;
+  if (g > 2048) g = 2048;
+  if (g < 1) g = 1;
+  return (int)g;
+}
+
+int nvfp4_launch_fill_u32(uint32_t* p, int n, uint32_t v, hipStream_t stream) {
+  hipLaunchKernelGGL(fill_u32_kernel, dim3((n + 255) / 256), dim3(256), 0, stream, p, n, v);
+  NVFP4_CHECK_LAUNCH();
+  return NVFP4_OK;
+}
+
+size_t nvfp4_quant_ws_layout(int64_t B, size_t* table_off) {
+  size_t amax_bytes = nvfp4_align256((size_t)B * 4);
+  if (table_off) *table_off = amax_bytes;
+  return amax_bytes + nvfp4_align256((size_t)B * 128 * 8 * 2);
+}
+
+// Internal launcher shared by nvfp4_quantize and the layer.
+int nvfp4_launch_quantize(const void* x_bf16, int64_t B, int64_t M, int64_t K, const float* amax_in,
+                          const int32_t* rows_dev, uint8_t* q, uint8_t* sf, float* gs_out, void* ws,
+                          hipStream_t stream) {
+  size_t table_off;
+  nvfp4_quant_ws_layout(B, &table_off);
+  uint32_t* amax_bits = reinterpret_cast<uint32_t*>(ws);
+  uint16_t* table = reinterpret_cast<uint16_t*>(reinterpret_cast<char*>(ws) + table_off);
+  const uint16_t* x = reinterpret_cast<const uint16_t*>(x_bf16);
+  if (!amax_in) {
+    hipLaunchKernelGGL(fill_u32_kernel, dim3((unsigned)((B + 255) / 256)), dim3(256), 0, stream, amax_bits,
+                       (int)B, 0u);
+    NVFP4_CHECK_LAUNCH();
+    int64_t per = M * K;
+    int64_t gx = (per / 8 + 255) / 256;
+    if (gx > 1024) gx = 1024;
+    if (gx < 1) gx = 1;
+    hipLaunchKernelGGL(amax_kernel, dim3((unsigned)gx, (unsigned)B), dim3(256), 0, stream, x, per, rows_dev, K,
+                       amax_bits);
+    NVFP4_CHECK_LAUNCH();
+  }
+  hipLaunchKernelGGL(table_kernel, dim3((unsigned)B), dim3(256), 0, stream, amax_in, amax_bits, table, gs_out);
+  NVFP4_CHECK_LAUNCH();
+  if (M == 0) return NVFP4_OK;
+  dim3 grid((unsigned)quant_grid(M * (K / 16)), (unsigned)B);
+  if (rows_dev)
+    hipLaunchKernelGGL(quantize_kernel<true>, grid, dim3(256), 0, stream, x, M, K, rows_dev, table, gs_out, q, sf);
+  else
+    hipLaunchKernelGGL(quantize_kernel<false>, grid, dim3(256), 0, stream, x, M, K, rows_dev, table, gs_out, q, sf);
+  NVFP4_CHECK_LAUNCH();
+  return NVFP4_OK;
+}
+
+extern "C" size_t nvfp4_quantize_ws_bytes(int64_t B, int64_t M, int64_t K) {
+  (void)M;
+  (void)K;
+  if (B < 1) return 0;
+  return nvfp4_quant_ws_layout(B, nullptr);
+}
+
+extern "C" int nvfp4_quantize(const void* x_bf16, int64_t B, int64_t M, int64_t K, const float* amax_in,
+                              uint8_t* q, uint8_t* sf, float* gs_out, void* ws, size_t ws_bytes, void* stream) {
+  if (B < 1 || M < 0 || K <= 0 || K % 32 != 0) return NVFP4_ERR_SHAPE;
+  if (M > 0 && (!x_bf16 || !q || !sf)) return NVFP4_ERR_NULL;
+  if (!gs_out || !ws) return NVFP4_ERR_NULL;
+  if ((M > 0 && (!nvfp4_aligned16(x_bf16) || !nvfp4_aligned16(q) || !nvfp4_aligned16(sf))) ||
+      !nvfp4_aligned16(ws))
+    return NVFP4_ERR_ALIGN;
+  if (ws_bytes < nvfp4_quantize_ws_bytes(B, M, K)) return NVFP4_ERR_WORKSPACE;
+  return nvfp4_launch_quantize(x_bf16, B, M, K, amax_in, nullptr, q, sf, gs_out, ws, (hipStream_t)stream);
+}

@@ -1,0 +1,242 @@
+// Slot routing for one rank's share of experts (step a3 of the layer).
+//
+// nvfp4_mega_moe.py history, local-expert-id commit: top-k ids are global;
+//   the rank owning [start, start + L) uses id - start.
+// src history, 1-D slot-id commits: one 1-D slot order serves both GEMMs.
+// nvfp4_cutedsl.py history, GPU-native routing and int32-offset commits:
+//   per-expert counts, int32 prefix-sum offsets, pairs sorted by expert,
+//   no host synchronisation.
+// The sort here is stable in the flat index t*k + j (histogram, prefix sum,
+// stable scatter), so the result is unique and deterministic.
+//
+// Three kernels over chunks of kRouteChunk flat entries:
+//   count    per-chunk histogram in LDS
+//   scan     one workgroup: counts, offsets, per-chunk bases, GEMM tile table
+//   scatter  per chunk, in flat order: rank among equal keys from ballots on
+//            the key bits, waves taking turns on an LDS running base per
+//            expert; also writes the -1 / 0 padding of slots >= S.
+#include "common.h"
+#include "internal.h"
+
+namespace nvfp4 {
+
+constexpr int kScanThreads = 1024;
+
+__global__ __launch_bounds__(256) void route_count_kernel(const int32_t* __restrict__ ids, int32_t n,
+                                                          int32_t start, int32_t L,
+                                                          int32_t* __restrict__ chunk_counts) {
+  extern __shared__ int32_t hist[];
+  for (int e = threadIdx.x; e < L; e += blockDim.x) hist[e] = 0;
+  __syncthreads();
+  const int base = blockIdx.x * kRouteChunk;
+  for (int i = threadIdx.x; i < kRouteChunk; i += blockDim.x) {
+    int f = base + i;
+    if (f < n) {
+      int64_t l = (int64_t)ids[f] - start;
+      if (l >= 0 && l < L) atomicAdd(&hist[l], 1);
+    }
+  }
+  __syncthreads();
+  for (int e = threadIdx.x; e < L; e += blockDim.x) chunk_counts[(size_t)blockIdx.x * L + e] = hist[e];
+}
+
+// Exclusive prefix sum over a 1024-thread workgroup; *total receives the sum.
+__device__ int block_exclusive_scan(int v, int* wsum, int* total) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  int incl = v;
+  for (int o = 1; o < 64; o <<= 1) {
+    int t = __shfl_up(incl, o, 64);
+    if (lane >= o) incl += t;
+  }
+  if (lane == 63) wsum[wave] = incl;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    int run = 0;
+    for (int w = 0; w < kScanThreads / 64; ++w) {
+      int t = wsum[w];
+      wsum[w] = run;
+      run += t;
+    }
+    wsum[kScanThreads / 64] = run;
+  }
+  __syncthreads();
+  int r = wsum[wave] + incl - v;
+  *total = wsum[kScanThreads / 64];
+  __syncthreads();
+  return r;
+}
+
+// One workgroup. Experts are split into contiguous runs of `per` per thread.
+__global__ __launch_bounds__(kScanThreads) void route_scan_kernel(
+    const int32_t* __restrict__ chunk_counts, int nchunks, int L, int tile_m, int32_t* __restrict__ counts,
+    int32_t* __restrict__ offsets, int32_t* __restrict__ bases, int32_t* __restrict__ tile_table) {
+  extern __shared__ int32_t sm[];
+  int32_t* s_cnt = sm;            // [L]
+  int32_t* s_off = sm + L;        // [L]
+  int32_t* s_toff = sm + 2 * L;   // [L]
+  __shared__ int wsum[kScanThreads / 64 + 1];
+  for (int e = threadIdx.x; e < L; e += blockDim.x) {
+    int c = 0;
+    for (int ch = 0; ch < nchunks; ++ch) c += chunk_counts[(size_t)ch * L + e];
+    s_cnt[e] = c;
+    counts[e] = c;
+  }
+  __syncthreads();
+  const int per = (L + kScanThreads - 1) / kScanThreads;
+  const int e0 = threadIdx.x * per;
+  int rows = 0, tiles = 0;
+  for (int e = e0; e < min(L, e0 + per); ++e) {
+    rows += s_cnt[e];
+    tiles += (s_cnt[e] + tile_m - 1) / tile_m;
+  }
+  int total_rows, total_tiles;
+  int row_base = block_exclusive_scan(rows, wsum, &total_rows);
+  int tile_base = block_exclusive_scan(tiles, wsum, &total_tiles);
+  for (int e = e0; e < min(L, e0 + per); ++e) {
+    s_off[e] = row_base;
+    s_toff[e] = tile_base;
+    row_base += s_cnt[e];
+    tile_base += (s_cnt[e] + tile_m - 1) / tile_m;
+  }
+  __syncthreads();
+  for (int e = threadIdx.x; e < L; e += blockDim.x) {
+    offsets[e] = s_off[e];
+    int run = s_off[e];
+    for (int ch = 0; ch < nchunks; ++ch) {
+      bases[(size_t)ch * L + e] = run;
+      run += chunk_counts[(size_t)ch * L + e];
+    }
+    int nt = (s_cnt[e] + tile_m - 1) / tile_m;
+    for (int mt = 0; mt < nt; ++mt) {
+      int t = s_toff[e] + mt;
+      tile_table[1 + 2 * t] = e;
+      tile_table[2 + 2 * t] = s_off[e] + mt * tile_m;
+    }
+  }
+  if (threadIdx.x == 0) {
+    offsets[L] = total_rows;
+    tile_table[0] = total_tiles;
+  }
+}
+
+__global__ __launch_bounds__(256) void route_scatter_kernel(
+    const int32_t* __restrict__ ids, const float* __restrict__ w, int32_t n, int32_t k, int32_t start, int32_t L,
+    int nbits, const int32_t* __restrict__ bases, const int32_t* __restrict__ offsets,
+    int32_t* __restrict__ slot_token, int32_t* __restrict__ slot_expert, float* __restrict__ slot_weight,
+    int32_t* __restrict__ token_slot) {
+  extern __shared__ int32_t running[];
+  const int chunk = blockIdx.x;
+  for (int e = threadIdx.x; e < L; e += blockDim.x) running[e] = bases[(size_t)chunk * L + e];
+  const int S = offsets[L];
+  for (int i = threadIdx.x; i < kRouteChunk; i += blockDim.x) {
+    int s = chunk * kRouteChunk + i;
+    if (s >= S && s < n) {
+      slot_token[s] = -1;
+      slot_expert[s] = -1;
+      slot_weight[s] = 0.0f;
+    }
+  }
+  __syncthreads();
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const unsigned long long below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  for (int round = 0; round < kRouteChunk / 256; ++round) {
+    const int f = chunk * kRouteChunk + round * 256 + threadIdx.x;
+    int key = L;  // L marks a dropped or absent entry
+    if (f < n) {
+      int64_t l = (int64_t)ids[f] - start;
+      if (l >= 0 && l < L) key = (int)l;
+    }
+    unsigned long long match = ~0ull;
+    for (int b = 0; b < nbits; ++b) {
+      int bit = (key >> b) & 1;
+      unsigned long long m = __ballot(bit);
+      match &= bit ? m : ~m;
+    }
+    const int rank = __popcll(match & below);
+    const int cnt = __popcll(match);
+    const bool last = (match >> lane) == 1ull;
+    int slot = -1;
+    for (int wv = 0; wv < 4; ++wv) {
+      if (wave == wv && key < L) {
+        slot = running[key] + rank;
+        if (last) running[key] += cnt;
+      }
+      __syncthreads();
+    }
+    if (f < n) {
+      token_slot[f] = slot;
+      if (slot >= 0) {
+        slot_token[slot] = f / k;
+        slot_expert[slot] = key;
+        slot_weight[slot] = w[f];
+      }
+    }
+  }
+}
+
+}  // namespace nvfp4
+
+using namespace nvfp4;
+
+static int route_nchunks(int32_t T, int32_t k) { return (int)(((int64_t)T * k + kRouteChunk - 1) / kRouteChunk); }
+
+size_t nvfp4_route_ws(int32_t T, int32_t k, int32_t num_local) {
+  size_t per = nvfp4_align256((size_t)route_nchunks(T, k) * num_local * 4);
+  return 2 * per + 256;
+}
+
+int nvfp4_launch_route(const int32_t* topk_ids, const float* topk_w, int32_t T, int32_t k, int32_t expert_start,
+                       int32_t num_local, int32_t tile_m, int32_t* counts, int32_t* offsets, int32_t* slot_token,
+                       int32_t* slot_expert, float* slot_weight, int32_t* token_slot, int32_t* tile_table,
+                       void* ws, hipStream_t stream) {
+  const int n = T * k;
+  const int nchunks = route_nchunks(T, k);
+  const int L = num_local;
+  size_t per = nvfp4_align256((size_t)nchunks * L * 4);
+  int32_t* chunk_counts = reinterpret_cast<int32_t*>(ws);
+  int32_t* bases = reinterpret_cast<int32_t*>(reinterpret_cast<char*>(ws) + per);
+  int nbits = 1;
+  while ((1 << nbits) <= L) ++nbits;  // keys 0..L must be distinct
+  if (nchunks > 0) {
+    hipLaunchKernelGGL(route_count_kernel, dim3(nchunks), dim3(256), L * 4, stream, topk_ids, n, expert_start, L,
+                       chunk_counts);
+    NVFP4_CHECK_LAUNCH();
+  }
+  hipLaunchKernelGGL(route_scan_kernel, dim3(1), dim3(kScanThreads), 3 * L * 4, stream, chunk_counts, nchunks, L,
+                     tile_m, counts, offsets, bases, tile_table);
+  NVFP4_CHECK_LAUNCH();
+  if (nchunks > 0) {
+    hipLaunchKernelGGL(route_scatter_kernel, dim3(nchunks), dim3(256), L * 4, stream, topk_ids, topk_w, n, k,
+                       expert_start, L, nbits, bases, offsets, slot_token, slot_expert, slot_weight, token_slot);
+    NVFP4_CHECK_LAUNCH();
+  }
+  return NVFP4_OK;
+}
+
+extern "C" size_t moe_route_ws_bytes(int32_t T, int32_t k, int32_t num_local) {
+  if (T < 0 || k < 1 || num_local < 1) return 0;
+  return nvfp4_route_ws(T, k, num_local);
+}
+
+extern "C" int64_t nvfp4_tile_table_len(int64_t slot_capacity, int32_t num_local, int32_t tile_m) {
+  if (slot_capacity < 0 || num_local < 1 || tile_m < 1) return 0;
+  return 1 + 2 * (slot_capacity / tile_m + num_local);
+}
+
+static bool valid_tile_m(int32_t t) { return t == 16 || t == 32 || t == 64 || t == 128 || t == 256; }
+
+extern "C" int moe_route_slots(const int32_t* topk_ids, const float* topk_w, int32_t T, int32_t k,
+                               int32_t expert_start, int32_t num_local, int32_t tile_m, int32_t* counts,
+                               int32_t* offsets, int32_t* slot_token, int32_t* slot_expert, float* slot_weight,
+                               int32_t* token_slot, int32_t* tile_table, void* ws, size_t ws_bytes, void* stream) {
+  if (T < 0 || k < 1 || k > 64 || num_local < 1 || num_local > 4096 || !valid_tile_m(tile_m))
+    return NVFP4_ERR_SHAPE;
+  if ((int64_t)T * k >= (1ll << 30)) return NVFP4_ERR_SHAPE;
+  if (!counts || !offsets || !tile_table || !ws) return NVFP4_ERR_NULL;
+  if (T > 0 && (!topk_ids || !topk_w || !slot_token || !slot_expert || !slot_weight || !token_slot))
+    return NVFP4_ERR_NULL;
+  if (!nvfp4_aligned16(ws)) return NVFP4_ERR_ALIGN;
+  if (ws_bytes < moe_route_ws_bytes(T, k, num_local)) return NVFP4_ERR_WORKSPACE;
+  return nvfp4_launch_route(topk_ids, topk_w, T, k, expert_start, num_local, tile_m, counts, offsets, slot_token,
+                            slot_expert, slot_weight, token_slot, tile_table, ws, (hipStream_t)stream);
+}

@@ -1,0 +1,113 @@
+// Weighted scatter back to token rows (step a8) and the offline gate/up
+// scale fold (weight preparation).
+//
+// Scatter — nvfp4_cutedsl.py history, GPU-native routing commit: each slot's
+// output row is added into its token's row times the routing weight; the
+// pages use an atomic scatter-add, here each token gathers its own k slots
+// in increasing j with float32 multiply then add (no fused multiply-add) and
+// rounds once to BF16, so the result is deterministic. Tokens with no local
+// slot get zeros (nvfp4_mega_moe.py history, expert-parallel note: the rank
+// writes a local partial output that the caller reduces).
+//
+// Fold — nvfp4_cutedsl.py history, finalize_weights commit: gate and up are
+// brought to one global scale max(gs_gate, gs_up) by one float32 multiply of
+// the smaller half's block scales by the ratio and a round trip to E4M3.
+#include "common.h"
+#include "internal.h"
+
+namespace nvfp4 {
+
+__global__ __launch_bounds__(256) void scatter_kernel(const uint16_t* __restrict__ y,
+                                                      const int32_t* __restrict__ token_slot,
+                                                      const float* __restrict__ topk_w, int T, int k, int H,
+                                                      uint16_t* __restrict__ out) {
+#pragma clang fp contract(off)  // separate multiply and add roundings, in j order
+  __shared__ int s_slot[64];
+  __shared__ float s_w[64];
+  const int t = blockIdx.x;
+  if (threadIdx.x < k) {
+    s_slot[threadIdx.x] = token_slot[(size_t)t * k + threadIdx.x];
+    s_w[threadIdx.x] = topk_w[(size_t)t * k + threadIdx.x];
+  }
+  __syncthreads();
+  const int nchunk = H / 8;
+  for (int c = threadIdx.x; c < nchunk; c += blockDim.x) {
+    float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+    for (int j = 0; j < k; ++j) {
+      const int s = s_slot[j];
+      if (s < 0) continue;
+      const float w = s_w[j];
+      uint4 v = *reinterpret_cast<const uint4*>(y + (size_t)s * H + c * 8);
+      uint32_t u[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const float p0 = w * bf16_to_f32(u[q] & 0xFFFFu);
+        const float p1 = w * bf16_to_f32(u[q] >> 16);
+        acc[2 * q] = acc[2 * q] + p0;
+        acc[2 * q + 1] = acc[2 * q + 1] + p1;
+      }
+    }
+    uint4 o;
+    o.x = f32_to_bf16(acc[0]) | (f32_to_bf16(acc[1]) << 16);
+    o.y = f32_to_bf16(acc[2]) | (f32_to_bf16(acc[3]) << 16);
+    o.z = f32_to_bf16(acc[4]) | (f32_to_bf16(acc[5]) << 16);
+    o.w = f32_to_bf16(acc[6]) | (f32_to_bf16(acc[7]) << 16);
+    *reinterpret_cast<uint4*>(out + (size_t)t * H + c * 8) = o;
+  }
+}
+
+__global__ __launch_bounds__(256) void fold_kernel(uint8_t* __restrict__ w1_sf, const float* __restrict__ gs_gate,
+                                                   const float* __restrict__ gs_up, float* __restrict__ gs1,
+                                                   int L, int inter, int k16) {
+  const int64_t per_e = (int64_t)2 * inter * k16;
+  const int64_t n = per_e * L;
+  for (int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; idx < n;
+       idx += (int64_t)gridDim.x * blockDim.x) {
+    const int e = (int)(idx / per_e);
+    const int64_t rem = idx - (int64_t)e * per_e;
+    const int row = (int)(rem / k16);
+    const float g = gs_gate[e], u = gs_up[e];
+    const float m = fmaxf(g, u);
+    if (rem == 0) gs1[e] = m;
+    const float p = row < inter ? g : u;
+    if (p < m) {
+      const float ratio = (float)((double)p / (double)m);  // = RN_f32(p / m): 53 >= 2*24 + 2
+      const float prod = __fmul_rn(e4m3_to_f32(w1_sf[idx]), ratio);
+      w1_sf[idx] = (uint8_t)e4m3_encode_rne_sat((double)prod);
+    }
+  }
+}
+
+}  // namespace nvfp4
+
+using namespace nvfp4;
+
+int nvfp4_launch_scatter(const void* y_bf16, const int32_t* token_slot, const float* topk_w, int32_t T, int32_t k,
+                         int32_t H, void* out_bf16, hipStream_t stream) {
+  if (T == 0) return NVFP4_OK;
+  hipLaunchKernelGGL(scatter_kernel, dim3(T), dim3(256), 0, stream, reinterpret_cast<const uint16_t*>(y_bf16),
+                     token_slot, topk_w, T, k, H, reinterpret_cast<uint16_t*>(out_bf16));
+  NVFP4_CHECK_LAUNCH();
+  return NVFP4_OK;
+}
+
+extern "C" int moe_weighted_scatter(const void* y_bf16, const int32_t* token_slot, const float* topk_w, int32_t T,
+                                    int32_t k, int32_t H, void* out_bf16, void* stream) {
+  if (T < 0 || k < 1 || k > 64 || H <= 0 || H % 8 != 0) return NVFP4_ERR_SHAPE;
+  if (T > 0 && (!y_bf16 || !token_slot || !topk_w || !out_bf16)) return NVFP4_ERR_NULL;
+  if (T > 0 && (!nvfp4_aligned16(y_bf16) || !nvfp4_aligned16(out_bf16))) return NVFP4_ERR_ALIGN;
+  return nvfp4_launch_scatter(y_bf16, token_slot, topk_w, T, k, H, out_bf16, (hipStream_t)stream);
+}
+
+extern "C" int nvfp4_fold_scales(uint8_t* w1_sf, const float* gs_gate, const float* gs_up, float* gs1,
+                                 int32_t num_local, int32_t inter, int32_t K, void* stream) {
+  if (num_local < 1 || inter < 1 || K <= 0 || K % 16 != 0) return NVFP4_ERR_SHAPE;
+  if (!w1_sf || !gs_gate || !gs_up || !gs1) return NVFP4_ERR_NULL;
+  const int64_t n = (int64_t)num_local * 2 * inter * (K / 16);
+  int64_t grid = (n + 255) / 256;
+  if (grid > 4096) grid = 4096;
+  hipLaunchKernelGGL(fold_kernel, dim3((unsigned)grid), dim3(256), 0, (hipStream_t)stream, w1_sf, gs_gate, gs_up,
+                     gs1, num_local, inter, K / 16);
+  NVFP4_CHECK_LAUNCH();
+  return NVFP4_OK;
+}

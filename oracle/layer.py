@@ -41,29 +41,33 @@ def _deq32(q, sf):
     return dequantize(q, sf, 1.0, dtype=np.float32)
 
 
-def grouped_gemm(a_q, a_sf, a_row_index, a_gs, b_q, b_sf, b_gs, offsets) -> np.ndarray:
+def grouped_gemm(a_q, a_sf, a_row_index, a_gs, b_q, b_sf, b_gs, offsets, map_fn=map) -> np.ndarray:
     """Per-expert NVFP4 GEMM in slot order.
 
     Row s in [offsets[e], offsets[e+1]) uses A row a_row_index[s] (or s when
     a_row_index is None) and expert e's weight b_q[e] [N, K/2] / b_sf[e] [N, K/16].
     Returns float32 [S, N] = RN_f32(alpha_e * (A_hat @ W_hat_e^T)) with
-    alpha_e = RN_f32(a_gs * b_gs[e]).
+    alpha_e = RN_f32(a_gs * b_gs[e]). Experts are independent; map_fn lets a
+    caller run them on several threads (same result).
     """
     offsets = np.asarray(offsets)
     L = len(offsets) - 1
     S = int(offsets[-1])
     N = b_q.shape[1]
     out = np.zeros((S, N), np.float32)
-    for e in range(L):
+
+    def one(e):
         r0, r1 = int(offsets[e]), int(offsets[e + 1])
         if r1 == r0:
-            continue
+            return
         rows = np.arange(r0, r1) if a_row_index is None else np.asarray(a_row_index[r0:r1])
         a_hat = _deq32(a_q[rows], a_sf[rows])
         w_hat = _deq32(b_q[e], b_sf[e])
         acc = np.matmul(a_hat, w_hat.T)
         alpha = np.float32(np.float32(a_gs) * np.float32(b_gs[e]))
         out[r0:r1] = acc * alpha
+
+    list(map_fn(one, range(L)))
     return out
 
 
@@ -105,18 +109,18 @@ class OracleTrace:
     out: np.ndarray
 
 
-def moe_forward(x_bits, topk_ids, topk_w, expert_start, w: dict) -> OracleTrace:
+def moe_forward(x_bits, topk_ids, topk_w, expert_start, w: dict, map_fn=map) -> OracleTrace:
     """Whole layer on one rank's share; w as returned by prepare_weights."""
     L, I = w["num_local"], w["inter"]
     x_q, x_sf, gs_x = quantize(x_bits)
     r = route(topk_ids, topk_w, expert_start, L)
     S = r["S"]
     g_out = grouped_gemm(x_q, x_sf, r["slot_token"], gs_x, w["w1_q"], w["w1_sf"], w["w1_gs"],
-                         r["offsets"])
+                         r["offsets"], map_fn)
     h = silu_mul(g_out, I)
     h_q, h_sf, gs_h = quantize(h)
     y = f32_to_bf16(grouped_gemm(h_q, h_sf, None, gs_h, w["w2_q"], w["w2_sf"], w["w2_gs"],
-                                 r["offsets"]))
+                                 r["offsets"], map_fn))
     out = scatter(y, r["token_slot"], np.asarray(topk_w, np.float32))
     assert y.shape[0] == S
     return OracleTrace(x_q, x_sf, gs_x, r, h, h_q, h_sf, gs_h, y, out)

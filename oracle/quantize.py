@@ -22,15 +22,15 @@ Readings where the pages leave a step open (each listed in the design notes):
   * The sign bit is the sign bit of the BF16 input (so -0.0 keeps it).
   * amax == 0 gives gs = 0, all scales 0 and all magnitudes 0.
 
-Exactness: inputs are BF16 (8 significant bits), gs is float32 (24 bits), an
-E4M3 scale has 4 significant bits and the E2M1 rounding midpoints
-(0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5) have at most 3, so every product
-formed below (6*gs, dec(sf)*gs, c*dec(sf)*gs) is exact in float64 and the
-comparisons decide exactly. The one division, bmax / (6 gs), is rounded to
-float64 before the E4M3 rounding; an E4M3 value or midpoint has at most 5
-significant bits, so a quotient of an 8-bit by a 27-bit number that is not
-one of them lies at least 2^-32 (relative) away — far beyond float64's
-rounding — and the E4M3 decision is unaffected.
+Exactness: inputs are BF16 (8 significant bits), gs is float32 (24 bits) and
+an E4M3 scale has 4, so 6*gs and dec(sf)*gs are exact in float64. The two
+quotients, bmax / (6 gs) and |x| / (dec(sf) gs), are rounded to float64
+before they are compared with grid midpoints. A midpoint has at most 5
+significant bits (E4M3) or 3 (E2M1: 0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5), so
+a quotient of an 8-bit number by a number of at most 28 bits that is not
+exactly a midpoint lies at least 2^-37 (relative) away from it — far beyond
+float64's rounding error of 2^-53 — and an exact tie stays exact. Every
+decision is therefore the one the real quotient gives.
 """
 from __future__ import annotations
 
@@ -38,12 +38,15 @@ import numpy as np
 
 from .formats import bf16_to_f64, e4m3_decode, e4m3_encode, pack_nibbles, e2m1_decode, unpack_nibbles
 
-# midpoints between consecutive E2M1 magnitudes and whether an exact tie
-# rounds up (the upper neighbour has the even code)
-_MIDPOINTS = ((0.25, False), (0.75, True), (1.25, False), (1.75, True),
-              (2.5, False), (3.5, True), (5.0, False))
+# midpoints between consecutive E2M1 magnitudes; an exact tie rounds up at
+# 0.75, 1.75 and 3.5 (the upper neighbour has the even code) and down elsewhere
+_MIDPOINTS = np.array([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0])
+_TIE_UP = np.array([0.75, 1.75, 3.5])
 
 GS_DIVISOR = np.float32(6.0 * 448.0)  # 2688
+
+# values of the two elements held by each byte: (element 2j, element 2j+1)
+_BYTE_PAIRS = e2m1_decode(unpack_nibbles(np.arange(256, dtype=np.uint8)[:, None])).astype(np.float32)
 
 
 def global_scale(amax) -> np.float32:
@@ -74,10 +77,14 @@ def quantize(x_bits: np.ndarray, amax=None):
     else:
         sf = e4m3_encode(bmax / (6.0 * np.float64(gs)))
     step = e4m3_decode(sf) * np.float64(gs)          # dequant factor per block, exact
-    mag = np.zeros((M, K // 16, 16), np.uint8)
-    for c, tie_up in _MIDPOINTS:
-        t = (c * step)[..., None]                     # exact
-        mag += (blocks >= t) if tie_up else (blocks > t)
+    with np.errstate(divide="ignore", invalid="ignore"):
+        r = blocks / step[..., None]                  # |x| in units of the block's step
+    # nearest E2M1 index = number of midpoints below r, plus one at a tie that rounds up
+    mag = np.zeros(r.shape, np.uint8)
+    for c in _MIDPOINTS:
+        mag += r > c
+    for c in _TIE_UP:
+        mag += r == c
     mag[step == 0] = 0
     sign = ((x_bits >> 15) & 1).astype(np.uint8).reshape(M, K // 16, 16)
     nib = (sign << 3) | mag
@@ -100,7 +107,7 @@ def dequantize(q: np.ndarray, sf: np.ndarray, gs=1.0, dtype=np.float64) -> np.nd
     q = np.asarray(q, dtype=np.uint8)
     R, Kh = q.shape
     K = Kh * 2
-    vals = e2m1_decode(unpack_nibbles(q)).reshape(R, K // 16, 16)
+    vals = _BYTE_PAIRS[q].reshape(R, K // 16, 16)    # byte -> (low nibble, high nibble) values
     s = e4m3_decode(sf)[..., None]
     out = (vals * s).reshape(R, K)
     if gs != 1.0:

@@ -1,0 +1,58 @@
+"""Shared test inputs and helpers (no method arithmetic here)."""
+import zlib
+
+import numpy as np
+
+import workloads as W
+
+E4M3_SCALES_FOR_TIES = [0x01, 0x05, 0x07, 0x08, 0x30, 0x38, 0x3F, 0x52, 0x7E]
+E4M3_VALUES = {  # exact values of the codes above (E4M3: bias 7, subnormal step 2^-9)
+    0x01: 2.0 ** -9, 0x05: 5 * 2.0 ** -9, 0x07: 7 * 2.0 ** -9, 0x08: 2.0 ** -6, 0x30: 0.5,
+    0x38: 1.0, 0x3F: 1.875, 0x52: 10.0, 0x7E: 448.0,
+}
+
+
+def adversarial_rows(rng, n_rows=6):
+    """BF16 rows with gs = 1 (one element 2688) and blocks whose elements sit
+    exactly on E2M1 rounding midpoints of their block scale."""
+    rows = []
+    mids = [0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0]
+    scales = [E4M3_VALUES[c] for c in E4M3_SCALES_FOR_TIES]
+    for _ in range(n_rows):
+        row = [2688.0] + [0.0] * 15
+        for s in rng.choice(scales, 3):
+            vals = [6.0 * s] + [float(c * s) * float(rng.choice([-1, 1])) for c in rng.choice(mids, 15)]
+            rng.shuffle(vals)
+            row += vals
+        rows.append(row)
+    return W.bf16_bits(np.asarray(rows, np.float32))
+
+
+def quant_case(name):
+    """BF16 bit arrays for the quantizer parity cases."""
+    rng = np.random.default_rng(zlib.crc32(name.encode()))
+    if name == "tiny_x":
+        return W.make_activations(W.get_config("tiny"))
+    if name == "mid_x":
+        return W.make_activations(W.get_config("mid"))
+    if name == "t3_outliers":
+        x = rng.standard_t(3, (256, 1024)).astype(np.float32)
+        x[rng.random(x.shape) < 0.001] = 2000.0
+        return W.bf16_bits(x)
+    if name == "ties":
+        return adversarial_rows(rng, 8)
+    if name == "subnormal":
+        return W.bf16_bits((rng.standard_normal((4, 256)) * 2.0 ** -128).astype(np.float32))
+    if name == "zeros":
+        x = np.zeros((3, 64), np.float32)
+        b = W.bf16_bits(x)
+        b[1, 5] = 0x8000
+        return b
+    if name == "wide":
+        return W.bf16_bits((rng.standard_normal((64, 512)) * np.exp2(rng.uniform(-20, 20, (64, 512))))
+                           .astype(np.float32))
+    if name == "ragged_rows":
+        return W.bf16_bits(rng.standard_normal((333, 96)).astype(np.float32))
+    if name == "quant_full":
+        return W.make_quant_input(W.get_config("quant"))
+    raise KeyError(name)

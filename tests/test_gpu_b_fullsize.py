@@ -1,0 +1,128 @@
+"""HIP path vs the CPU oracle at the full shard sizes, in the launch
+configuration the benchmark times (48 local experts of 384, hidden 7168,
+intermediate 3072).
+
+* decode shard (64 tokens) and prefill shard (8192 tokens) share one set of
+  weights; every expert's NVFP4 weights are compared bit for bit.
+* skewed shard (16384 tokens, Zipf popularity, cold experts, W_up 30x):
+  weights, activation quantization and routing bit for bit; the layer output
+  within 1e-2 x max|oracle|.
+The oracle runs its experts on a thread pool (same arithmetic per expert).
+"""
+import os
+import time
+from concurrent.futures import ThreadPoolExecutor
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+import workloads as W
+
+pytestmark = [pytest.mark.gpu, pytest.mark.timeout(900)]
+TOL = 1e-2
+DEV = "cuda:0"
+THREADS = min(16, len(os.sched_getaffinity(0)))
+
+
+def log(msg):
+    print(f"[gpu-full] {msg}", flush=True)
+
+
+def to_bf16(bits):
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(DEV)
+
+
+def to_dev(a):
+    return torch.from_numpy(np.ascontiguousarray(a)).to(DEV)
+
+
+def rel_err(got, ref):
+    s = float(np.abs(ref).max())
+    return float(np.abs(got - ref).max()) / s if s > 0 else float(np.abs(got).max())
+
+
+@pytest.fixture(scope="module")
+def nv():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    import nvfp4_quantized_moe_amd as nv
+    return nv
+
+
+class Shard:
+    def __init__(self, nv, weight_cfg):
+        t = time.time()
+        self.wg, self.wu, self.wd = W.make_weights(weight_cfg)
+        log(f"{weight_cfg.name} weights generated in {time.time() - t:.1f}s")
+        t = time.time()
+        self.gpu = nv.prepare_weights(to_bf16(self.wg), to_bf16(self.wu), to_bf16(self.wd))
+        torch.cuda.synchronize()
+        with ThreadPoolExecutor(THREADS) as ex:
+            self.P = O.prepare_weights(self.wg, self.wu, self.wd, map_fn=ex.map)
+        log(f"{weight_cfg.name} weights prepared (GPU + oracle on {THREADS} threads) in {time.time() - t:.1f}s")
+
+
+@pytest.fixture(scope="module")
+def shared(nv):
+    return Shard(nv, W.get_config("decode"))
+
+
+@pytest.fixture(scope="module")
+def skewed(nv):
+    return Shard(nv, W.get_config("skewed"))
+
+
+def _check_weights(nv, sh):
+    for key in ("w1_q", "w1_sf", "w1_gs", "w2_q", "w2_sf", "w2_gs"):
+        assert np.array_equal(getattr(sh.gpu, key).cpu().numpy(), sh.P[key]), key
+
+
+def _run(nv, sh, name):
+    cfg = W.get_config(name)
+    ids, w = W.make_router(cfg)
+    x = W.make_activations(cfg)
+    T, k = ids.shape
+    lay = nv.nvfp4_moe_ws_layout(T, k, cfg.hidden, cfg.inter, cfg.num_local)
+    ws = torch.empty(lay["end"], dtype=torch.uint8, device=DEV)
+    log(f"{name}: GPU forward T={T}")
+    out = nv.nvfp4_moe_forward(sh.gpu, to_bf16(x), to_dev(ids), to_dev(w), cfg.expert_start, ws=ws)
+    torch.cuda.synchronize()
+    t = time.time()
+    with ThreadPoolExecutor(THREADS) as ex:
+        tr = O.moe_forward(x, ids, w, cfg.expert_start, sh.P, map_fn=ex.map)
+    log(f"{name}: oracle forward {time.time() - t:.1f}s, S={tr.routing['S']}")
+    H = cfg.hidden
+    assert np.array_equal(nv.ws_view(ws, lay, "x_q", torch.uint8, (T, H // 2)).cpu().numpy(), tr.x_q)
+    assert np.array_equal(nv.ws_view(ws, lay, "x_sf", torch.uint8, (T, H // 16)).cpu().numpy(), tr.x_sf)
+    cap = T * k
+    for key in ("slot_token", "token_slot"):
+        assert np.array_equal(nv.ws_view(ws, lay, key, torch.int32, (cap,)).cpu().numpy(), tr.routing[key])
+    got = out.float().cpu().numpy()
+    ref = O.bf16_to_f32(tr.out)
+    err = rel_err(got, ref)
+    S = tr.routing["S"]
+    h = nv.ws_view(ws, lay, "h", torch.bfloat16, (cap, cfg.inter))[:S].float().cpu().numpy()
+    eh = rel_err(h, O.bf16_to_f32(tr.h))
+    log(f"{name}: h rel err {eh:.3e}, out rel err {err:.3e}")
+    assert eh <= TOL and err <= TOL
+    out2 = nv.nvfp4_moe_forward(sh.gpu, to_bf16(x), to_dev(ids), to_dev(w), cfg.expert_start, ws=ws)
+    assert torch.equal(out2.view(torch.int16), out.view(torch.int16))
+
+
+def test_full_weights_bit_exact(nv, shared):
+    _check_weights(nv, shared)
+
+
+def test_full_decode(nv, shared):
+    _run(nv, shared, "decode")
+
+
+def test_full_prefill(nv, shared):
+    _run(nv, shared, "prefill")
+
+
+def test_full_skewed(nv, skewed):
+    _check_weights(nv, skewed)
+    assert np.all(skewed.P["gs_up"] > 20 * skewed.P["gs_gate"])
+    _run(nv, skewed, "skewed")

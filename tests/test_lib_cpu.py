@@ -1,0 +1,87 @@
+"""The C-ABI library loads and exports every entry point of include/nvfp4moe.h
+(CPU only: no kernel is launched). Argument validation happens on the host
+before any launch, so invalid calls return their status here too."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+LIB = os.path.join(ROOT, "nvfp4_quantized_moe_amd", "libnvfp4moe.so")
+HEADER = os.path.join(ROOT, "include", "nvfp4moe.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(LIB), reason="library not built (run build())")
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"^\s*(?:const\s+)?[A-Za-z_][\w\s\*]*?\b([a-z_][a-z0-9_]*)\s*\(", text, flags=re.M)
+    return sorted(set(n for n in names if n not in ("if", "sizeof")))
+
+
+def test_header_declares_the_boundary():
+    names = _declared()
+    for n in ("nvfp4_quantize", "moe_route_slots", "nvfp4_grouped_gemm", "nvfp4_moe_forward",
+              "moe_weighted_scatter", "nvfp4_fold_scales"):
+        assert n in names
+
+
+def test_every_declared_symbol_is_exported():
+    lib = ctypes.CDLL(LIB)
+    missing = [n for n in _declared() if not hasattr(lib, n)]
+    assert not missing, missing
+
+
+def _lib():
+    import nvfp4_quantized_moe_amd as nv
+    return nv
+
+
+def test_status_strings_and_sizes():
+    nv = _lib()
+    assert nv._status_string(0) == b"ok"
+    assert b"workspace" in nv._status_string(4)
+    assert nv.version() == 100
+    assert nv.nvfp4_tile_table_len(512, 48, 32) == 1 + 2 * (16 + 48)
+    lay = nv.nvfp4_moe_ws_layout(64, 8, 7168, 3072, 48)
+    offs = [lay[r] for r in nv.WS_REGIONS]
+    assert offs == sorted(offs) and all(o % 256 == 0 for o in offs)
+    assert lay["end"] == nv.nvfp4_moe_ws_bytes(64, 8, 7168, 3072, 48)
+    assert lay["y"] - lay["h_sf"] >= 512 * 3072 // 16
+    assert nv.nvfp4_moe_tile_m(64, 8, 48) == 32 and nv.nvfp4_moe_tile_m(8192, 8, 48) == 128
+
+
+def test_invalid_arguments_are_rejected_before_launch():
+    nv = _lib()
+    buf = ctypes.c_void_p(4096)       # never dereferenced: validation fails first
+    odd = ctypes.c_void_p(4097)
+    null = None
+    s = None
+    # quantize: bad K, NULL outputs, misalignment, small workspace
+    assert nv._quantize(buf, 1, 4, 48, null, buf, buf, buf, buf, 1 << 20, s) == 2
+    assert nv._quantize(buf, 1, 4, 64, null, null, buf, buf, buf, 1 << 20, s) == 1
+    assert nv._quantize(odd, 1, 4, 64, null, buf, buf, buf, buf, 1 << 20, s) == 3
+    assert nv._quantize(buf, 1, 4, 64, null, buf, buf, buf, buf, 8, s) == 4
+    assert nv._quantize(buf, 0, 4, 64, null, buf, buf, buf, buf, 1 << 20, s) == 2
+    # route: k out of range, tile_m unsupported, NULL outputs
+    args = [buf] * 7
+    assert nv._route(buf, buf, 4, 0, 0, 8, 32, *args, buf, 1 << 20, s) == 2
+    assert nv._route(buf, buf, 4, 2, 0, 8, 48, *args, buf, 1 << 20, s) == 2
+    assert nv._route(buf, buf, 4, 2, 0, 8, 32, null, *args[1:], buf, 1 << 20, s) == 1
+    # grouped GEMM: K not a multiple of 128, unknown epilogue, odd tile height
+    g = [buf] * 9
+    assert nv._gemm(*g, 8, 64, 256, 96, 32, 0, buf, null, s) == 2
+    assert nv._gemm(*g, 8, 64, 256, 256, 32, 7, buf, null, s) == 6
+    assert nv._gemm(*g, 8, 64, 256, 256, 64, 0, buf, null, s) == 2
+    assert nv._gemm(*g, 8, 64, 256, 256, 32, 1, buf, null, s) == 1   # SiLU epilogue needs amax_out
+    # scatter / fold
+    assert nv._scatter(buf, buf, buf, 4, 2, 12, buf, s) == 2
+    assert nv._fold(null, buf, buf, buf, 4, 64, 256, s) == 1
+    # forward: NULL weights struct, bad hidden
+    assert nv._forward(None, buf, 4, buf, buf, 2, 0, buf, buf, 1 << 30, s) == 1
+    w = nv._Weights(8, 200, 128, 4096, 4096, 4096, 4096, 4096, 4096)
+    assert nv._forward(ctypes.byref(w), buf, 4, buf, buf, 2, 0, buf, buf, 1 << 30, s) == 2
+    w = nv._Weights(8, 256, 128, 4096, 4096, 4096, 4096, 4096, 4096)
+    assert nv._forward(ctypes.byref(w), buf, 4, buf, buf, 2, 0, buf, buf, 16, s) == 4

@@ -15,6 +15,7 @@ import pytest
 
 import oracle as O
 import workloads as W
+from _cases import adversarial_rows
 
 GOLD = os.path.join(os.path.dirname(__file__), "golden")
 E4M3_POS = [Fraction(float(v)) for v in O.e4m3_decode(np.arange(0, 0x7F, dtype=np.uint8))]
@@ -73,18 +74,7 @@ def brute_quantize(x_bits):
 
 
 def _adversarial_rows(rng, n_rows=6):
-    """Rows with gs = 1 and blocks whose elements sit exactly on E2M1 midpoints."""
-    rows = []
-    mids = [0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0]
-    scales = [float(v) for v in O.e4m3_decode(np.array([0x01, 0x05, 0x07, 0x08, 0x30, 0x38, 0x3F, 0x55, 0x7E], np.uint8))]
-    for _ in range(n_rows):
-        row = [2688.0] + [0.0] * 15
-        for s in rng.choice(scales, 3):
-            vals = [6.0 * s] + [float(c * s) * float(rng.choice([-1, 1])) for c in rng.choice(mids, 15)]
-            rng.shuffle(vals)
-            row += vals
-        rows.append(row)
-    return _bits(rows)
+    return adversarial_rows(rng, n_rows)
 
 
 def test_worked_example_from_pages():
