@@ -131,9 +131,11 @@ int moe_route_slots(const int32_t* topk_ids, const float* topk_w, int32_t T, int
  *   g = RN_bf16(G[s, n]), u = RN_bf16(G[s, I + n]), d[s, n] = RN_bf16(silu(g) * u)
  *   with silu(g) = g / (1 + exp(-g)) in float32; amax_out[0] is raised (atomic max)
  *   to max |d| over the rows written, so the caller sets it to 0 first.
+ * Activation row indices must satisfy (row + 1) * K/2 < 2^31, as must rows_cap * K/2
+ * and N * K/2 (32-bit buffer offsets).
  * Only rows of listed tiles are written. Requires K % 128 == 0, N % 64 == 0
  * (N % 128 == 0 for NVFP4_EPI_SILU_MUL), 1 <= L, tile_m 32 (decode-shaped
- * batches) or 128 (prefill-shaped).
+ * batches), 64 (prefill-shaped) or 128 (large groups).
  */
 enum { NVFP4_EPI_BF16 = 0, NVFP4_EPI_SILU_MUL = 1 };
 int nvfp4_grouped_gemm(const uint8_t* a_q, const uint8_t* a_sf, const int32_t* a_row_index,

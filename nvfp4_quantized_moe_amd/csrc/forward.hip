@@ -32,7 +32,7 @@ extern "C" int nvfp4moe_version(void) { return 100; }
 
 extern "C" int32_t nvfp4_moe_tile_m(int32_t T, int32_t k, int32_t num_local) {
   // prefill-shaped when the slot capacity averages >= 64 rows per local expert
-  return ((int64_t)T * k >= (int64_t)64 * num_local) ? 128 : 32;
+  return ((int64_t)T * k >= (int64_t)64 * num_local) ? 64 : 32;
 }
 
 extern "C" size_t nvfp4_moe_ws_layout(int32_t T, int32_t k, int32_t hidden, int32_t inter, int32_t num_local,

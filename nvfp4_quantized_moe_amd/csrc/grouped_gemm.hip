@@ -33,29 +33,57 @@
 
 namespace nvfp4 {
 
-constexpr int kBK = 128;           // K elements per stage
-constexpr int kRowBytes = kBK / 2; // 64 FP4 bytes per row per stage
-constexpr int kRowPitch = 80;      // LDS pitch of a row (16 bytes padding)
-constexpr int kSfBytes = kBK / 16; // 8 scale bytes per row per stage
+constexpr int kBK = 128;        // K elements per stage
+constexpr int kAPitch = 272;    // LDS bytes per fp16 A row of a stage (256 + 16 padding)
 
-template <int SUB_M, int SUB_N, int WAVES_M, int WAVES_N>
+template <int SUB_M, int SUB_N, int WAVES, int P>
 struct GemmCfg {
-  static constexpr int BM = 32 * SUB_M * WAVES_M;
-  static constexpr int BN = 32 * SUB_N * WAVES_N;
-  static constexpr int THREADS = 64 * WAVES_M * WAVES_N;
-  static constexpr int A_BYTES = BM * kRowPitch;
-  static constexpr int B_BYTES = BN * kRowPitch;
-  static constexpr int STAGE = A_BYTES + B_BYTES + (BM + BN) * kSfBytes;
-  static constexpr int LDS = 2 * STAGE;
-  // 16-byte data chunks and 8-byte scale chunks per stage
-  static constexpr int A_CHUNKS = BM * (kRowBytes / 16);
-  static constexpr int B_CHUNKS = BN * (kRowBytes / 16);
-  static constexpr int A_PER_T = (A_CHUNKS + THREADS - 1) / THREADS;
-  static constexpr int B_PER_T = (B_CHUNKS + THREADS - 1) / THREADS;
-  static constexpr int SA_PER_T = (BM + THREADS - 1) / THREADS;
-  static constexpr int SB_PER_T = (BN + THREADS - 1) / THREADS;
+  static constexpr int BM = 32 * SUB_M;            // rows of the row tile
+  static constexpr int BN = 32 * SUB_N * WAVES;    // weight rows of the column tile
+  static constexpr int THREADS = 64 * WAVES;
+  static constexpr int A_TASKS = BM * 4;           // (row, 32-element chunk) per stage
+  static constexpr int A_PER_T = (A_TASKS + THREADS - 1) / THREADS;
+  static constexpr int LDS = 2 * BM * kAPitch;
 };
 
+// Buffer resources (gfx9 descriptor): loads at offsets >= num_records return
+// zero, so rows past a group's end and column tiles past N need no branches.
+constexpr uint32_t kRsrcWord3 = 0x00020000u;
+constexpr uint32_t kOutOfRange = 0x80000000u;  // offset that is never in range
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t num_records) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)num_records, (int)kRsrcWord3);
+}
+__device__ __forceinline__ uint4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0));
+}
+__device__ __forceinline__ uint32_t buf_load4(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b32(r, (int)off, 0, 0);
+}
+__device__ __forceinline__ uint32_t buf_load2(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b16(r, (int)off, 0, 0);
+}
+
+__device__ __forceinline__ uint32_t pick_u32(const uint4& v, int i) {
+  return i == 0 ? v.x : i == 1 ? v.y : i == 2 ? v.z : v.w;
+}
+
+// E4M3 scale byte SEL of a word -> (s, s) in fp16 (both conversions exact)
+template <int SEL>
+__device__ __forceinline__ half2_t scale_pair(uint32_t sw) {
+  _Float16 s = (_Float16)__builtin_amdgcn_cvt_f32_fp8(sw, SEL);
+  half2_t r;
+  r[0] = s;
+  r[1] = s;
+  return r;
+}
+
+__device__ __forceinline__ half2_t scale_pair_dyn(uint32_t sw, int sel) {
+  return sel == 0 ? scale_pair<0>(sw) : sel == 1 ? scale_pair<1>(sw) : sel == 2 ? scale_pair<2>(sw)
+                                                                                  : scale_pair<3>(sw);
+}
+
+// 8 E2M1 values (one dword, element 8d..8d+7 in nibble order) times a scale pair
 __device__ __forceinline__ half8_t decode8(uint32_t w, half2_t s2) {
   half2_t p0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 0);
   half2_t p1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 1);
@@ -71,151 +99,128 @@ __device__ __forceinline__ half8_t decode8(uint32_t w, half2_t s2) {
   return r;
 }
 
-__device__ __forceinline__ uint32_t pick_u32(const uint4& v, int i) {
-  return i == 0 ? v.x : i == 1 ? v.y : i == 2 ? v.z : v.w;
-}
+__device__ __forceinline__ float silu_f32(float g) { return g * __builtin_amdgcn_rcpf(1.0f + __expf(-g)); }
 
-template <int SEL>
-__device__ __forceinline__ half2_t scale_pair(uint32_t sw) {
-  _Float16 s = (_Float16)__builtin_amdgcn_cvt_f32_fp8(sw, SEL);  // E4M3 -> f32 -> f16, both exact
-  half2_t r;
-  r[0] = s;
-  r[1] = s;
-  return r;
-}
-
-__device__ __forceinline__ float silu_f32(float g) { return g / (1.0f + __expf(-g)); }
-
-template <int SUB_M, int SUB_N, int WAVES_M, int WAVES_N, int EPI>
-__global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void grouped_gemm_kernel(
+// Work item = (row tile from the tile table, column tile). The row tile's
+// activations are decoded once per stage into LDS as fp16 and shared by the
+// waves; each wave streams its own 32*SUB_N weight rows from global memory
+// into registers, P stages ahead, and decodes them just before its MFMAs.
+template <int SUB_M, int SUB_N, int WAVES, int P, int EPI>
+__global__ __launch_bounds__(64 * WAVES) void grouped_gemm_kernel(
     const uint8_t* __restrict__ a_q, const uint8_t* __restrict__ a_sf, const int32_t* __restrict__ a_row_index,
     const float* __restrict__ a_gs, const uint8_t* __restrict__ b_q, const uint8_t* __restrict__ b_sf,
     const float* __restrict__ b_gs, const int32_t* __restrict__ offsets, const int32_t* __restrict__ tile_table,
-    int max_tiles, int N, int K, int n_out, int n_ntiles, uint16_t* __restrict__ d, float* __restrict__ amax_out) {
-  using C = GemmCfg<SUB_M, SUB_N, WAVES_M, WAVES_N>;
+    int max_tiles, int N, int K, int n_out, int n_ntiles, int col_fastest, uint16_t* __restrict__ d,
+    float* __restrict__ amax_out) {
+  using C = GemmCfg<SUB_M, SUB_N, WAVES, P>;
   extern __shared__ __align__(16) uint8_t lds[];
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
-  const int wm = wave / WAVES_N, wn = wave % WAVES_N;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
   const int lr = lane & 31, lg = lane >> 5;
 
   int ntiles = tile_table[0];
   ntiles = ntiles < max_tiles ? ntiles : max_tiles;
   const int items = ntiles * n_ntiles;
   const int G = gridDim.x;
+  // consecutive slots on one XCD: blocks are dispatched round-robin over the XCDs
   const int slot = (G % kXcds == 0) ? (blockIdx.x % kXcds) * (G / kXcds) + blockIdx.x / kXcds : blockIdx.x;
-  const int64_t a_pitch = K / 2, a_spitch = K / 16;
+  const int64_t pitch = K / 2, spitch = K / 16;
   const int nstages = K / kBK;
+  // activation rows: every valid row offset is below 2^31 (checked on the host)
+  const __amdgpu_buffer_rsrc_t ra_q = make_rsrc(a_q, 0x7FFFFFFFu);
+  const __amdgpu_buffer_rsrc_t ra_s = make_rsrc(a_sf, 0x7FFFFFFFu);
+  const int half_n = N / 2;
   float amax_local = 0.0f;
 
   for (int item = slot; item < items; item += G) {
-    const int mt = item / n_ntiles, nt = item % n_ntiles;
+    // row-tile order: the row tiles of one column tile are adjacent, so the
+    // row tiles of one expert share its weight tile in L2 at the same time;
+    // column order: adjacent items walk one expert's weights contiguously
+    const int mt = col_fastest ? item / n_ntiles : item % ntiles;
+    const int nt = col_fastest ? item % n_ntiles : item / ntiles;
     const int e = tile_table[1 + 2 * mt];
     const int r0 = tile_table[2 + 2 * mt];
     const int r_end = min(r0 + C::BM, offsets[e + 1]);
     const float alpha = a_gs[0] * b_gs[e];
-    const uint8_t* bq = b_q + (size_t)e * N * a_pitch;
-    const uint8_t* bs = b_sf + (size_t)e * N * a_spitch;
+    const __amdgpu_buffer_rsrc_t rb_q = make_rsrc(b_q + (size_t)e * N * pitch, (uint32_t)(N * pitch));
+    const __amdgpu_buffer_rsrc_t rb_s = make_rsrc(b_sf + (size_t)e * N * spitch, (uint32_t)(N * spitch));
 
-    // per-thread source rows for this item (fixed across stages)
-    const uint8_t* a_src[C::A_PER_T];
-    const uint8_t* b_src[C::B_PER_T];
-    const uint8_t* sa_src[C::SA_PER_T];
-    const uint8_t* sb_src[C::SB_PER_T];
+    // activation staging tasks of this thread: 16 FP4 bytes + 2 scale bytes per
+    // stage at byte offsets a_off / as_off (out of range for rows past the group)
+    uint32_t a_off[C::A_PER_T], as_off[C::A_PER_T];
 #pragma unroll
     for (int i = 0; i < C::A_PER_T; ++i) {
-      int c = tid + i * C::THREADS, row = c >> 2;
-      const uint8_t* p = nullptr;
-      if (c < C::A_CHUNKS && r0 + row < r_end) {
-        int ar = a_row_index ? a_row_index[r0 + row] : r0 + row;
-        p = a_q + (size_t)ar * a_pitch + (c & 3) * 16;
+      const int task = tid + i * C::THREADS, row = task >> 2, c = task & 3;
+      a_off[i] = kOutOfRange;
+      as_off[i] = kOutOfRange;
+      if (task < C::A_TASKS && r0 + row < r_end) {
+        const uint32_t ar = (uint32_t)(a_row_index ? a_row_index[r0 + row] : r0 + row);
+        a_off[i] = ar * (uint32_t)pitch + 16u * c;
+        as_off[i] = ar * (uint32_t)spitch + 2u * c;
       }
-      a_src[i] = p;
     }
+    // weight rows: subtile j of this wave covers 32 consecutive rows starting at the
+    // wave-uniform row0[j] (-1 when past the end); lane lr takes row0[j] + lr and
+    // lane half lg reads bytes [32 lg, 32 lg + 32) of each 64-byte stage
+    int row0[SUB_N];
 #pragma unroll
-    for (int i = 0; i < C::SA_PER_T; ++i) {
-      int row = tid + i * C::THREADS;
-      const uint8_t* p = nullptr;
-      if (row < C::BM && r0 + row < r_end) {
-        int ar = a_row_index ? a_row_index[r0 + row] : r0 + row;
-        p = a_sf + (size_t)ar * a_spitch;
-      }
-      sa_src[i] = p;
-    }
-    auto brow = [&](int r) -> int {  // LDS row of the column tile -> weight row (or -1)
+    for (int j = 0; j < SUB_N; ++j) {
+      const int ch = wave * SUB_N + j;
       if (EPI == NVFP4_EPI_SILU_MUL) {
-        int c = r >> 5, half_n = N / 2;
-        int col = nt * (C::BN / 2) + (c >> 1) * 32 + (r & 31);
-        if (col >= half_n) return -1;
-        return (c & 1) ? half_n + col : col;
+        const int col0 = nt * (C::BN / 2) + (ch >> 1) * 32;
+        row0[j] = col0 < half_n ? ((ch & 1) ? half_n + col0 : col0) : -1;
       } else {
-        int col = nt * C::BN + r;
-        return col < N ? col : -1;
+        const int col0 = nt * C::BN + ch * 32;
+        row0[j] = col0 < N ? col0 : -1;
       }
-    };
-#pragma unroll
-    for (int i = 0; i < C::B_PER_T; ++i) {
-      int c = tid + i * C::THREADS, row = c >> 2;
-      const uint8_t* p = nullptr;
-      if (c < C::B_CHUNKS) {
-        int wr = brow(row);
-        if (wr >= 0) p = bq + (size_t)wr * a_pitch + (c & 3) * 16;
-      }
-      b_src[i] = p;
     }
-#pragma unroll
-    for (int i = 0; i < C::SB_PER_T; ++i) {
-      int row = tid + i * C::THREADS;
-      const uint8_t* p = nullptr;
-      if (row < C::BN) {
-        int wr = brow(row);
-        if (wr >= 0) p = bs + (size_t)wr * a_spitch;
-      }
-      sb_src[i] = p;
-    }
+    const uint32_t b_lane = (uint32_t)lr * (uint32_t)pitch + 32u * lg;
+    const uint32_t bs_lane = (uint32_t)lr * (uint32_t)spitch + 4u * lg;
 
-    uint4 ra[C::A_PER_T], rb[C::B_PER_T];
-    uint2 rsa[C::SA_PER_T], rsb[C::SB_PER_T];
-    auto gload = [&](int s) {
-      const int kb = s * kRowBytes, ks = s * kSfBytes;
-#pragma unroll
-      for (int i = 0; i < C::A_PER_T; ++i)
-        ra[i] = a_src[i] ? *reinterpret_cast<const uint4*>(a_src[i] + kb) : make_uint4(0, 0, 0, 0);
-#pragma unroll
-      for (int i = 0; i < C::B_PER_T; ++i)
-        rb[i] = b_src[i] ? *reinterpret_cast<const uint4*>(b_src[i] + kb) : make_uint4(0, 0, 0, 0);
-#pragma unroll
-      for (int i = 0; i < C::SA_PER_T; ++i)
-        rsa[i] = sa_src[i] ? *reinterpret_cast<const uint2*>(sa_src[i] + ks) : make_uint2(0, 0);
-#pragma unroll
-      for (int i = 0; i < C::SB_PER_T; ++i)
-        rsb[i] = sb_src[i] ? *reinterpret_cast<const uint2*>(sb_src[i] + ks) : make_uint2(0, 0);
-    };
-    auto lstore = [&](int buf) {
-      uint8_t* st = lds + buf * C::STAGE;
-      uint8_t* sA = st;
-      uint8_t* sB = st + C::A_BYTES;
-      uint8_t* sSA = st + C::A_BYTES + C::B_BYTES;
-      uint8_t* sSB = sSA + C::BM * kSfBytes;
+    // Register rings of P stages for both operands. Global loads complete in
+    // issue order, so stage s's activation and weight loads are issued
+    // together, P - 1 stages ahead; waiting for one stage never waits for a
+    // later stage's loads.
+    uint4 ra[P][C::A_PER_T];
+    uint32_t rsa[P][C::A_PER_T];
+    uint4 rb[P][SUB_N][2];
+    uint32_t rsb[P][SUB_N];
+    // stages past the end read zeros (out-of-range offsets), so the loop body
+    // needs no branches around its loads
+    auto load_a = [&](int s, int slot_) {
+      const bool in = s < nstages;
 #pragma unroll
       for (int i = 0; i < C::A_PER_T; ++i) {
-        int c = tid + i * C::THREADS;
-        if (c < C::A_CHUNKS) *reinterpret_cast<uint4*>(sA + (c >> 2) * kRowPitch + (c & 3) * 16) = ra[i];
+        ra[slot_][i] = buf_load16(ra_q, in ? a_off[i] + (uint32_t)(s * 64) : kOutOfRange);
+        rsa[slot_][i] = buf_load2(ra_s, in ? as_off[i] + (uint32_t)(s * 8) : kOutOfRange);
       }
+    };
+    auto store_a = [&](int buf, int slot_) {
+      uint8_t* base = lds + buf * (C::BM * kAPitch);
 #pragma unroll
-      for (int i = 0; i < C::B_PER_T; ++i) {
-        int c = tid + i * C::THREADS;
-        if (c < C::B_CHUNKS) *reinterpret_cast<uint4*>(sB + (c >> 2) * kRowPitch + (c & 3) * 16) = rb[i];
+      for (int i = 0; i < C::A_PER_T; ++i) {
+        const int task = tid + i * C::THREADS;
+        if (task < C::A_TASKS) {
+          uint8_t* dst = base + (task >> 2) * kAPitch + (task & 3) * 64;
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            half8_t v = decode8(pick_u32(ra[slot_][i], q), scale_pair_dyn(rsa[slot_][i], q >> 1));
+            *reinterpret_cast<half8_t*>(dst + 16 * q) = v;
+          }
+        }
       }
+    };
+    auto load_b = [&](int s, int slot_) {
+      const bool in = s < nstages;
 #pragma unroll
-      for (int i = 0; i < C::SA_PER_T; ++i) {
-        int row = tid + i * C::THREADS;
-        if (row < C::BM) *reinterpret_cast<uint2*>(sSA + row * kSfBytes) = rsa[i];
-      }
-#pragma unroll
-      for (int i = 0; i < C::SB_PER_T; ++i) {
-        int row = tid + i * C::THREADS;
-        if (row < C::BN) *reinterpret_cast<uint2*>(sSB + row * kSfBytes) = rsb[i];
+      for (int j = 0; j < SUB_N; ++j) {
+        const bool ok = in && row0[j] >= 0;
+        const uint32_t o = ok ? (uint32_t)row0[j] * (uint32_t)pitch + b_lane + s * 64 : kOutOfRange;
+        const uint32_t os = ok ? (uint32_t)row0[j] * (uint32_t)spitch + bs_lane + s * 8 : kOutOfRange;
+        rb[slot_][j][0] = buf_load16(rb_q, o);
+        rb[slot_][j][1] = buf_load16(rb_q, o + 16);
+        rsb[slot_][j] = buf_load4(rb_s, os);
       }
     };
 
@@ -227,91 +232,84 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void grouped_gemm_kernel(
 #pragma unroll
         for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
 
-    __syncthreads();  // previous item's readers are done with both buffers
-    gload(0);
-    lstore(0);
+    __syncthreads();  // the previous item's waves are done with the LDS buffers
+#pragma unroll
+    for (int p = 0; p < P - 1; ++p) {
+      load_a(p, p);
+      load_b(p, p);
+    }
+    store_a(0, 0);
     __syncthreads();
-    for (int s = 0; s < nstages; ++s) {
-      const int buf = s & 1;
-      if (s + 1 < nstages) gload(s + 1);
-      const uint8_t* st = lds + buf * C::STAGE;
-      const uint8_t* sA = st;
-      const uint8_t* sB = st + C::A_BYTES;
-      const uint8_t* sSA = st + C::A_BYTES + C::B_BYTES;
-      const uint8_t* sSB = sSA + C::BM * kSfBytes;
-      // raw FP4 of this lane: 32 bytes (64 K values) per subtile, and 4 scale bytes
-      uint4 fa[SUB_M][2], fb[SUB_N][2];
-      uint32_t sa[SUB_M], sb[SUB_N];
+
+    // the stage count is rounded up to a multiple of P; the extra stages multiply zeros
+    for (int s0 = 0; s0 < nstages; s0 += P) {
 #pragma unroll
-      for (int i = 0; i < SUB_M; ++i) {
-        int row = wm * 32 * SUB_M + i * 32 + lr;
-        const uint8_t* p = sA + row * kRowPitch + lg * 32;
-        fa[i][0] = *reinterpret_cast<const uint4*>(p);
-        fa[i][1] = *reinterpret_cast<const uint4*>(p + 16);
-        sa[i] = *reinterpret_cast<const uint32_t*>(sSA + row * kSfBytes + lg * 4);
-      }
+      for (int u = 0; u < P; ++u) {
+        const int s = s0 + u;
+        load_a(s + P - 1, (u + P - 1) % P);
+        load_b(s + P - 1, (u + P - 1) % P);
+        const uint8_t* abuf = lds + (s & 1) * (C::BM * kAPitch) + lr * kAPitch + 128 * lg;
+        // software pipeline over the 8 MFMA steps of the stage: the operands of
+        // step t + 1 are read and decoded while the MFMAs of step t execute
+        half8_t av[2][SUB_M], bv[2][SUB_N];
 #pragma unroll
-      for (int j = 0; j < SUB_N; ++j) {
-        int row = wn * 32 * SUB_N + j * 32 + lr;
-        const uint8_t* p = sB + row * kRowPitch + lg * 32;
-        fb[j][0] = *reinterpret_cast<const uint4*>(p);
-        fb[j][1] = *reinterpret_cast<const uint4*>(p + 16);
-        sb[j] = *reinterpret_cast<const uint32_t*>(sSB + row * kSfBytes + lg * 4);
-      }
+        for (int i = 0; i < SUB_M; ++i) av[0][i] = *reinterpret_cast<const half8_t*>(abuf + 32 * i * kAPitch);
 #pragma unroll
-      for (int t = 0; t < 8; ++t) {
-        half8_t av[SUB_M], bv[SUB_N];
+        for (int j = 0; j < SUB_N; ++j) bv[0][j] = decode8(rb[u][j][0].x, scale_pair<0>(rsb[u][j]));
 #pragma unroll
-        for (int i = 0; i < SUB_M; ++i) {
-          uint32_t w = pick_u32(fa[i][t >> 2], t & 3);
-          half2_t s2 = (t >> 1) == 0 ? scale_pair<0>(sa[i])
-                     : (t >> 1) == 1 ? scale_pair<1>(sa[i])
-                     : (t >> 1) == 2 ? scale_pair<2>(sa[i]) : scale_pair<3>(sa[i]);
-          av[i] = decode8(w, s2);
+        for (int t = 0; t < 8; ++t) {
+          const int cur = t & 1, nxt = cur ^ 1;
+          if (t + 1 < 8) {
+#pragma unroll
+            for (int i = 0; i < SUB_M; ++i)
+              av[nxt][i] = *reinterpret_cast<const half8_t*>(abuf + 32 * i * kAPitch + 16 * (t + 1));
+#pragma unroll
+            for (int j = 0; j < SUB_N; ++j)
+              bv[nxt][j] = decode8(pick_u32(rb[u][j][(t + 1) >> 2], (t + 1) & 3),
+                                   scale_pair_dyn(rsb[u][j], (t + 1) >> 1));
+          }
+#pragma unroll
+          for (int i = 0; i < SUB_M; ++i)
+#pragma unroll
+            for (int j = 0; j < SUB_N; ++j)
+              acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(av[cur][i], bv[cur][j], acc[i][j], 0, 0, 0);
+          // issue order: the next step's LDS reads first, then one MFMA followed by
+          // a share of the next step's VALU decode, repeated
+          __builtin_amdgcn_sched_group_barrier(0x100, SUB_M, 0);
+#pragma unroll
+          for (int m = 0; m < SUB_M * SUB_N; ++m) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x002, (10 * SUB_N + SUB_M * SUB_N - 1) / (SUB_M * SUB_N), 0);
+          }
         }
-#pragma unroll
-        for (int j = 0; j < SUB_N; ++j) {
-          uint32_t w = pick_u32(fb[j][t >> 2], t & 3);
-          half2_t s2 = (t >> 1) == 0 ? scale_pair<0>(sb[j])
-                     : (t >> 1) == 1 ? scale_pair<1>(sb[j])
-                     : (t >> 1) == 2 ? scale_pair<2>(sb[j]) : scale_pair<3>(sb[j]);
-          bv[j] = decode8(w, s2);
-        }
-#pragma unroll
-        for (int i = 0; i < SUB_M; ++i)
-#pragma unroll
-          for (int j = 0; j < SUB_N; ++j)
-            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(av[i], bv[j], acc[i][j], 0, 0, 0);
-      }
-      if (s + 1 < nstages) {
-        lstore(buf ^ 1);
+        store_a((s + 1) & 1, (u + 1) % P);
         __syncthreads();
       }
     }
 
-    // epilogue: lane holds column (lane & 31) and rows 8*(v/4) + 4*lg + (v%4) of each 32x32 tile
+    // epilogue: lane holds column lr and rows 8*(v/4) + 4*lg + (v%4) of each 32x32 tile
 #pragma unroll
     for (int i = 0; i < SUB_M; ++i) {
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
-        const int row = r0 + wm * 32 * SUB_M + i * 32 + 8 * (v >> 2) + 4 * lg + (v & 3);
+        const int row = r0 + i * 32 + 8 * (v >> 2) + 4 * lg + (v & 3);
         if (row >= r_end) continue;
         if (EPI == NVFP4_EPI_SILU_MUL) {
 #pragma unroll
           for (int j = 0; j < SUB_N; j += 2) {
-            const int c = wn * SUB_N + j;  // 32-row chunk of the column tile (even: gate)
-            const int col = nt * (C::BN / 2) + (c >> 1) * 32 + lr;
+            const int ch = wave * SUB_N + j;  // even chunk: gate, next chunk: up
+            const int col = nt * (C::BN / 2) + (ch >> 1) * 32 + lr;
             if (col >= n_out) continue;
-            float g = bf16_to_f32(f32_to_bf16(acc[i][j][v] * alpha));
-            float u = bf16_to_f32(f32_to_bf16(acc[i][j + 1][v] * alpha));
-            uint32_t h = f32_to_bf16(silu_f32(g) * u);
+            const float g = bf16_to_f32(f32_to_bf16(acc[i][j][v] * alpha));
+            const float u = bf16_to_f32(f32_to_bf16(acc[i][j + 1][v] * alpha));
+            const uint32_t h = f32_to_bf16(silu_f32(g) * u);
             d[(size_t)row * n_out + col] = (uint16_t)h;
             amax_local = fmaxf(amax_local, fabsf(bf16_to_f32(h)));
           }
         } else {
 #pragma unroll
           for (int j = 0; j < SUB_N; ++j) {
-            const int col = nt * C::BN + wn * 32 * SUB_N + j * 32 + lr;
+            const int col = nt * C::BN + (wave * SUB_N + j) * 32 + lr;
             if (col >= n_out) continue;
             d[(size_t)row * n_out + col] = (uint16_t)f32_to_bf16(acc[i][j][v] * alpha);
           }
@@ -320,37 +318,42 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void grouped_gemm_kernel(
     }
   }
   if (EPI == NVFP4_EPI_SILU_MUL) {
-    float m = wave_max(amax_local);
+    const float m = wave_max(amax_local);
     if (lane == 0 && m > 0.0f) atomicMax(reinterpret_cast<unsigned int*>(amax_out), __float_as_uint(m));
   }
 }
 
-template <int SUB_M, int SUB_N, int WAVES_M, int WAVES_N, int EPI>
+template <int SUB_M, int SUB_N, int WAVES, int P, int EPI>
 static int launch_cfg(const uint8_t* a_q, const uint8_t* a_sf, const int32_t* a_row_index, const float* a_gs,
                       const uint8_t* b_q, const uint8_t* b_sf, const float* b_gs, const int32_t* offsets,
                       const int32_t* tile_table, int32_t num_local, int32_t rows_cap, int32_t N, int32_t K,
-                      void* d, float* amax_out, hipStream_t stream) {
-  using C = GemmCfg<SUB_M, SUB_N, WAVES_M, WAVES_N>;
+                      void* d, float* amax_out, hipStream_t stream, int col_fastest = 0) {
+  using C = GemmCfg<SUB_M, SUB_N, WAVES, P>;
+  static_assert(EPI != NVFP4_EPI_SILU_MUL || SUB_N % 2 == 0, "gate/up pairs live in one wave");
   const int n_out = EPI == NVFP4_EPI_SILU_MUL ? N / 2 : N;
   const int bn_out = EPI == NVFP4_EPI_SILU_MUL ? C::BN / 2 : C::BN;
   const int n_ntiles = (n_out + bn_out - 1) / bn_out;
   const int max_tiles = rows_cap / C::BM + num_local;
-  int64_t max_items = (int64_t)max_tiles * n_ntiles;
-  int occupancy = (160 * 1024) / C::LDS;
-  if (occupancy > 4) occupancy = 4;
-  if (occupancy < 1) occupancy = 1;
-  int64_t grid = 256 * occupancy;
+  const int64_t max_items = (int64_t)max_tiles * n_ntiles;
+  auto kern = grouped_gemm_kernel<SUB_M, SUB_N, WAVES, P, EPI>;
+  static int per_cu = 0;  // resident workgroups per CU (host query, once per instance)
+  if (per_cu == 0) {
+    if (C::LDS > 64 * 1024 &&
+        hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
+                            C::LDS) != hipSuccess)
+      return NVFP4_ERR_HIP;
+    int nb = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, reinterpret_cast<const void*>(kern), C::THREADS,
+                                                     C::LDS) != hipSuccess || nb < 1)
+      nb = 1;
+    per_cu = nb;
+  }
+  int64_t grid = 256LL * per_cu;
   if (grid > max_items) grid = max_items;
   if (grid >= kXcds) grid -= grid % kXcds;
   if (grid < 1) grid = 1;
-  auto kern = grouped_gemm_kernel<SUB_M, SUB_N, WAVES_M, WAVES_N, EPI>;
-  static bool attr_set = false;  // raising the dynamic LDS limit is idempotent
-  if (!attr_set) {
-    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize, C::LDS);
-    attr_set = true;
-  }
   hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(C::THREADS), C::LDS, stream, a_q, a_sf, a_row_index, a_gs,
-                     b_q, b_sf, b_gs, offsets, tile_table, max_tiles, N, K, n_out, n_ntiles,
+                     b_q, b_sf, b_gs, offsets, tile_table, max_tiles, N, K, n_out, n_ntiles, col_fastest,
                      reinterpret_cast<uint16_t*>(d), amax_out);
   NVFP4_CHECK_LAUNCH();
   return NVFP4_OK;
@@ -360,9 +363,10 @@ static int launch_cfg(const uint8_t* a_q, const uint8_t* a_sf, const int32_t* a_
 
 using namespace nvfp4;
 
-// Tile heights with a kernel configuration: 32 (decode-shaped batches: one
-// MFMA row tile, four waves across N) and 128 (prefill-shaped: 2 x 2 waves of
-// 64 x 64).
+// Row-tile heights with a kernel configuration:
+//   32  decode-shaped batches: 2 waves, each 32 weight rows, 4 stages in flight
+//   64  prefill-shaped: 4 waves, each 64 x 128, 3 stages in flight
+//   128 large groups: 4 waves, each 128 x 64, 3 stages in flight
 int nvfp4_launch_grouped_gemm(const uint8_t* a_q, const uint8_t* a_sf, const int32_t* a_row_index,
                               const float* a_gs, const uint8_t* b_q, const uint8_t* b_sf, const float* b_gs,
                               const int32_t* offsets, const int32_t* tile_table, int32_t num_local,
@@ -370,16 +374,17 @@ int nvfp4_launch_grouped_gemm(const uint8_t* a_q, const uint8_t* a_sf, const int
                               float* amax_out, hipStream_t stream) {
 #define NVFP4_GEMM_ARGS a_q, a_sf, a_row_index, a_gs, b_q, b_sf, b_gs, offsets, tile_table, num_local, rows_cap, \
                         N, K, d, amax_out, stream
-  if (tile_m == 32) {
-    if (epilogue == NVFP4_EPI_SILU_MUL) return launch_cfg<1, 2, 1, 4, NVFP4_EPI_SILU_MUL>(NVFP4_GEMM_ARGS);
-    return launch_cfg<1, 2, 1, 4, NVFP4_EPI_BF16>(NVFP4_GEMM_ARGS);
+#define NVFP4_GEMM_CFG(SM, SN, W, PF)                                                          \
+  return epilogue == NVFP4_EPI_SILU_MUL ? launch_cfg<SM, SN, W, PF, NVFP4_EPI_SILU_MUL>(NVFP4_GEMM_ARGS) \
+                                        : launch_cfg<SM, SN, W, PF, NVFP4_EPI_BF16>(NVFP4_GEMM_ARGS)
+  switch (tile_m) {
+    case 32: NVFP4_GEMM_CFG(1, 2, 2, 4);
+    case 64: NVFP4_GEMM_CFG(2, 4, 4, 3);
+    case 128: NVFP4_GEMM_CFG(4, 2, 4, 3);
+    default: return NVFP4_ERR_SHAPE;
   }
-  if (tile_m == 128) {
-    if (epilogue == NVFP4_EPI_SILU_MUL) return launch_cfg<2, 2, 2, 2, NVFP4_EPI_SILU_MUL>(NVFP4_GEMM_ARGS);
-    return launch_cfg<2, 2, 2, 2, NVFP4_EPI_BF16>(NVFP4_GEMM_ARGS);
-  }
+#undef NVFP4_GEMM_CFG
 #undef NVFP4_GEMM_ARGS
-  return NVFP4_ERR_SHAPE;
 }
 
 extern "C" int nvfp4_grouped_gemm(const uint8_t* a_q, const uint8_t* a_sf, const int32_t* a_row_index,
@@ -390,12 +395,14 @@ extern "C" int nvfp4_grouped_gemm(const uint8_t* a_q, const uint8_t* a_sf, const
   if (epilogue != NVFP4_EPI_BF16 && epilogue != NVFP4_EPI_SILU_MUL) return NVFP4_ERR_ARG;
   if (num_local < 1 || rows_cap < 0 || N <= 0 || K <= 0 || K % kBK != 0 || N % 64 != 0) return NVFP4_ERR_SHAPE;
   if (epilogue == NVFP4_EPI_SILU_MUL && N % 128 != 0) return NVFP4_ERR_SHAPE;
-  if (tile_m != 32 && tile_m != 128) return NVFP4_ERR_SHAPE;
+  if (tile_m != 32 && tile_m != 64 && tile_m != 128) return NVFP4_ERR_SHAPE;
   if (!a_q || !a_sf || !a_gs || !b_q || !b_sf || !b_gs || !offsets || !tile_table || !d) return NVFP4_ERR_NULL;
   if (epilogue == NVFP4_EPI_SILU_MUL && !amax_out) return NVFP4_ERR_NULL;
   if (!nvfp4_aligned16(a_q) || !nvfp4_aligned16(a_sf) || !nvfp4_aligned16(b_q) || !nvfp4_aligned16(b_sf) ||
       !nvfp4_aligned16(d))
     return NVFP4_ERR_ALIGN;
+  // buffer offsets are 32-bit: activation row offsets and one expert's weights stay below 2^31
+  if ((int64_t)rows_cap * (K / 2) >= (1ll << 31) || (int64_t)N * (K / 2) >= (1ll << 31)) return NVFP4_ERR_SHAPE;
   if (rows_cap == 0) return NVFP4_OK;
   return nvfp4_launch_grouped_gemm(a_q, a_sf, a_row_index, a_gs, b_q, b_sf, b_gs, offsets, tile_table, num_local,
                                    rows_cap, N, K, tile_m, epilogue, d, amax_out, (hipStream_t)stream);

@@ -179,7 +179,7 @@ GEMM_CASES = {
 
 
 @pytest.mark.parametrize("case", list(GEMM_CASES))
-@pytest.mark.parametrize("tile_m", [32, 128])
+@pytest.mark.parametrize("tile_m", [32, 64, 128])
 @pytest.mark.parametrize("epi", [0, 1])
 def test_grouped_gemm(nv, case, tile_m, epi):
     L, N, K, T, counts, gather = GEMM_CASES[case]

@@ -50,7 +50,7 @@ def test_status_strings_and_sizes():
     assert offs == sorted(offs) and all(o % 256 == 0 for o in offs)
     assert lay["end"] == nv.nvfp4_moe_ws_bytes(64, 8, 7168, 3072, 48)
     assert lay["y"] - lay["h_sf"] >= 512 * 3072 // 16
-    assert nv.nvfp4_moe_tile_m(64, 8, 48) == 32 and nv.nvfp4_moe_tile_m(8192, 8, 48) == 128
+    assert nv.nvfp4_moe_tile_m(64, 8, 48) == 32 and nv.nvfp4_moe_tile_m(8192, 8, 48) == 64
 
 
 def test_invalid_arguments_are_rejected_before_launch():
@@ -74,7 +74,7 @@ def test_invalid_arguments_are_rejected_before_launch():
     g = [buf] * 9
     assert nv._gemm(*g, 8, 64, 256, 96, 32, 0, buf, null, s) == 2
     assert nv._gemm(*g, 8, 64, 256, 256, 32, 7, buf, null, s) == 6
-    assert nv._gemm(*g, 8, 64, 256, 256, 64, 0, buf, null, s) == 2
+    assert nv._gemm(*g, 8, 64, 256, 256, 48, 0, buf, null, s) == 2
     assert nv._gemm(*g, 8, 64, 256, 256, 32, 1, buf, null, s) == 1   # SiLU epilogue needs amax_out
     # scatter / fold
     assert nv._scatter(buf, buf, buf, 4, 2, 12, buf, s) == 2
