@@ -30,6 +30,25 @@ def log(msg):
     print(f"[gpu-full] {msg}", flush=True)
 
 
+class ProgressMap:
+    """Thread-pool map for the oracle that logs each finished expert, so a
+    long oracle pass keeps printing."""
+
+    def __init__(self, ex, what):
+        self.ex, self.what, self.done = ex, what, 0
+
+    def __call__(self, fn, items):
+        items = list(items)
+
+        def one(i):
+            r = fn(i)
+            self.done += 1
+            if self.done % 8 == 0:
+                log(f"{self.what}: {self.done} expert calls done")
+            return r
+        return self.ex.map(one, items)
+
+
 def to_bf16(bits):
     return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(DEV)
 
@@ -59,7 +78,7 @@ class Shard:
         self.gpu = nv.prepare_weights(to_bf16(self.wg), to_bf16(self.wu), to_bf16(self.wd))
         torch.cuda.synchronize()
         with ThreadPoolExecutor(THREADS) as ex:
-            self.P = O.prepare_weights(self.wg, self.wu, self.wd, map_fn=ex.map)
+            self.P = O.prepare_weights(self.wg, self.wu, self.wd, map_fn=ProgressMap(ex, "oracle weights"))
         log(f"{weight_cfg.name} weights prepared (GPU + oracle on {THREADS} threads) in {time.time() - t:.1f}s")
 
 
@@ -78,7 +97,37 @@ def _check_weights(nv, sh):
         assert np.array_equal(getattr(sh.gpu, key).cpu().numpy(), sh.P[key]), key
 
 
-def _run(nv, sh, name):
+def _touched_only(cfg, ids):
+    """Global ids remapped so that the touched local experts become 0..n-1
+    (all others fall outside), and the list of touched local experts."""
+    loc = ids.astype(np.int64) - cfg.expert_start
+    touched = np.unique(loc[(loc >= 0) & (loc < cfg.num_local)])
+    remap = np.full(cfg.num_local, len(touched), np.int64)
+    remap[touched] = np.arange(len(touched))
+    inside = (loc >= 0) & (loc < cfg.num_local)
+    new = np.where(inside, remap[np.clip(loc, 0, cfg.num_local - 1)], len(touched) + 1)
+    return new.astype(ids.dtype), touched
+
+
+def _cosines(sh, cfg, x, ids, w, got):
+    """Cosine of the layer output against the BF16 layer built from the
+    dequantized NVFP4 weights (the gate) and against the original BF16
+    weights (logged), over the touched experts."""
+    I = cfg.inter
+    ids2, touched = _touched_only(cfg, ids)
+    f = lambda q, sf, gs: O.f32_to_bf16(O.dequantize(q, sf, gs, np.float32))
+    P = sh.P
+    dg = np.stack([f(P["w1_q"][e, :I], P["w1_sf"][e, :I], P["w1_gs"][e]) for e in touched])
+    du = np.stack([f(P["w1_q"][e, I:], P["w1_sf"][e, I:], P["w1_gs"][e]) for e in touched])
+    dd = np.stack([f(P["w2_q"][e], P["w2_sf"][e], P["w2_gs"][e]) for e in touched])
+    c_deq = O.cosine(got, O.bf16_reference_layer(x, ids2, w, 0, dg, du, dd))
+    del dg, du, dd
+    c_bf16 = O.cosine(got, O.bf16_reference_layer(x, ids2, w, 0, sh.wg[touched], sh.wu[touched],
+                                                  sh.wd[touched]))
+    return c_deq, c_bf16
+
+
+def _run(nv, sh, name, cosine=False):
     cfg = W.get_config(name)
     ids, w = W.make_router(cfg)
     x = W.make_activations(cfg)
@@ -90,7 +139,7 @@ def _run(nv, sh, name):
     torch.cuda.synchronize()
     t = time.time()
     with ThreadPoolExecutor(THREADS) as ex:
-        tr = O.moe_forward(x, ids, w, cfg.expert_start, sh.P, map_fn=ex.map)
+        tr = O.moe_forward(x, ids, w, cfg.expert_start, sh.P, map_fn=ProgressMap(ex, f"oracle {name}"))
     log(f"{name}: oracle forward {time.time() - t:.1f}s, S={tr.routing['S']}")
     H = cfg.hidden
     assert np.array_equal(nv.ws_view(ws, lay, "x_q", torch.uint8, (T, H // 2)).cpu().numpy(), tr.x_q)
@@ -106,6 +155,10 @@ def _run(nv, sh, name):
     eh = rel_err(h, O.bf16_to_f32(tr.h))
     log(f"{name}: h rel err {eh:.3e}, out rel err {err:.3e}")
     assert eh <= TOL and err <= TOL
+    if cosine:
+        c_deq, c_bf16 = _cosines(sh, cfg, x, ids, w, got)
+        log(f"{name}: cosine {c_deq:.4f} vs dequantized-weight BF16 layer, {c_bf16:.4f} vs original BF16 weights")
+        assert c_deq >= 0.98
     out2 = nv.nvfp4_moe_forward(sh.gpu, to_bf16(x), to_dev(ids), to_dev(w), cfg.expert_start, ws=ws)
     assert torch.equal(out2.view(torch.int16), out.view(torch.int16))
 
@@ -115,7 +168,7 @@ def test_full_weights_bit_exact(nv, shared):
 
 
 def test_full_decode(nv, shared):
-    _run(nv, shared, "decode")
+    _run(nv, shared, "decode", cosine=True)
 
 
 def test_full_prefill(nv, shared):
