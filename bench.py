@@ -32,6 +32,7 @@ PEAK_FP16_TFLOPS = 2500.0     # MI355X dense fp16/bf16 MFMA
 PEAK_FP4_TFLOPS = 10100.0     # MI355X dense fp4 MFMA (not usable for block-16 E4M3 scales)
 PEAK_HBM_GBS = 8000.0
 PROFILE_DIR = os.path.join(ROOT, "profiles")
+COPY_CAL_BYTES = 1 << 30      # bytes read (and written) by the calibration copy
 
 
 def log(msg):
@@ -67,7 +68,16 @@ def main():
     ap.add_argument("--config", default="prefill", choices=["prefill", "decode", "skewed"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run a plain 1 GiB device copy (elementwise negate) three times, "
+                         "so that counter runs can scale FETCH_SIZE / WRITE_SIZE")
+    ap.add_argument("--summarize-traffic", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="write the per-launch HBM traffic of the L1 GEMM from two rocprofv3 --pmc "
+                         "csv runs (FETCH_SIZE, WRITE_SIZE) to profiles/ and exit")
     args = ap.parse_args()
+    if args.summarize_traffic:
+        summarize_traffic(args.config, *args.summarize_traffic)
+        return
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU; --gpus {args.gpus} is not supported "
               f"(expert-parallel sharding across GPUs is described in DESIGN.md, not built)", file=sys.stderr)
@@ -91,6 +101,13 @@ def main():
 
     weights = nv.prepare_weights(bf16(wg), bf16(wu), bf16(wd))
     torch.cuda.synchronize()
+    if args.copy_calibration:
+        src = torch.ones(COPY_CAL_BYTES // 4, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            torch.neg(src, out=dst)
+        torch.cuda.synchronize()
+        del src, dst
 
     def run_layer(cfg_, ids_, w_, x_, steps, warmup):
         T, k = ids_.shape
@@ -119,7 +136,7 @@ def main():
                  nv.ws_view(ws, lay, "x_sf", torch.uint8, (T, cfg_.hidden // 16)),
                  nv.ws_view(ws, lay, "slot_token", torch.int32, (cap,)),
                  nv.ws_view(ws, lay, "scalars", torch.float32, (4,))[0:1],
-                 weights.w1_q, weights.w1_sf, weights.w1_gs,
+                 weights.w1, weights.w1_gs,
                  nv.ws_view(ws, lay, "offsets", torch.int32, (cfg_.num_local + 1,)),
                  nv.ws_view(ws, lay, "tiles", torch.int32, (nv.nvfp4_tile_table_len(cap, cfg_.num_local, tile_m),)))
         h = torch.empty((cap, cfg_.inter), dtype=torch.bfloat16, device=dev)
@@ -191,27 +208,76 @@ def main():
     print(json.dumps(result), flush=True)
 
 
+def _counter_rows(d, counter):
+    """(kernel name, value) per dispatch from a rocprofv3 csv counter run."""
+    import csv
+    import glob
+    files = glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)
+    if not files:
+        raise SystemExit(f"no counter_collection.csv under {d}")
+    rows = []
+    for f in files:
+        for r in csv.DictReader(open(f)):
+            if r["Counter_Name"] == counter:
+                rows.append((r["Kernel_Name"], float(r["Counter_Value"])))
+    return rows
+
+
+def summarize_traffic(workload, fetch_dir, write_dir):
+    """Per-launch HBM bytes of the L1 GEMM (the grouped GEMM instance with the
+    SiLU*up epilogue), each counter scaled by what it reads for the plain
+    1 GiB copy of --copy-calibration."""
+    out = {}
+    for tag, d, counter in (("fetch", fetch_dir, "FETCH_SIZE"), ("write", write_dir, "WRITE_SIZE")):
+        rows = _counter_rows(d, counter)
+        cal = [v for n, v in rows if "neg" in n.lower()]
+        l1 = [v for n, v in rows if "grouped_gemm_kernel" in n and n.replace(" ", "").split(">")[0].endswith(",1")]
+        if not cal or not l1:
+            raise SystemExit(f"{counter}: calibration dispatches {len(cal)}, L1 GEMM dispatches {len(l1)}")
+        factor = COPY_CAL_BYTES / (float(np.median(cal)) * 1024.0)
+        out[tag] = dict(kib=float(np.mean(l1)), factor=factor, n=len(l1),
+                        bytes=float(np.mean(l1)) * 1024.0 * factor)
+    path = os.path.join(PROFILE_DIR, f"l1_gemm_{workload}_traffic.txt")
+    with open(path, "w") as f:
+        f.write(f"# HBM traffic of the L1 grouped GEMM (gate+up, SiLU*up epilogue), {workload} shard\n")
+        f.write("# counters from two rocprofv3 runs on the MI355X box, from the repository root:\n")
+        for c, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
+            f.write(f"#   timeout -s KILL 120 rocprofv3 --pmc {c} -f csv -d {d} -o run -- python -u bench.py "
+                    f"--config {workload} --steps 2 --warmup 1 --no-decode --no-cpu-baseline --copy-calibration\n")
+        f.write(f"# summarized with: python bench.py --config {workload} --summarize-traffic {fetch_dir} {write_dir}\n")
+        f.write("# each counter (KiB per dispatch) is scaled by bytes / counter of a plain 1 GiB copy\n")
+        f.write(f"kernel_source_sha = {kernel_source_sha()}\n")
+        for tag in ("fetch", "write"):
+            o = out[tag]
+            f.write(f"{tag}_kib_per_launch = {o['kib']:.1f}\n{tag}_copy_factor = {o['factor']:.4f}\n"
+                    f"{tag}_dispatches = {o['n']}\n{tag}_bytes_per_launch = {o['bytes']:.0f}\n")
+        f.write(f"hbm_bytes_per_launch = {out['fetch']['bytes'] + out['write']['bytes']:.0f}\n")
+    print(open(path).read())
+
+
 def cpu_baseline(cfg, ids, w, x, wg, wu, wd, T):
     """The CPU oracle timed on a bounded sample of the same workload: the
-    first n tokens (all of their local slots) through a1..a8. Weight
-    preparation (offline) is not timed."""
+    first n tokens (all of their local slots) through steps a1..a8, experts
+    spread over a pool of worker threads with one BLAS thread each, so the
+    core count is the pool size. Weight preparation (offline) is not timed."""
     import oracle as O
-    n = min(T, int(os.environ.get("NVFP4_BENCH_ORACLE_TOKENS", "1024")))
+    from threadpoolctl import threadpool_limits
+    n = min(T, int(os.environ.get("NVFP4_BENCH_ORACLE_TOKENS", "4096")))
     cores = len(os.sched_getaffinity(0))
     threads = min(16, cores)
     t0 = time.time()
     with ThreadPoolExecutor(max_workers=threads) as ex:
         P = O.prepare_weights(wg, wu, wd, map_fn=ex.map)
     log(f"oracle weight preparation (untimed) {time.time() - t0:.1f}s")
-    t = time.perf_counter()
-    with ThreadPoolExecutor(max_workers=threads) as ex:
+    with threadpool_limits(limits=1), ThreadPoolExecutor(max_workers=threads) as ex:
+        t = time.perf_counter()
         O.moe_forward(x[:n], ids[:n], w[:n], cfg.expert_start, P, map_fn=ex.map)
-    dt = time.perf_counter() - t
+        dt = time.perf_counter() - t
     log(f"oracle forward on {n} tokens: {dt:.1f}s")
     return {"value": round(n / dt, 2), "unit": "tokens/s", "cores": threads, "kind": "oracle",
             "sample": f"first {n} of {T} tokens of the {cfg.name} shard (all their local slots), "
-                      f"steps a1-a8; experts on {threads} threads, BLAS threads inside each; "
-                      f"{cores} host cores visible; {dt:.1f}s"}
+                      f"steps a1-a8 in {dt:.1f}s; experts on {threads} worker threads with one BLAS "
+                      f"thread each; {cores} host cores visible"}
 
 
 if __name__ == "__main__":

@@ -110,6 +110,27 @@ int moe_route_slots(const int32_t* topk_ids, const float* topk_w, int32_t T, int
                     float* slot_weight, int32_t* token_slot, int32_t* tile_table,
                     void* ws, size_t ws_bytes, void* stream);
 
+/* ---------------------------------------------------------- weight packing
+ * Offline weight preparation, step three (after quantize and fold): the
+ * grouped GEMM reads weights in a packed order that matches its MFMA operand
+ * fragments, so that every load instruction of a wave reads one contiguous
+ * 1 KB (or 256 B) block. Packing is a byte permutation of (q, sf); nothing is
+ * rounded. (Layout of this library's own design; the NVFP4 values and scales
+ * are those of nvfp4_quantize.)
+ *
+ * Input: B matrices, q uint8 [B, N, K/2] and sf uint8 [B, N, K/16], row-major.
+ * Output: packed uint8 [B][N/32][K/128][2304], one 2304-byte chunk per
+ * (matrix b, 32-row subtile t, 128-element K stage c):
+ *   chunk[h*1024 + 16*l + i] = q [b, 32t + l%32, 64c + 32*(l/32) + 16h + i]
+ *                                           h in {0,1}, l in [0,64), i in [0,16)
+ *   chunk[2048 + 4*l + i]    = sf[b, 32t + l%32, 8c + 4*(l/32) + i]        i in [0,4)
+ * Size: nvfp4_packed_bytes(B, N, K) = B * N * K * 9/16 bytes (same as q + sf).
+ * Requires B >= 0, N % 32 == 0, K % 128 == 0; nvfp4_packed_bytes returns -1 otherwise.
+ */
+int64_t nvfp4_packed_bytes(int64_t B, int64_t N, int64_t K);
+int nvfp4_pack_weights(const uint8_t* q, const uint8_t* sf, int64_t B, int64_t N, int64_t K,
+                       uint8_t* packed, void* stream);
+
 /* ------------------------------------------------------------ grouped GEMM
  * NVFP4 x NVFP4 grouped GEMM over slot rows (nvfp4_mega_moe.py history: alpha
  * commit; src history: 1-D slot ids, gather only for L1; tests history:
@@ -121,25 +142,26 @@ int moe_route_slots(const int32_t* topk_ids, const float* topk_w, int32_t T, int
  *   G[s, n] = alpha_e * sum_k A_hat[a, k] * W_hat_e[n, k],  alpha_e = RN_f32(a_gs[0] * b_gs[e])
  * with A_hat, W_hat the exact dequantized values without global scale and the
  * sum in float32.
- *   a_q uint8 [*, K/2], a_sf uint8 [*, K/16]; b_q uint8 [L, N, K/2]; b_sf uint8 [L, N, K/16];
+ *   a_q uint8 [*, K/2], a_sf uint8 [*, K/16] (row-major NVFP4);
+ *   b_packed: the L expert matrices W_e [N, K] packed by nvfp4_pack_weights (B = L);
  *   a_gs float [1]; b_gs float [L]; offsets int32 [L+1]; tile_table as from moe_route_slots
  *   with the same tile_m; rows_cap = capacity of the row arrays (tile_table holds at
  *   most nvfp4_tile_table_len(rows_cap, L, tile_m) entries).
  * epilogue NVFP4_EPI_BF16:        d = BF16 [rows_cap, N], d[s, n] = RN_bf16(G[s, n]).
- * epilogue NVFP4_EPI_SILU_MUL:    N = 2*I (gate rows [0, I), up rows [I, 2I) of b;
+ * epilogue NVFP4_EPI_SILU_MUL:    N = 2*I (gate rows [0, I), up rows [I, 2I) of W_e;
  *   nvfp4_cutedsl.py history, intermediate-split commit), d = BF16 [rows_cap, I],
  *   g = RN_bf16(G[s, n]), u = RN_bf16(G[s, I + n]), d[s, n] = RN_bf16(silu(g) * u)
  *   with silu(g) = g / (1 + exp(-g)) in float32; amax_out[0] is raised (atomic max)
  *   to max |d| over the rows written, so the caller sets it to 0 first.
  * Activation row indices must satisfy (row + 1) * K/2 < 2^31, as must rows_cap * K/2
- * and N * K/2 (32-bit buffer offsets).
+ * and N * K * 9/16 (32-bit buffer offsets).
  * Only rows of listed tiles are written. Requires K % 128 == 0, N % 64 == 0
  * (N % 128 == 0 for NVFP4_EPI_SILU_MUL), 1 <= L, tile_m 32 (decode-shaped
  * batches), 64 (prefill-shaped) or 128 (large groups).
  */
 enum { NVFP4_EPI_BF16 = 0, NVFP4_EPI_SILU_MUL = 1 };
 int nvfp4_grouped_gemm(const uint8_t* a_q, const uint8_t* a_sf, const int32_t* a_row_index,
-                       const float* a_gs, const uint8_t* b_q, const uint8_t* b_sf, const float* b_gs,
+                       const float* a_gs, const uint8_t* b_packed, const float* b_gs,
                        const int32_t* offsets, const int32_t* tile_table, int32_t num_local,
                        int32_t rows_cap, int32_t N, int32_t K, int32_t tile_m, int32_t epilogue,
                        void* d, float* amax_out, void* stream);
@@ -171,22 +193,22 @@ int nvfp4_fold_scales(uint8_t* w1_sf, const float* gs_gate, const float* gs_up, 
  *   quantize x (own gs) -> route -> L1 grouped GEMM with the SiLU*up epilogue
  *   (alpha = gs_x * w1_gs[e]) -> re-quantize h (gs_h from the epilogue's amax)
  *   -> L2 grouped GEMM (alpha = gs_h * w2_gs[e]) -> weighted scatter.
- * Weights (host struct of device pointers), L = num_local:
- *   w1_q [L, 2I, H/2], w1_sf [L, 2I, H/16], w1_gs [L]   gate rows [0,I), up rows [I,2I),
- *                                                         gate/up scales folded to one gs
- *   w2_q [L, H, I/2],  w2_sf [L, H, I/16],  w2_gs [L]
+ * Weights (host struct of device pointers), L = num_local, each packed by
+ * nvfp4_pack_weights from its row-major NVFP4 form:
+ *   w1: W1 [L, 2I, H] packed (B = L, N = 2I, K = H), w1_gs [L]
+ *       gate rows [0,I), up rows [I,2I), gate/up scales folded to one gs (nvfp4_fold_scales)
+ *   w2: W2 [L, H, I] packed (B = L, N = H, K = I),   w2_gs [L]
  * x_bf16 [T, H]; topk_ids int32 [T, k] global ids; topk_w float [T, k];
  * out_bf16 [T, H] (tokens with no local expert get zeros).
  * ws: at least nvfp4_moe_ws_bytes(...) bytes; its regions (nvfp4_moe_ws_layout)
- * hold the intermediates after the call. Requires H % 128 == 0, I % 64 == 0.
+ * hold the intermediates after the call. Requires H % 128 == 0, I % 128 == 0,
+ * T*k < 2^30, and T*H/2, T*k*I/2 and 2I*H*9/16 below 2^31.
  */
 typedef struct {
   int32_t num_local, hidden, inter;
-  const uint8_t* w1_q;
-  const uint8_t* w1_sf;
+  const uint8_t* w1;
   const float* w1_gs;
-  const uint8_t* w2_q;
-  const uint8_t* w2_sf;
+  const uint8_t* w2;
   const float* w2_gs;
 } nvfp4_moe_weights;
 

@@ -17,7 +17,8 @@ import torch
 __all__ = [
     "lib", "LIB_PATH", "NVFP4Error", "EPI_BF16", "EPI_SILU_MUL", "WS_REGIONS", "nvfp4_quantize",
     "nvfp4_quantize_ws_bytes", "moe_route_slots", "moe_route_ws_bytes", "nvfp4_tile_table_len",
-    "nvfp4_grouped_gemm", "moe_weighted_scatter", "nvfp4_fold_scales", "nvfp4_moe_forward",
+    "nvfp4_grouped_gemm", "moe_weighted_scatter", "nvfp4_fold_scales", "nvfp4_packed_bytes",
+    "nvfp4_pack_weights", "nvfp4_moe_forward",
     "nvfp4_moe_ws_bytes", "nvfp4_moe_ws_layout", "nvfp4_moe_tile_m", "MoEWeights", "prepare_weights",
     "ws_view",
 ]
@@ -36,8 +37,7 @@ _vp, _i32, _i64, _sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c
 
 class _Weights(ctypes.Structure):
     _fields_ = [("num_local", _i32), ("hidden", _i32), ("inter", _i32),
-                ("w1_q", _vp), ("w1_sf", _vp), ("w1_gs", _vp),
-                ("w2_q", _vp), ("w2_sf", _vp), ("w2_gs", _vp)]
+                ("w1", _vp), ("w1_gs", _vp), ("w2", _vp), ("w2_gs", _vp)]
 
 
 def _sig(name, res, *args):
@@ -55,8 +55,10 @@ _route_ws = _sig("moe_route_ws_bytes", _sz, _i32, _i32, _i32)
 _tile_len = _sig("nvfp4_tile_table_len", _i64, _i64, _i32, _i32)
 _route = _sig("moe_route_slots", ctypes.c_int, _vp, _vp, _i32, _i32, _i32, _i32, _i32,
               _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp)
-_gemm = _sig("nvfp4_grouped_gemm", ctypes.c_int, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+_gemm = _sig("nvfp4_grouped_gemm", ctypes.c_int, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
              _i32, _i32, _i32, _i32, _i32, _i32, _vp, _vp, _vp)
+_packed_bytes = _sig("nvfp4_packed_bytes", _i64, _i64, _i64, _i64)
+_pack = _sig("nvfp4_pack_weights", ctypes.c_int, _vp, _vp, _i64, _i64, _i64, _vp, _vp)
 _scatter = _sig("moe_weighted_scatter", ctypes.c_int, _vp, _vp, _vp, _i32, _i32, _i32, _vp, _vp)
 _fold = _sig("nvfp4_fold_scales", ctypes.c_int, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _vp)
 _moe_ws_layout = _sig("nvfp4_moe_ws_layout", _sz, _i32, _i32, _i32, _i32, _i32, _i32,
@@ -158,14 +160,35 @@ def moe_route_slots(topk_ids, topk_w, expert_start, num_local, tile_m):
 
 # ------------------------------------------------------------------ grouped GEMM
 
-def nvfp4_grouped_gemm(a_q, a_sf, a_row_index, a_gs, b_q, b_sf, b_gs, offsets, tile_table, rows_cap,
-                       tile_m, epilogue=EPI_BF16, d=None, amax_out=None):
-    L, N, Kh = b_q.shape
+def nvfp4_packed_bytes(B, N, K) -> int:
+    return int(_packed_bytes(B, N, K))
+
+
+def nvfp4_pack_weights(q, sf, out=None):
+    """Row-major NVFP4 matrices q uint8 [B, N, K/2], sf uint8 [B, N, K/16] ->
+    packed uint8 [B, N/32, K/128, 2304] in the grouped GEMM's operand order."""
+    _dev(q, torch.uint8, "q")
+    _dev(sf, torch.uint8, "sf")
+    B, N, Kh = q.shape
     K = Kh * 2
-    dev = b_q.device
+    if tuple(sf.shape) != (B, N, K // 16):
+        raise ValueError(f"sf shape {tuple(sf.shape)} does not match q {tuple(q.shape)}")
+    if N % 32 or K % 128:
+        raise ValueError(f"packing needs N % 32 == 0 and K % 128 == 0, got N={N}, K={K}")
+    out = torch.empty((B, N // 32, K // 128, 2304), dtype=torch.uint8, device=q.device) if out is None else out
+    _check(_pack(_ptr(q), _ptr(sf), B, N, K, _ptr(out), _stream()), "nvfp4_pack_weights")
+    return out
+
+
+def nvfp4_grouped_gemm(a_q, a_sf, a_row_index, a_gs, b_packed, b_gs, offsets, tile_table, rows_cap,
+                       tile_m, epilogue=EPI_BF16, d=None, amax_out=None):
+    """b_packed: uint8 [L, N/32, K/128, 2304] from nvfp4_pack_weights."""
+    L, n32, k128, chunk = b_packed.shape
+    N, K = n32 * 32, k128 * 128
+    dev = b_packed.device
     n_out = N // 2 if epilogue == EPI_SILU_MUL else N
     d = torch.empty((rows_cap, n_out), dtype=torch.bfloat16, device=dev) if d is None else d
-    _check(_gemm(_ptr(a_q), _ptr(a_sf), _ptr(a_row_index), _ptr(a_gs), _ptr(b_q), _ptr(b_sf), _ptr(b_gs),
+    _check(_gemm(_ptr(a_q), _ptr(a_sf), _ptr(a_row_index), _ptr(a_gs), _ptr(b_packed), _ptr(b_gs),
                  _ptr(offsets), _ptr(tile_table), L, rows_cap, N, K, tile_m, epilogue, _ptr(d), _ptr(amax_out),
                  _stream()), "nvfp4_grouped_gemm")
     return d
@@ -217,34 +240,43 @@ def ws_view(ws, layout, region, dtype, shape):
 
 
 class MoEWeights:
-    """Device NVFP4 layer weights for one rank (L local experts)."""
+    """Device NVFP4 layer weights for one rank (L local experts): packed W1
+    (gate rows then up rows, scales folded to w1_gs) and packed W2. With
+    keep_unpacked, prepare_weights also keeps the row-major forms (w1_q,
+    w1_sf, w2_q, w2_sf) for inspection."""
 
-    def __init__(self, w1_q, w1_sf, w1_gs, w2_q, w2_sf, w2_gs):
-        self.w1_q, self.w1_sf, self.w1_gs = w1_q, w1_sf, w1_gs
-        self.w2_q, self.w2_sf, self.w2_gs = w2_q, w2_sf, w2_gs
-        self.num_local, two_i, hh = w1_q.shape
-        self.hidden, self.inter = hh * 2, two_i // 2
-        self._c = _Weights(self.num_local, self.hidden, self.inter, w1_q.data_ptr(), w1_sf.data_ptr(),
-                           w1_gs.data_ptr(), w2_q.data_ptr(), w2_sf.data_ptr(), w2_gs.data_ptr())
+    def __init__(self, w1, w1_gs, w2, w2_gs):
+        self.w1, self.w1_gs, self.w2, self.w2_gs = w1, w1_gs, w2, w2_gs
+        self.num_local = w1.shape[0]
+        self.inter = w1.shape[1] * 32 // 2
+        self.hidden = w1.shape[2] * 128
+        if tuple(w2.shape[:3]) != (self.num_local, self.hidden // 32, self.inter // 128):
+            raise ValueError(f"packed W2 shape {tuple(w2.shape)} does not match W1 {tuple(w1.shape)}")
+        self._c = _Weights(self.num_local, self.hidden, self.inter, w1.data_ptr(), w1_gs.data_ptr(),
+                           w2.data_ptr(), w2_gs.data_ptr())
 
 
-def prepare_weights(w_gate, w_up, w_down) -> MoEWeights:
+def prepare_weights(w_gate, w_up, w_down, keep_unpacked=False) -> MoEWeights:
     """Offline weight preparation on the GPU: quantize each (expert, projection)
-    with its own global scale, then fold the gate/up scale ratio.
+    with its own global scale, fold the gate/up scale ratio, and pack both
+    matrices for the grouped GEMM.
 
     w_gate, w_up: BF16 [L, I, H]; w_down: BF16 [L, H, I].
     """
     L, I, H = w_gate.shape
     gate_up = torch.cat([w_gate, w_up], dim=1).contiguous()          # [L, 2I, H]: tensor b = 2e + p
     q1, sf1, gs_pair = nvfp4_quantize(gate_up.view(2 * L, I, H))
+    del gate_up
     w1_q = q1.view(L, 2 * I, H // 2)
     w1_sf = sf1.view(L, 2 * I, H // 16)
     gs_pair = gs_pair.view(L, 2)
     gs_gate, gs_up = gs_pair[:, 0].contiguous(), gs_pair[:, 1].contiguous()
     w1_gs = nvfp4_fold_scales(w1_sf, gs_gate, gs_up)
     w2_q, w2_sf, w2_gs = nvfp4_quantize(w_down.contiguous())
-    w = MoEWeights(w1_q, w1_sf, w1_gs, w2_q, w2_sf, w2_gs)
+    w = MoEWeights(nvfp4_pack_weights(w1_q, w1_sf), w1_gs, nvfp4_pack_weights(w2_q, w2_sf), w2_gs)
     w.gs_gate, w.gs_up = gs_gate, gs_up
+    if keep_unpacked:
+        w.w1_q, w.w1_sf, w.w2_q, w.w2_sf = w1_q, w1_sf, w2_q, w2_sf
     return w
 
 

@@ -28,7 +28,7 @@ extern "C" const char* nvfp4_status_string(int status) {
   }
 }
 
-extern "C" int nvfp4moe_version(void) { return 100; }
+extern "C" int nvfp4moe_version(void) { return 200; }
 
 extern "C" int32_t nvfp4_moe_tile_m(int32_t T, int32_t k, int32_t num_local) {
   // prefill-shaped when the slot capacity averages >= 64 rows per local expert
@@ -79,11 +79,13 @@ extern "C" int nvfp4_moe_forward(const nvfp4_moe_weights* w, const void* x_bf16,
   if (T < 0 || k < 1 || k > 64 || L < 1 || L > 4096 || H <= 0 || I <= 0) return NVFP4_ERR_SHAPE;
   if (H % 128 != 0 || I % 128 != 0) return NVFP4_ERR_SHAPE;
   if ((int64_t)T * k >= (1ll << 30)) return NVFP4_ERR_SHAPE;
-  if (!w->w1_q || !w->w1_sf || !w->w1_gs || !w->w2_q || !w->w2_sf || !w->w2_gs || !ws) return NVFP4_ERR_NULL;
+  // the GEMMs address one expert's packed weights and the activation rows with 32-bit offsets
+  if ((int64_t)2 * I * H / 32 * 18 >= (1ll << 31) || (int64_t)T * (H / 2) >= (1ll << 31) ||
+      (int64_t)T * k * (I / 2) >= (1ll << 31))
+    return NVFP4_ERR_SHAPE;
+  if (!w->w1 || !w->w1_gs || !w->w2 || !w->w2_gs || !ws) return NVFP4_ERR_NULL;
   if (T > 0 && (!x_bf16 || !topk_ids || !topk_w || !out_bf16)) return NVFP4_ERR_NULL;
-  if (!nvfp4_aligned16(w->w1_q) || !nvfp4_aligned16(w->w1_sf) || !nvfp4_aligned16(w->w2_q) ||
-      !nvfp4_aligned16(w->w2_sf) || !nvfp4_aligned16(ws))
-    return NVFP4_ERR_ALIGN;
+  if (!nvfp4_aligned16(w->w1) || !nvfp4_aligned16(w->w2) || !nvfp4_aligned16(ws)) return NVFP4_ERR_ALIGN;
   if (T > 0 && (!nvfp4_aligned16(x_bf16) || !nvfp4_aligned16(out_bf16))) return NVFP4_ERR_ALIGN;
   if (ws_bytes < nvfp4_moe_ws_bytes(T, k, H, I, L)) return NVFP4_ERR_WORKSPACE;
 
@@ -123,7 +125,7 @@ extern "C" int nvfp4_moe_forward(const nvfp4_moe_weights* w, const void* x_bf16,
     return st;
   if (cap > 0) {
     // a4/a5: L1 with the fused SiLU*up epilogue and amax of h
-    if ((st = nvfp4_launch_grouped_gemm(x_q, x_sf, slot_token, &scalars[0], w->w1_q, w->w1_sf, w->w1_gs, offsets,
+    if ((st = nvfp4_launch_grouped_gemm(x_q, x_sf, slot_token, &scalars[0], w->w1, w->w1_gs, offsets,
                                         tiles, L, cap, 2 * I, H, tile_m, NVFP4_EPI_SILU_MUL, h, &scalars[1],
                                         stream)))
       return st;
@@ -133,7 +135,7 @@ extern "C" int nvfp4_moe_forward(const nvfp4_moe_weights* w, const void* x_bf16,
     return st;
   if (cap > 0) {
     // a7: L2 in slot order
-    if ((st = nvfp4_launch_grouped_gemm(h_q, h_sf, nullptr, &scalars[2], w->w2_q, w->w2_sf, w->w2_gs, offsets,
+    if ((st = nvfp4_launch_grouped_gemm(h_q, h_sf, nullptr, &scalars[2], w->w2, w->w2_gs, offsets,
                                         tiles, L, cap, H, I, tile_m, NVFP4_EPI_BF16, y, nullptr, stream)))
       return st;
   }

@@ -22,12 +22,15 @@
 // Structure: a persistent grid walks work items (row tile from the device
 // tile table x column tile); block ids are remapped so that each XCD (own L2)
 // takes a contiguous run of items, which share the row tile's activations.
-// Each item streams K in stages of 128: FP4 bytes and scale bytes of the row
-// and column tiles go global -> registers -> LDS (double buffered, next stage
-// loaded while the current one is multiplied); every wave decodes its own
-// fragments from LDS. Within a 128-wide stage, lane half g of a wave takes
-// the contiguous K range [64g, 64g + 64) across the 8 MFMA steps; A and B use
-// the same assignment, so each MFMA step still sums matching K indices.
+// Each item streams K in stages of 128. The row tile's activations (row-major
+// NVFP4, gathered through the slot's token) go global -> registers -> LDS as
+// fp16, double buffered; every wave reads its A fragments from LDS. Weights
+// are stored pre-packed in MFMA fragment order (nvfp4_pack_weights), so each
+// wave streams its own 32-row subtiles global -> registers with every load
+// instruction reading 1 KB (or 256 B of scales) contiguously, P stages ahead.
+// Within a 128-wide stage, lane half g of a wave takes the contiguous K range
+// [64g, 64g + 64) across the 8 MFMA steps; A and B use the same assignment,
+// so each MFMA step still sums matching K indices.
 #include "common.h"
 #include "internal.h"
 
@@ -35,6 +38,12 @@ namespace nvfp4 {
 
 constexpr int kBK = 128;        // K elements per stage
 constexpr int kAPitch = 272;    // LDS bytes per fp16 A row of a stage (256 + 16 padding)
+// Packed weights: one chunk per (matrix, 32-row subtile, 128-wide K stage):
+// [h = 0, 1][lane 0..63][16 B] FP4 bytes, then [lane 0..63][4 B] scales, where
+// lane l holds row 32*sub + l%32, FP4 bytes [32*(l/32) + 16*h, +16) of the
+// stage's 64 bytes and scale bytes [4*(l/32), +4) of the stage's 8.
+constexpr int kPackChunk = 2304;
+constexpr int kPackScaleOff = 2048;
 
 template <int SUB_M, int SUB_N, int WAVES, int P>
 struct GemmCfg {
@@ -108,10 +117,9 @@ __device__ __forceinline__ float silu_f32(float g) { return g * __builtin_amdgcn
 template <int SUB_M, int SUB_N, int WAVES, int P, int EPI>
 __global__ __launch_bounds__(64 * WAVES) void grouped_gemm_kernel(
     const uint8_t* __restrict__ a_q, const uint8_t* __restrict__ a_sf, const int32_t* __restrict__ a_row_index,
-    const float* __restrict__ a_gs, const uint8_t* __restrict__ b_q, const uint8_t* __restrict__ b_sf,
-    const float* __restrict__ b_gs, const int32_t* __restrict__ offsets, const int32_t* __restrict__ tile_table,
-    int max_tiles, int N, int K, int n_out, int n_ntiles, int col_fastest, uint16_t* __restrict__ d,
-    float* __restrict__ amax_out) {
+    const float* __restrict__ a_gs, const uint8_t* __restrict__ b_packed, const float* __restrict__ b_gs,
+    const int32_t* __restrict__ offsets, const int32_t* __restrict__ tile_table, int max_tiles, int N, int K,
+    int n_out, int n_ntiles, int col_fastest, uint16_t* __restrict__ d, float* __restrict__ amax_out) {
   using C = GemmCfg<SUB_M, SUB_N, WAVES, P>;
   extern __shared__ __align__(16) uint8_t lds[];
   const int tid = threadIdx.x;
@@ -127,6 +135,7 @@ __global__ __launch_bounds__(64 * WAVES) void grouped_gemm_kernel(
   const int slot = (G % kXcds == 0) ? (blockIdx.x % kXcds) * (G / kXcds) + blockIdx.x / kXcds : blockIdx.x;
   const int64_t pitch = K / 2, spitch = K / 16;
   const int nstages = K / kBK;
+  const uint32_t b_bytes = (uint32_t)((int64_t)N * K / 32 * 18);  // one expert's packed weights
   // activation rows: every valid row offset is below 2^31 (checked on the host)
   const __amdgpu_buffer_rsrc_t ra_q = make_rsrc(a_q, 0x7FFFFFFFu);
   const __amdgpu_buffer_rsrc_t ra_s = make_rsrc(a_sf, 0x7FFFFFFFu);
@@ -143,8 +152,7 @@ __global__ __launch_bounds__(64 * WAVES) void grouped_gemm_kernel(
     const int r0 = tile_table[2 + 2 * mt];
     const int r_end = min(r0 + C::BM, offsets[e + 1]);
     const float alpha = a_gs[0] * b_gs[e];
-    const __amdgpu_buffer_rsrc_t rb_q = make_rsrc(b_q + (size_t)e * N * pitch, (uint32_t)(N * pitch));
-    const __amdgpu_buffer_rsrc_t rb_s = make_rsrc(b_sf + (size_t)e * N * spitch, (uint32_t)(N * spitch));
+    const __amdgpu_buffer_rsrc_t rbw = make_rsrc(b_packed + (size_t)e * b_bytes, b_bytes);
 
     // activation staging tasks of this thread: 16 FP4 bytes + 2 scale bytes per
     // stage at byte offsets a_off / as_off (out of range for rows past the group)
@@ -162,7 +170,7 @@ __global__ __launch_bounds__(64 * WAVES) void grouped_gemm_kernel(
     }
     // weight rows: subtile j of this wave covers 32 consecutive rows starting at the
     // wave-uniform row0[j] (-1 when past the end); lane lr takes row0[j] + lr and
-    // lane half lg reads bytes [32 lg, 32 lg + 32) of each 64-byte stage
+    // lane half lg holds bytes [32 lg, 32 lg + 32) of each 64-byte stage
     int row0[SUB_N];
 #pragma unroll
     for (int j = 0; j < SUB_N; ++j) {
@@ -175,8 +183,8 @@ __global__ __launch_bounds__(64 * WAVES) void grouped_gemm_kernel(
         row0[j] = col0 < N ? col0 : -1;
       }
     }
-    const uint32_t b_lane = (uint32_t)lr * (uint32_t)pitch + 32u * lg;
-    const uint32_t bs_lane = (uint32_t)lr * (uint32_t)spitch + 4u * lg;
+    const uint32_t b_lane = 16u * (uint32_t)lane;
+    const uint32_t bs_lane = kPackScaleOff + 4u * (uint32_t)lane;
 
     // Register rings of P stages for both operands. Global loads complete in
     // issue order, so stage s's activation and weight loads are issued
@@ -216,11 +224,12 @@ __global__ __launch_bounds__(64 * WAVES) void grouped_gemm_kernel(
 #pragma unroll
       for (int j = 0; j < SUB_N; ++j) {
         const bool ok = in && row0[j] >= 0;
-        const uint32_t o = ok ? (uint32_t)row0[j] * (uint32_t)pitch + b_lane + s * 64 : kOutOfRange;
-        const uint32_t os = ok ? (uint32_t)row0[j] * (uint32_t)spitch + bs_lane + s * 8 : kOutOfRange;
-        rb[slot_][j][0] = buf_load16(rb_q, o);
-        rb[slot_][j][1] = buf_load16(rb_q, o + 16);
-        rsb[slot_][j] = buf_load4(rb_s, os);
+        const uint32_t chunk = ((uint32_t)(row0[j] >> 5) * (uint32_t)nstages + (uint32_t)s) * kPackChunk;
+        const uint32_t o = ok ? chunk + b_lane : kOutOfRange;   // kOutOfRange + 1024 stays out of range
+        const uint32_t os = ok ? chunk + bs_lane : kOutOfRange;
+        rb[slot_][j][0] = buf_load16(rbw, o);
+        rb[slot_][j][1] = buf_load16(rbw, o + 1024);
+        rsb[slot_][j] = buf_load4(rbw, os);
       }
     };
 
@@ -325,7 +334,7 @@ __global__ __launch_bounds__(64 * WAVES) void grouped_gemm_kernel(
 
 template <int SUB_M, int SUB_N, int WAVES, int P, int EPI>
 static int launch_cfg(const uint8_t* a_q, const uint8_t* a_sf, const int32_t* a_row_index, const float* a_gs,
-                      const uint8_t* b_q, const uint8_t* b_sf, const float* b_gs, const int32_t* offsets,
+                      const uint8_t* b_packed, const float* b_gs, const int32_t* offsets,
                       const int32_t* tile_table, int32_t num_local, int32_t rows_cap, int32_t N, int32_t K,
                       void* d, float* amax_out, hipStream_t stream, int col_fastest = 0) {
   using C = GemmCfg<SUB_M, SUB_N, WAVES, P>;
@@ -353,7 +362,7 @@ static int launch_cfg(const uint8_t* a_q, const uint8_t* a_sf, const int32_t* a_
   if (grid >= kXcds) grid -= grid % kXcds;
   if (grid < 1) grid = 1;
   hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(C::THREADS), C::LDS, stream, a_q, a_sf, a_row_index, a_gs,
-                     b_q, b_sf, b_gs, offsets, tile_table, max_tiles, N, K, n_out, n_ntiles, col_fastest,
+                     b_packed, b_gs, offsets, tile_table, max_tiles, N, K, n_out, n_ntiles, col_fastest,
                      reinterpret_cast<uint16_t*>(d), amax_out);
   NVFP4_CHECK_LAUNCH();
   return NVFP4_OK;
@@ -368,11 +377,11 @@ using namespace nvfp4;
 //   64  prefill-shaped: 4 waves, each 64 x 128, 3 stages in flight
 //   128 large groups: 4 waves, each 128 x 64, 3 stages in flight
 int nvfp4_launch_grouped_gemm(const uint8_t* a_q, const uint8_t* a_sf, const int32_t* a_row_index,
-                              const float* a_gs, const uint8_t* b_q, const uint8_t* b_sf, const float* b_gs,
+                              const float* a_gs, const uint8_t* b_packed, const float* b_gs,
                               const int32_t* offsets, const int32_t* tile_table, int32_t num_local,
                               int32_t rows_cap, int32_t N, int32_t K, int32_t tile_m, int32_t epilogue, void* d,
                               float* amax_out, hipStream_t stream) {
-#define NVFP4_GEMM_ARGS a_q, a_sf, a_row_index, a_gs, b_q, b_sf, b_gs, offsets, tile_table, num_local, rows_cap, \
+#define NVFP4_GEMM_ARGS a_q, a_sf, a_row_index, a_gs, b_packed, b_gs, offsets, tile_table, num_local, rows_cap, \
                         N, K, d, amax_out, stream
 #define NVFP4_GEMM_CFG(SM, SN, W, PF)                                                          \
   return epilogue == NVFP4_EPI_SILU_MUL ? launch_cfg<SM, SN, W, PF, NVFP4_EPI_SILU_MUL>(NVFP4_GEMM_ARGS) \
@@ -388,7 +397,7 @@ int nvfp4_launch_grouped_gemm(const uint8_t* a_q, const uint8_t* a_sf, const int
 }
 
 extern "C" int nvfp4_grouped_gemm(const uint8_t* a_q, const uint8_t* a_sf, const int32_t* a_row_index,
-                                  const float* a_gs, const uint8_t* b_q, const uint8_t* b_sf, const float* b_gs,
+                                  const float* a_gs, const uint8_t* b_packed, const float* b_gs,
                                   const int32_t* offsets, const int32_t* tile_table, int32_t num_local,
                                   int32_t rows_cap, int32_t N, int32_t K, int32_t tile_m, int32_t epilogue, void* d,
                                   float* amax_out, void* stream) {
@@ -396,14 +405,59 @@ extern "C" int nvfp4_grouped_gemm(const uint8_t* a_q, const uint8_t* a_sf, const
   if (num_local < 1 || rows_cap < 0 || N <= 0 || K <= 0 || K % kBK != 0 || N % 64 != 0) return NVFP4_ERR_SHAPE;
   if (epilogue == NVFP4_EPI_SILU_MUL && N % 128 != 0) return NVFP4_ERR_SHAPE;
   if (tile_m != 32 && tile_m != 64 && tile_m != 128) return NVFP4_ERR_SHAPE;
-  if (!a_q || !a_sf || !a_gs || !b_q || !b_sf || !b_gs || !offsets || !tile_table || !d) return NVFP4_ERR_NULL;
+  if (!a_q || !a_sf || !a_gs || !b_packed || !b_gs || !offsets || !tile_table || !d) return NVFP4_ERR_NULL;
   if (epilogue == NVFP4_EPI_SILU_MUL && !amax_out) return NVFP4_ERR_NULL;
-  if (!nvfp4_aligned16(a_q) || !nvfp4_aligned16(a_sf) || !nvfp4_aligned16(b_q) || !nvfp4_aligned16(b_sf) ||
-      !nvfp4_aligned16(d))
+  if (!nvfp4_aligned16(a_q) || !nvfp4_aligned16(a_sf) || !nvfp4_aligned16(b_packed) || !nvfp4_aligned16(d))
     return NVFP4_ERR_ALIGN;
-  // buffer offsets are 32-bit: activation row offsets and one expert's weights stay below 2^31
-  if ((int64_t)rows_cap * (K / 2) >= (1ll << 31) || (int64_t)N * (K / 2) >= (1ll << 31)) return NVFP4_ERR_SHAPE;
+  // buffer offsets are 32-bit: activation row offsets and one expert's packed weights stay below 2^31
+  if ((int64_t)rows_cap * (K / 2) >= (1ll << 31) || (int64_t)N * K / 32 * 18 >= (1ll << 31)) return NVFP4_ERR_SHAPE;
   if (rows_cap == 0) return NVFP4_OK;
-  return nvfp4_launch_grouped_gemm(a_q, a_sf, a_row_index, a_gs, b_q, b_sf, b_gs, offsets, tile_table, num_local,
+  return nvfp4_launch_grouped_gemm(a_q, a_sf, a_row_index, a_gs, b_packed, b_gs, offsets, tile_table, num_local,
                                    rows_cap, N, K, tile_m, epilogue, d, amax_out, (hipStream_t)stream);
+}
+
+// ------------------------------------------------------------ weight packing
+
+// One thread per (matrix, subtile, stage, lane): moves the lane's 32 FP4 bytes
+// and 4 scale bytes from the row-major tensors into the packed chunk.
+__global__ __launch_bounds__(256) void pack_kernel(const uint8_t* __restrict__ q, const uint8_t* __restrict__ sf,
+                                                   int64_t total, int N, int K, uint8_t* __restrict__ out) {
+  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= total) return;
+  const int nst = K / kBK, nsub = N / 32;
+  const int l = (int)(idx & 63);
+  int64_t rest = idx >> 6;
+  const int c = (int)(rest % nst);
+  rest /= nst;
+  const int sub = (int)(rest % nsub);
+  const int64_t b = rest / nsub;
+  const int64_t row = b * N + sub * 32 + (l & 31);
+  const int g = l >> 5;
+  const uint4* src = reinterpret_cast<const uint4*>(q + row * (K / 2) + 64 * c + 32 * g);
+  const uint32_t s = *reinterpret_cast<const uint32_t*>(sf + row * (K / 16) + 8 * c + 4 * g);
+  uint8_t* dst = out + ((b * nsub + sub) * nst + c) * kPackChunk;
+  *reinterpret_cast<uint4*>(dst + 16 * l) = src[0];
+  *reinterpret_cast<uint4*>(dst + 1024 + 16 * l) = src[1];
+  *reinterpret_cast<uint32_t*>(dst + kPackScaleOff + 4 * l) = s;
+}
+
+extern "C" int64_t nvfp4_packed_bytes(int64_t B, int64_t N, int64_t K) {
+  if (B < 0 || N <= 0 || K <= 0 || N % 32 != 0 || K % kBK != 0) return -1;
+  return B * N * K / 32 * 18;
+}
+
+extern "C" int nvfp4_pack_weights(const uint8_t* q, const uint8_t* sf, int64_t B, int64_t N, int64_t K,
+                                  uint8_t* packed, void* stream) {
+  if (B < 0 || N <= 0 || K <= 0 || N % 32 != 0 || K % kBK != 0 || N >= (1ll << 30) || K >= (1ll << 30))
+    return NVFP4_ERR_SHAPE;
+  if (!q || !sf || !packed) return NVFP4_ERR_NULL;
+  if (!nvfp4_aligned16(q) || !nvfp4_aligned16(sf) || !nvfp4_aligned16(packed)) return NVFP4_ERR_ALIGN;
+  const int64_t total = B * (N / 32) * (K / kBK) * 64;
+  if (total == 0) return NVFP4_OK;
+  const int64_t blocks = (total + 255) / 256;
+  if (blocks >= (1ll << 31)) return NVFP4_ERR_SHAPE;
+  hipLaunchKernelGGL(pack_kernel, dim3((unsigned)blocks), dim3(256), 0, (hipStream_t)stream, q, sf, total, (int)N,
+                     (int)K, packed);
+  NVFP4_CHECK_LAUNCH();
+  return NVFP4_OK;
 }

@@ -20,7 +20,7 @@ int nvfp4_launch_route(const int32_t* topk_ids, const float* topk_w, int32_t T, 
                        void* ws, hipStream_t stream);
 
 int nvfp4_launch_grouped_gemm(const uint8_t* a_q, const uint8_t* a_sf, const int32_t* a_row_index,
-                              const float* a_gs, const uint8_t* b_q, const uint8_t* b_sf, const float* b_gs,
+                              const float* a_gs, const uint8_t* b_packed, const float* b_gs,
                               const int32_t* offsets, const int32_t* tile_table, int32_t num_local,
                               int32_t rows_cap, int32_t N, int32_t K, int32_t tile_m, int32_t epilogue, void* d,
                               float* amax_out, hipStream_t stream);

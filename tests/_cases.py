@@ -56,3 +56,18 @@ def quant_case(name):
     if name == "quant_full":
         return W.make_quant_input(W.get_config("quant"))
     raise KeyError(name)
+
+
+def pack_weights_np(q, sf):
+    """The packed weight order of nvfp4_pack_weights, written from its
+    definition in include/nvfp4moe.h with array reshapes:
+    q uint8 [B, N, K/2], sf uint8 [B, N, K/16] -> uint8 [B, N/32, K/128, 2304]."""
+    B, N, Kh = q.shape
+    nsub, nst = N // 32, (2 * Kh) // 128
+    # row = 32*sub + r; FP4 byte 64c + 32g + 16h + i  ->  chunk byte h*1024 + 16*(32g + r) + i
+    qr = q.reshape(B, nsub, 32, nst, 2, 2, 16)                      # B, sub, r, c, g, h, i
+    part_q = qr.transpose(0, 1, 3, 5, 4, 2, 6).reshape(B, nsub, nst, 2048)
+    # scale byte 8c + 4g + i  ->  chunk byte 2048 + 4*(32g + r) + i
+    sr = sf.reshape(B, nsub, 32, nst, 2, 4)                         # B, sub, r, c, g, i
+    part_s = sr.transpose(0, 1, 3, 4, 2, 5).reshape(B, nsub, nst, 256)
+    return np.ascontiguousarray(np.concatenate([part_q, part_s], axis=-1))

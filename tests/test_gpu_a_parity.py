@@ -12,7 +12,7 @@ import torch
 
 import oracle as O
 import workloads as W
-from _cases import quant_case
+from _cases import pack_weights_np, quant_case
 
 pytestmark = pytest.mark.gpu
 TOL = 1e-2
@@ -153,6 +153,29 @@ def test_scatter_bit_exact(nv, T, k, H):
     assert np.array_equal(bits_of(out), O.scatter(y, ts, w))
 
 
+# ------------------------------------------------------------- weight packing
+
+@pytest.mark.parametrize("shape", [(1, 32, 128), (3, 96, 384), (2, 6144 // 8, 7168 // 4)])
+def test_pack_weights(nv, shape):
+    B, N, K = shape
+    rng = np.random.default_rng(N + K)
+    q = rng.integers(0, 256, (B, N, K // 2), dtype=np.uint8)
+    sf = rng.integers(0, 256, (B, N, K // 16), dtype=np.uint8)
+    log(f"pack B={B} N={N} K={K}")
+    got = nv.nvfp4_pack_weights(to_dev(q), to_dev(sf))
+    torch.cuda.synchronize()
+    assert got.numel() == nv.nvfp4_packed_bytes(B, N, K)
+    assert np.array_equal(got.cpu().numpy(), pack_weights_np(q, sf))
+
+
+def test_pack_weights_rejects_bad_shapes(nv):
+    q = torch.zeros((1, 48, 64), dtype=torch.uint8, device=DEV)
+    sf = torch.zeros((1, 48, 8), dtype=torch.uint8, device=DEV)
+    with pytest.raises(ValueError):
+        nv.nvfp4_pack_weights(q, sf)
+    assert nv.nvfp4_packed_bytes(1, 48, 128) == -1
+
+
 # --------------------------------------------------------------- grouped GEMM
 
 def _gemm_inputs(seed, L, N, K, T, counts, gather):
@@ -195,8 +218,9 @@ def test_grouped_gemm(nv, case, tile_m, epi):
     canary = torch.full((cap, n_out), -7.0, dtype=torch.bfloat16, device=DEV)
     amax = torch.zeros(1, dtype=torch.float32, device=DEV)
     log(f"gemm {case} tile_m={tile_m} epi={epi} S={S}")
+    b_packed = nv.nvfp4_pack_weights(to_dev(b_q), to_dev(b_sf))
     d = nv.nvfp4_grouped_gemm(to_dev(a_q), to_dev(a_sf), None if ri is None else to_dev(ri), to_dev(a_gs),
-                              to_dev(b_q), to_dev(b_sf), to_dev(b_gs), to_dev(offsets), to_dev(tt), cap, tile_m,
+                              b_packed, to_dev(b_gs), to_dev(offsets), to_dev(tt), cap, tile_m,
                               epilogue=epi, d=canary, amax_out=amax if epi == 1 else None)
     torch.cuda.synchronize()
     got = d.float().cpu().numpy()
@@ -237,10 +261,12 @@ def _deq_ref(P, cfg, x, ids, w):
 def test_layer(nv, name):
     cfg, ids, w, x, wg, wu, wd = _layer_inputs(name)
     log(f"layer {name} T={cfg.tokens} k={cfg.top_k} L={cfg.num_local} H={cfg.hidden} I={cfg.inter}")
-    weights = nv.prepare_weights(to_bf16(wg), to_bf16(wu), to_bf16(wd))
+    weights = nv.prepare_weights(to_bf16(wg), to_bf16(wu), to_bf16(wd), keep_unpacked=True)
     P = O.prepare_weights(wg, wu, wd)
     for key in ("w1_q", "w1_sf", "w1_gs", "w2_q", "w2_sf", "w2_gs"):
         assert np.array_equal(getattr(weights, key).cpu().numpy(), P[key]), key
+    assert np.array_equal(weights.w1.cpu().numpy(), pack_weights_np(P["w1_q"], P["w1_sf"]))
+    assert np.array_equal(weights.w2.cpu().numpy(), pack_weights_np(P["w2_q"], P["w2_sf"]))
     T, k = ids.shape
     H = cfg.hidden
     lay = nv.nvfp4_moe_ws_layout(T, k, H, cfg.inter, cfg.num_local)

@@ -19,6 +19,7 @@ import torch
 
 import oracle as O
 import workloads as W
+from _cases import pack_weights_np
 
 pytestmark = [pytest.mark.gpu, pytest.mark.timeout(900)]
 TOL = 1e-2
@@ -75,7 +76,7 @@ class Shard:
         self.wg, self.wu, self.wd = W.make_weights(weight_cfg)
         log(f"{weight_cfg.name} weights generated in {time.time() - t:.1f}s")
         t = time.time()
-        self.gpu = nv.prepare_weights(to_bf16(self.wg), to_bf16(self.wu), to_bf16(self.wd))
+        self.gpu = nv.prepare_weights(to_bf16(self.wg), to_bf16(self.wu), to_bf16(self.wd), keep_unpacked=True)
         torch.cuda.synchronize()
         with ThreadPoolExecutor(THREADS) as ex:
             self.P = O.prepare_weights(self.wg, self.wu, self.wd, map_fn=ProgressMap(ex, "oracle weights"))
@@ -95,6 +96,8 @@ def skewed(nv):
 def _check_weights(nv, sh):
     for key in ("w1_q", "w1_sf", "w1_gs", "w2_q", "w2_sf", "w2_gs"):
         assert np.array_equal(getattr(sh.gpu, key).cpu().numpy(), sh.P[key]), key
+    assert np.array_equal(sh.gpu.w1.cpu().numpy(), pack_weights_np(sh.P["w1_q"], sh.P["w1_sf"]))
+    assert np.array_equal(sh.gpu.w2.cpu().numpy(), pack_weights_np(sh.P["w2_q"], sh.P["w2_sf"]))
 
 
 def _touched_only(cfg, ids):

@@ -24,7 +24,7 @@ def _declared():
 def test_header_declares_the_boundary():
     names = _declared()
     for n in ("nvfp4_quantize", "moe_route_slots", "nvfp4_grouped_gemm", "nvfp4_moe_forward",
-              "moe_weighted_scatter", "nvfp4_fold_scales"):
+              "moe_weighted_scatter", "nvfp4_fold_scales", "nvfp4_pack_weights", "nvfp4_packed_bytes"):
         assert n in names
 
 
@@ -43,7 +43,7 @@ def test_status_strings_and_sizes():
     nv = _lib()
     assert nv._status_string(0) == b"ok"
     assert b"workspace" in nv._status_string(4)
-    assert nv.version() == 100
+    assert nv.version() == 200
     assert nv.nvfp4_tile_table_len(512, 48, 32) == 1 + 2 * (16 + 48)
     lay = nv.nvfp4_moe_ws_layout(64, 8, 7168, 3072, 48)
     offs = [lay[r] for r in nv.WS_REGIONS]
@@ -71,17 +71,28 @@ def test_invalid_arguments_are_rejected_before_launch():
     assert nv._route(buf, buf, 4, 2, 0, 8, 48, *args, buf, 1 << 20, s) == 2
     assert nv._route(buf, buf, 4, 2, 0, 8, 32, null, *args[1:], buf, 1 << 20, s) == 1
     # grouped GEMM: K not a multiple of 128, unknown epilogue, odd tile height
-    g = [buf] * 9
+    g = [buf] * 8
     assert nv._gemm(*g, 8, 64, 256, 96, 32, 0, buf, null, s) == 2
     assert nv._gemm(*g, 8, 64, 256, 256, 32, 7, buf, null, s) == 6
     assert nv._gemm(*g, 8, 64, 256, 256, 48, 0, buf, null, s) == 2
     assert nv._gemm(*g, 8, 64, 256, 256, 32, 1, buf, null, s) == 1   # SiLU epilogue needs amax_out
+    # packed size / pack: N not a multiple of 32, K not a multiple of 128, NULL input, misaligned output
+    assert nv.nvfp4_packed_bytes(2, 64, 256) == 2 * 64 * 256 * 9 // 16
+    assert nv.nvfp4_packed_bytes(1, 48, 256) == -1 and nv.nvfp4_packed_bytes(1, 64, 192) == -1
+    assert nv._pack(buf, buf, 1, 48, 256, buf, s) == 2
+    assert nv._pack(buf, buf, 1, 64, 192, buf, s) == 2
+    assert nv._pack(null, buf, 1, 64, 256, buf, s) == 1
+    assert nv._pack(buf, buf, 1, 64, 256, odd, s) == 3
     # scatter / fold
     assert nv._scatter(buf, buf, buf, 4, 2, 12, buf, s) == 2
     assert nv._fold(null, buf, buf, buf, 4, 64, 256, s) == 1
     # forward: NULL weights struct, bad hidden
     assert nv._forward(None, buf, 4, buf, buf, 2, 0, buf, buf, 1 << 30, s) == 1
-    w = nv._Weights(8, 200, 128, 4096, 4096, 4096, 4096, 4096, 4096)
+    w = nv._Weights(8, 200, 128, 4096, 4096, 4096, 4096)
     assert nv._forward(ctypes.byref(w), buf, 4, buf, buf, 2, 0, buf, buf, 1 << 30, s) == 2
-    w = nv._Weights(8, 256, 128, 4096, 4096, 4096, 4096, 4096, 4096)
+    w = nv._Weights(8, 256, 128, 4096, 4096, 4096, 4096)
     assert nv._forward(ctypes.byref(w), buf, 4, buf, buf, 2, 0, buf, buf, 16, s) == 4
+    w = nv._Weights(8, 256, 128, 4096, 4096, None, 4096)
+    assert nv._forward(ctypes.byref(w), buf, 4, buf, buf, 2, 0, buf, buf, 1 << 30, s) == 1
+    w = nv._Weights(8, 256, 128, 4097, 4096, 4096, 4096)
+    assert nv._forward(ctypes.byref(w), buf, 4, buf, buf, 2, 0, buf, buf, 1 << 30, s) == 3
