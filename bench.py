@@ -67,6 +67,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--config", default="prefill", choices=["prefill", "decode", "skewed"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--settle-ms", type=float, default=300.0,
+                    help="untimed GPU time spent on the workload before the warmup steps, so that "
+                         "the clocks leave their start-of-load transient (steady state is timed)")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy (elementwise negate) three times, "
@@ -119,6 +122,7 @@ def main():
         def step():
             nv.nvfp4_moe_forward(weights, d_x, d_ids, d_w, cfg_.expert_start, out=out, ws=ws)
 
+        settle(step, args.settle_ms)
         for _ in range(warmup):
             step()
         torch.cuda.synchronize()
@@ -144,8 +148,8 @@ def main():
         stream = torch.cuda.current_stream()
         ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         n_l1 = max(steps, 5)
-        for _ in range(2):
-            nv.nvfp4_grouped_gemm(*gargs, cap, tile_m, nv.EPI_SILU_MUL, d=h, amax_out=amax)
+        settle(lambda: nv.nvfp4_grouped_gemm(*gargs, cap, tile_m, nv.EPI_SILU_MUL, d=h, amax_out=amax),
+               args.settle_ms / 2)
         ev0.record(stream)
         for _ in range(n_l1):
             nv.nvfp4_grouped_gemm(*gargs, cap, tile_m, nv.EPI_SILU_MUL, d=h, amax_out=amax)
@@ -203,9 +207,142 @@ def main():
             "l1_gemm_ms": round(rd["l1_ms"], 4), "l1_gemm_GBs": round(l1g, 1),
             "l1_gemm_hbm_frac": round(l1g / PEAK_HBM_GBS, 4),
         }
+    if cfg.name == "prefill" and not args.no_decode:
+        result["decode"]["flushed"] = decode_flushed(nv, weights, W.get_config("decode"), dev)
+        result["decode"]["graph"] = decode_graph(nv, weights, W.get_config("decode"), dev, max(args.steps, 50))
+        result["quantize"] = quantize_c1(nv, W, dev, args.settle_ms)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(cfg, ids, w, x, wg, wu, wd, T)
     print(json.dumps(result), flush=True)
+
+
+def decode_flushed(nv, weights, dcfg, dev, steps=30):
+    """Decode shard with the last-level cache (256 MB) flushed before every step:
+    each step timed alone with events, after a 512 MB write outside the events."""
+    import torch
+    import workloads as W
+    ids, w = W.make_router(dcfg)
+    x = W.make_activations(dcfg)
+    T, k = ids.shape
+    d_x = torch.from_numpy(x.view(np.int16)).view(torch.bfloat16).to(dev)
+    d_ids, d_w = torch.from_numpy(ids).to(dev), torch.from_numpy(w).to(dev)
+    lay = nv.nvfp4_moe_ws_layout(T, k, dcfg.hidden, dcfg.inter, dcfg.num_local)
+    ws = torch.empty(lay["end"], dtype=torch.uint8, device=dev)
+    out = torch.empty((T, dcfg.hidden), dtype=torch.bfloat16, device=dev)
+    scratch = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+    # flush, then the step between two events, all enqueued without host waits,
+    # so the host's launch latency is not inside the events
+    evs = []
+    for i in range(steps + 3):
+        scratch.fill_(i & 0xFF)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        nv.nvfp4_moe_forward(weights, d_x, d_ids, d_w, dcfg.expert_start, out=out, ws=ws)
+        e1.record()
+        evs.append((e0, e1))
+    torch.cuda.synchronize()
+    times = [a.elapsed_time(b) for a, b in evs[3:]]
+    counts = nv.ws_view(ws, lay, "counts", torch.int32, (dcfg.num_local,)).cpu().numpy()
+    touched = int((counts > 0).sum())
+    H, I = dcfg.hidden, dcfg.inter
+    bytes_w = touched * (2 * I * (H // 2 + H // 16) + H * (I // 2 + I // 16))
+    med = float(np.median(times))
+    return {"ms_per_step_median": round(med, 4), "ms_p10": round(float(np.percentile(times, 10)), 4),
+            "ms_p90": round(float(np.percentile(times, 90)), 4),
+            "tokens_per_s": round(T / (med * 1e-3), 1),
+            "layer_weight_GBs": round(bytes_w / (med * 1e-3) / 1e9, 1),
+            "layer_hbm_frac": round(bytes_w / (med * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
+
+
+def decode_graph(nv, weights, dcfg, dev, steps):
+    """Decode shard with the whole layer captured once in a HIP graph (through
+    torch.cuda.graph) and replayed back to back: the launch latency of the
+    layer's small kernels is what this removes."""
+    import torch
+    import workloads as W
+    ids, w = W.make_router(dcfg)
+    x = W.make_activations(dcfg)
+    T, k = ids.shape
+    d_x = torch.from_numpy(x.view(np.int16)).view(torch.bfloat16).to(dev)
+    d_ids, d_w = torch.from_numpy(ids).to(dev), torch.from_numpy(w).to(dev)
+    lay = nv.nvfp4_moe_ws_layout(T, k, dcfg.hidden, dcfg.inter, dcfg.num_local)
+    ws = torch.empty(lay["end"], dtype=torch.uint8, device=dev)
+    out = torch.empty((T, dcfg.hidden), dtype=torch.bfloat16, device=dev)
+    fwd = lambda: nv.nvfp4_moe_forward(weights, d_x, d_ids, d_w, dcfg.expert_start, out=out, ws=ws)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        for _ in range(3):
+            fwd()
+    torch.cuda.current_stream().wait_stream(s)
+    eager = out.clone()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        fwd()
+    for _ in range(5):
+        g.replay()
+    torch.cuda.synchronize()
+    same = bool(torch.equal(out.view(torch.int16), eager.view(torch.int16)))
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    counts = nv.ws_view(ws, lay, "counts", torch.int32, (dcfg.num_local,)).cpu().numpy()
+    touched = int((counts > 0).sum())
+    H, I = dcfg.hidden, dcfg.inter
+    bytes_w = touched * (2 * I * (H // 2 + H // 16) + H * (I // 2 + I // 16))
+    return {"ms_per_step": round(ms, 4), "tokens_per_s": round(T / (ms * 1e-3), 1),
+            "layer_weight_GBs": round(bytes_w / (ms * 1e-3) / 1e9, 1),
+            "layer_hbm_frac": round(bytes_w / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+            "replay_equals_eager": same}
+
+
+def quantize_c1(nv, W, dev, settle_ms, reps=50):
+    """Activation quantizer alone on the 4096 x 7168 Student-t(3) tensor with
+    +-2000 outliers: HBM bytes of one ideal pass (read x once, write codes,
+    scales and gs) over the measured time."""
+    import torch
+    qc = W.get_config("quant")
+    xq = W.make_quant_input(qc)
+    d = torch.from_numpy(xq.view(np.int16)).view(torch.bfloat16).to(dev)
+    M, K = xq.shape
+    q = torch.empty((1, M, K // 2), dtype=torch.uint8, device=dev)
+    sf = torch.empty((1, M, K // 16), dtype=torch.uint8, device=dev)
+    gs = torch.empty(1, dtype=torch.float32, device=dev)
+    ws = torch.empty(max(nv.nvfp4_quantize_ws_bytes(1, M, K), 256), dtype=torch.uint8, device=dev)
+    fn = lambda: nv.nvfp4_quantize(d, q=q, sf=sf, gs=gs, ws=ws)
+    settle(fn, settle_ms / 4)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        fn()
+    e1.record()
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / reps
+    ideal = M * K * 2 + M * K // 2 + M * K // 16 + 4
+    return {"workload": f"activation quantizer alone, [{M}, {K}] Student-t(3) with 0.1% at +-2000",
+            "us_per_call": round(us, 2), "ideal_bytes": ideal,
+            "GBs": round(ideal / (us * 1e-6) / 1e9, 1), "hbm_frac": round(ideal / (us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4),
+            "gs": float(gs.item())}
+
+
+def settle(fn, ms):
+    """Run fn back to back for about ms milliseconds of GPU time (untimed)."""
+    import torch
+    if ms <= 0:
+        return
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    fn()
+    e1.record()
+    torch.cuda.synchronize()
+    n = max(1, int(ms / max(e0.elapsed_time(e1), 1e-3)))
+    for _ in range(min(n, 20000)):
+        fn()
+    torch.cuda.synchronize()
 
 
 def _counter_rows(d, counter):

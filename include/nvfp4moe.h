@@ -99,7 +99,7 @@ int nvfp4_quantize(const void* x_bf16, int64_t B, int64_t M, int64_t K, const fl
  *               contributes ceil(counts[e] / tile_m) tiles starting at
  *               offsets[e], offsets[e] + tile_m, ... in expert order.
  * ws: at least moe_route_ws_bytes(T, k, num_local) bytes.
- * Requires T >= 0, 1 <= k <= 64, 1 <= num_local <= 4096, tile_m in {16, 32, 64, 128, 256},
+ * Requires T >= 0, 1 <= k <= 64, 1 <= num_local <= 4096, tile_m a multiple of 16 in [16, 256],
  * T*k < 2^30.
  */
 size_t moe_route_ws_bytes(int32_t T, int32_t k, int32_t num_local);

@@ -59,7 +59,7 @@ extern "C" size_t nvfp4_moe_ws_layout(int32_t T, int32_t k, int32_t hidden, int3
   put(NVFP4_WS_H_Q, cap * inter / 2);
   put(NVFP4_WS_H_SF, cap * inter / 16);
   put(NVFP4_WS_Y, cap * hidden * 2);
-  put(NVFP4_WS_QUANT_SCRATCH, nvfp4_quant_ws_layout(1, nullptr));
+  put(NVFP4_WS_QUANT_SCRATCH, nvfp4_quant_ws_layout(1));
   o[NVFP4_WS_END] = p;
   if (off)
     for (int r = 0; r < NVFP4_WS_NREGIONS; ++r) off[r] = o[r];
@@ -114,10 +114,10 @@ extern "C" int nvfp4_moe_forward(const nvfp4_moe_weights* w, const void* x_bf16,
   const int32_t cap = T * k;
   int st;
 
-  // scalars: gs_x, amax_h, gs_h, reserved
-  if ((st = nvfp4_launch_fill_u32(reinterpret_cast<uint32_t*>(scalars), 4, 0u, stream))) return st;
-  // a1/a2: quantize x with its own global scale
-  if ((st = nvfp4_launch_quantize(x_bf16, 1, T, H, nullptr, nullptr, x_q, x_sf, &scalars[0], qws, stream)))
+  // a1/a2: quantize x with its own global scale; the amax pass also zeroes the
+  // scalars (gs_x, amax_h, gs_h, reserved) before anything reads them
+  if ((st = nvfp4_launch_quantize(x_bf16, 1, T, H, nullptr, nullptr, x_q, x_sf, &scalars[0], qws,
+                                  reinterpret_cast<uint32_t*>(scalars), 4, stream)))
     return st;
   // a3: route
   if ((st = nvfp4_launch_route(topk_ids, topk_w, T, k, expert_start, L, tile_m, counts, offsets, slot_token,
@@ -131,7 +131,8 @@ extern "C" int nvfp4_moe_forward(const nvfp4_moe_weights* w, const void* x_bf16,
       return st;
   }
   // a6: re-quantize the S valid rows of h with gs_h = amax_h / 2688
-  if ((st = nvfp4_launch_quantize(h, 1, cap, I, &scalars[1], &offsets[L], h_q, h_sf, &scalars[2], qws, stream)))
+  if ((st = nvfp4_launch_quantize(h, 1, cap, I, &scalars[1], &offsets[L], h_q, h_sf, &scalars[2], qws, nullptr,
+                                  0, stream)))
     return st;
   if (cap > 0) {
     // a7: L2 in slot order

@@ -4,12 +4,14 @@
 #include <stddef.h>
 #include <stdint.h>
 
-// Quantizer workspace: amax bits [B] then threshold tables [B][128][8] uint16.
-size_t nvfp4_quant_ws_layout(int64_t B, size_t* table_off);
+// Quantizer workspace: per-workgroup amax partials, uint32 [B][1024].
+size_t nvfp4_quant_ws_layout(int64_t B);
 // rows_dev (optional, device): the number of valid rows is min(M, rows_dev[0]).
+// clear (optional, device): n_clear <= 256 words zeroed before the quantize kernel
+// runs (by the amax pass, or by a fill when amax_in is given).
 int nvfp4_launch_quantize(const void* x_bf16, int64_t B, int64_t M, int64_t K, const float* amax_in,
                           const int32_t* rows_dev, uint8_t* q, uint8_t* sf, float* gs_out, void* ws,
-                          hipStream_t stream);
+                          uint32_t* clear, int n_clear, hipStream_t stream);
 
 // Route workspace: per-chunk counts and bases, int32 [nchunks][num_local] each.
 constexpr int kRouteChunk = 1024;

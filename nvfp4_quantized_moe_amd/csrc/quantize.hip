@@ -17,12 +17,14 @@
 // midpoint is exact in float64 (3 x 4 x 24 significant bits) and is turned
 // into a BF16 bit-pattern threshold U such that |x| passes it iff
 // bits(|x|) > U. One table of 7 thresholds per scale code (127 codes) is
-// built per tensor, so the per-element work is seven integer compares.
+// built in LDS by every workgroup, so the per-element work is seven integer
+// compares.
 //
-// Kernels: fill (clear amax), amax (wave reductions + one atomic max per
-// workgroup on the float bits, order-free), table (gs and thresholds per
-// tensor), quantize (16-element blocks, one block per thread, persistent
-// grid-stride over the tensor).
+// Kernels: amax (wave reductions, one partial maximum per workgroup on the
+// float bits, order-free) and quantize (each workgroup reduces the partials,
+// derives gs and builds the threshold table in LDS, then quantizes 16-element
+// blocks, one per thread, grid-stride over the tensor). With amax given (the
+// h path) only the quantize kernel runs.
 #include "common.h"
 #include "internal.h"
 
@@ -37,12 +39,18 @@ __global__ void fill_u32_kernel(uint32_t* p, int n, uint32_t v) {
   if (i < n) p[i] = v;
 }
 
-// amax_bits[b] = max over x[b] of |x| as float32 bits (|x| >= 0, so the
-// unsigned order of the bits is the order of the values).
+// Per-workgroup partial maxima: partial[b][blockIdx.x] = max |x| over the
+// workgroup's share of x[b], as float32 bits (|x| >= 0, so the unsigned order
+// of the bits is the order of the values). Every workgroup of the fixed grid
+// writes its slot, so nothing has to be cleared first. Workgroup (0, 0) also
+// zeroes clear[0..n_clear), which later kernels of the same stream use as
+// atomic-max targets.
 __global__ __launch_bounds__(256) void amax_kernel(const uint16_t* __restrict__ x, int64_t per_batch,
                                                    const int32_t* __restrict__ rows_dev, int64_t K,
-                                                   uint32_t* __restrict__ amax_bits) {
+                                                   uint32_t* __restrict__ partial, uint32_t* __restrict__ clear,
+                                                   int n_clear) {
   const int b = blockIdx.y;
+  if (blockIdx.x == 0 && b == 0 && (int)threadIdx.x < n_clear) clear[threadIdx.x] = 0u;
   int64_t n = per_batch;
   if (rows_dev) {
     int64_t r = rows_dev[0];
@@ -64,24 +72,30 @@ __global__ __launch_bounds__(256) void amax_kernel(const uint16_t* __restrict__ 
   __shared__ uint32_t red[4];
   if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
   __syncthreads();
-  if (threadIdx.x == 0) {
-    uint32_t r = max(max(red[0], red[1]), max(red[2], red[3]));
-    if (r) atomicMax(&amax_bits[b], r << 16);
-  }
+  if (threadIdx.x == 0) partial[(size_t)b * gridDim.x + blockIdx.x] = max(max(red[0], red[1]), max(red[2], red[3])) << 16;
 }
 
-// Per tensor b: gs = RN_f32(amax / 2688) and the threshold table
-// table[b][code][j] (uint16, 8 per code, entry 7 unused).
-__global__ __launch_bounds__(256) void table_kernel(const float* __restrict__ amax_in,
-                                                    const uint32_t* __restrict__ amax_bits,
-                                                    uint16_t* __restrict__ table, float* __restrict__ gs_out) {
-  const int b = blockIdx.x;
-  float amax = amax_in ? amax_in[b] : __uint_as_float(amax_bits[b]);
+// amax of tensor b, gs = RN_f32(amax / 2688), and the threshold table of
+// every scale code into LDS: lut[code] holds the BF16 bit patterns U_j such
+// that |x| passes E2M1 midpoint j of that code iff bits(|x|) > U_j.
+__device__ __forceinline__ float block_gs_and_lut(const float* __restrict__ amax_in,
+                                                  const uint32_t* __restrict__ partial, int n_partial, int b,
+                                                  uint16_t* lut /* [128][8] in LDS */) {
+  __shared__ uint32_t red[4];
+  uint32_t m = 0;
+  if (amax_in) {
+    m = __float_as_uint(amax_in[b]);
+  } else {
+    for (int i = threadIdx.x; i < n_partial; i += blockDim.x) m = max(m, partial[(size_t)b * n_partial + i]);
+    m = wave_max_u32(m);
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
+    __syncthreads();
+    m = max(max(red[0], red[1]), max(red[2], red[3]));
+  }
+  const float amax = __uint_as_float(m);
   // float64 quotient rounded to float32: 53 >= 2*24 + 2, so this equals one
   // correctly rounded float32 division
-  float gs = (float)((double)amax / 2688.0);
-  if (threadIdx.x == 0) gs_out[b] = gs;
-  uint16_t* t = table + (size_t)b * 128 * 8;
+  const float gs = (float)((double)amax / 2688.0);
   for (int i = threadIdx.x; i < 128 * 8; i += blockDim.x) {
     int code = i >> 3, j = i & 7;
     uint32_t u = 0xFFFFu;
@@ -94,22 +108,23 @@ __global__ __launch_bounds__(256) void table_kernel(const float* __restrict__ am
       // tie-up midpoint: |x| >= thr <=>  bits > bits(RU(thr)) - 1
       u = (kTieUp[j] && exact) ? rd - 1u : rd;
     }
-    t[i] = (uint16_t)u;
+    lut[i] = (uint16_t)u;
   }
+  __syncthreads();
+  return gs;
 }
 
 template <bool kRowsDev>
 __global__ __launch_bounds__(256) void quantize_kernel(const uint16_t* __restrict__ x, int64_t M, int64_t K,
                                                        const int32_t* __restrict__ rows_dev,
-                                                       const uint16_t* __restrict__ table,
-                                                       const float* __restrict__ gs_arr,
-                                                       uint8_t* __restrict__ q, uint8_t* __restrict__ sf) {
+                                                       const float* __restrict__ amax_in,
+                                                       const uint32_t* __restrict__ partial, int n_partial,
+                                                       float* __restrict__ gs_out, uint8_t* __restrict__ q,
+                                                       uint8_t* __restrict__ sf) {
   const int b = blockIdx.y;
   __shared__ uint4 lut[128];
-  const uint4* tb = reinterpret_cast<const uint4*>(table + (size_t)b * 128 * 8);
-  if (threadIdx.x < 128) lut[threadIdx.x] = tb[threadIdx.x];
-  __syncthreads();
-  const float gs = gs_arr[b];
+  const float gs = block_gs_and_lut(amax_in, partial, n_partial, b, reinterpret_cast<uint16_t*>(lut));
+  if (blockIdx.x == 0 && threadIdx.x == 0) gs_out[b] = gs;
   const double six_gs = 6.0 * (double)gs;  // exact
   int64_t rows = M;
   if (kRowsDev) rows = min(rows, (int64_t)rows_dev[0]);
@@ -157,47 +172,48 @@ static int quant_grid(int64_t nblk) {
   return (int)g;
 }
 
+// workgroups of the amax pass per tensor (fixed by the tensor size, at most kAmaxGrid)
+constexpr int kAmaxGrid = 1024;
+static int amax_grid(int64_t per_batch) {
+  int64_t gx = (per_batch / 8 + 255) / 256;
+  if (gx > kAmaxGrid) gx = kAmaxGrid;
+  if (gx < 1) gx = 1;
+  return (int)gx;
+}
+
 int nvfp4_launch_fill_u32(uint32_t* p, int n, uint32_t v, hipStream_t stream) {
   hipLaunchKernelGGL(fill_u32_kernel, dim3((n + 255) / 256), dim3(256), 0, stream, p, n, v);
   NVFP4_CHECK_LAUNCH();
   return NVFP4_OK;
 }
 
-size_t nvfp4_quant_ws_layout(int64_t B, size_t* table_off) {
-  size_t amax_bytes = nvfp4_align256((size_t)B * 4);
-  if (table_off) *table_off = amax_bytes;
-  return amax_bytes + nvfp4_align256((size_t)B * 128 * 8 * 2);
-}
+size_t nvfp4_quant_ws_layout(int64_t B) { return nvfp4_align256((size_t)B * kAmaxGrid * 4); }
 
-// Internal launcher shared by nvfp4_quantize and the layer.
+// Internal launcher shared by nvfp4_quantize and the layer: two launches
+// (amax partials, quantize) or one when amax_in is given.
 int nvfp4_launch_quantize(const void* x_bf16, int64_t B, int64_t M, int64_t K, const float* amax_in,
                           const int32_t* rows_dev, uint8_t* q, uint8_t* sf, float* gs_out, void* ws,
-                          hipStream_t stream) {
-  size_t table_off;
-  nvfp4_quant_ws_layout(B, &table_off);
-  uint32_t* amax_bits = reinterpret_cast<uint32_t*>(ws);
-  uint16_t* table = reinterpret_cast<uint16_t*>(reinterpret_cast<char*>(ws) + table_off);
+                          uint32_t* clear, int n_clear, hipStream_t stream) {
+  uint32_t* partial = reinterpret_cast<uint32_t*>(ws);
   const uint16_t* x = reinterpret_cast<const uint16_t*>(x_bf16);
+  const int64_t per = M * K;
+  const int gx = amax_grid(per);
   if (!amax_in) {
-    hipLaunchKernelGGL(fill_u32_kernel, dim3((unsigned)((B + 255) / 256)), dim3(256), 0, stream, amax_bits,
-                       (int)B, 0u);
-    NVFP4_CHECK_LAUNCH();
-    int64_t per = M * K;
-    int64_t gx = (per / 8 + 255) / 256;
-    if (gx > 1024) gx = 1024;
-    if (gx < 1) gx = 1;
     hipLaunchKernelGGL(amax_kernel, dim3((unsigned)gx, (unsigned)B), dim3(256), 0, stream, x, per, rows_dev, K,
-                       amax_bits);
+                       partial, clear, clear ? n_clear : 0);
+    NVFP4_CHECK_LAUNCH();
+  } else if (clear && n_clear > 0) {
+    hipLaunchKernelGGL(fill_u32_kernel, dim3(1), dim3(256), 0, stream, clear, n_clear, 0u);
     NVFP4_CHECK_LAUNCH();
   }
-  hipLaunchKernelGGL(table_kernel, dim3((unsigned)B), dim3(256), 0, stream, amax_in, amax_bits, table, gs_out);
-  NVFP4_CHECK_LAUNCH();
-  if (M == 0) return NVFP4_OK;
+  // M == 0 still launches one workgroup per tensor: it writes gs
   dim3 grid((unsigned)quant_grid(M * (K / 16)), (unsigned)B);
   if (rows_dev)
-    hipLaunchKernelGGL(quantize_kernel<true>, grid, dim3(256), 0, stream, x, M, K, rows_dev, table, gs_out, q, sf);
+    hipLaunchKernelGGL(quantize_kernel<true>, grid, dim3(256), 0, stream, x, M, K, rows_dev, amax_in, partial, gx,
+                       gs_out, q, sf);
   else
-    hipLaunchKernelGGL(quantize_kernel<false>, grid, dim3(256), 0, stream, x, M, K, rows_dev, table, gs_out, q, sf);
+    hipLaunchKernelGGL(quantize_kernel<false>, grid, dim3(256), 0, stream, x, M, K, rows_dev, amax_in, partial, gx,
+                       gs_out, q, sf);
   NVFP4_CHECK_LAUNCH();
   return NVFP4_OK;
 }
@@ -206,7 +222,7 @@ extern "C" size_t nvfp4_quantize_ws_bytes(int64_t B, int64_t M, int64_t K) {
   (void)M;
   (void)K;
   if (B < 1) return 0;
-  return nvfp4_quant_ws_layout(B, nullptr);
+  return nvfp4_quant_ws_layout(B);
 }
 
 extern "C" int nvfp4_quantize(const void* x_bf16, int64_t B, int64_t M, int64_t K, const float* amax_in,
@@ -218,5 +234,6 @@ extern "C" int nvfp4_quantize(const void* x_bf16, int64_t B, int64_t M, int64_t 
       !nvfp4_aligned16(ws))
     return NVFP4_ERR_ALIGN;
   if (ws_bytes < nvfp4_quantize_ws_bytes(B, M, K)) return NVFP4_ERR_WORKSPACE;
-  return nvfp4_launch_quantize(x_bf16, B, M, K, amax_in, nullptr, q, sf, gs_out, ws, (hipStream_t)stream);
+  return nvfp4_launch_quantize(x_bf16, B, M, K, amax_in, nullptr, q, sf, gs_out, ws, nullptr, 0,
+                               (hipStream_t)stream);
 }

@@ -15,6 +15,8 @@
 //   scatter  per chunk, in flat order: rank among equal keys from ballots on
 //            the key bits, waves taking turns on an LDS running base per
 //            expert; also writes the -1 / 0 padding of slots >= S.
+// Batches of at most 1024 flat entries (decode) take all three steps in one
+// workgroup and one launch (route_small_kernel), with the same result.
 #include "common.h"
 #include "internal.h"
 
@@ -66,22 +68,12 @@ __device__ int block_exclusive_scan(int v, int* wsum, int* total) {
   return r;
 }
 
-// One workgroup. Experts are split into contiguous runs of `per` per thread.
-__global__ __launch_bounds__(kScanThreads) void route_scan_kernel(
-    const int32_t* __restrict__ chunk_counts, int nchunks, int L, int tile_m, int32_t* __restrict__ counts,
-    int32_t* __restrict__ offsets, int32_t* __restrict__ bases, int32_t* __restrict__ tile_table) {
-  extern __shared__ int32_t sm[];
-  int32_t* s_cnt = sm;            // [L]
-  int32_t* s_off = sm + L;        // [L]
-  int32_t* s_toff = sm + 2 * L;   // [L]
-  __shared__ int wsum[kScanThreads / 64 + 1];
-  for (int e = threadIdx.x; e < L; e += blockDim.x) {
-    int c = 0;
-    for (int ch = 0; ch < nchunks; ++ch) c += chunk_counts[(size_t)ch * L + e];
-    s_cnt[e] = c;
-    counts[e] = c;
-  }
-  __syncthreads();
+// Offsets and tile bases of every expert from s_cnt (one workgroup of
+// kScanThreads; experts in contiguous runs of `per` per thread): writes
+// s_off, s_toff, counts, offsets, tile_table; returns S.
+__device__ int scan_experts(const int32_t* s_cnt, int L, int tile_m, int32_t* s_off, int32_t* s_toff, int* wsum,
+                            int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
+                            int32_t* __restrict__ tile_table) {
   const int per = (L + kScanThreads - 1) / kScanThreads;
   const int e0 = threadIdx.x * per;
   int rows = 0, tiles = 0;
@@ -100,12 +92,8 @@ __global__ __launch_bounds__(kScanThreads) void route_scan_kernel(
   }
   __syncthreads();
   for (int e = threadIdx.x; e < L; e += blockDim.x) {
+    counts[e] = s_cnt[e];
     offsets[e] = s_off[e];
-    int run = s_off[e];
-    for (int ch = 0; ch < nchunks; ++ch) {
-      bases[(size_t)ch * L + e] = run;
-      run += chunk_counts[(size_t)ch * L + e];
-    }
     int nt = (s_cnt[e] + tile_m - 1) / tile_m;
     for (int mt = 0; mt < nt; ++mt) {
       int t = s_toff[e] + mt;
@@ -116,6 +104,102 @@ __global__ __launch_bounds__(kScanThreads) void route_scan_kernel(
   if (threadIdx.x == 0) {
     offsets[L] = total_rows;
     tile_table[0] = total_tiles;
+  }
+  return total_rows;
+}
+
+// Rank of this lane's key among the lanes of its wave with the same key
+// (lower lanes first), the number of such lanes, and whether this lane is
+// the highest of them. Keys are compared on their nbits low bits.
+__device__ __forceinline__ void wave_key_rank(int key, int nbits, int* rank, int* cnt, bool* last) {
+  const int lane = threadIdx.x & 63;
+  const unsigned long long below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  unsigned long long match = ~0ull;
+  for (int b = 0; b < nbits; ++b) {
+    int bit = (key >> b) & 1;
+    unsigned long long m = __ballot(bit);
+    match &= bit ? m : ~m;
+  }
+  *rank = __popcll(match & below);
+  *cnt = __popcll(match);
+  *last = (match >> lane) == 1ull;
+}
+
+// One workgroup. Per-expert totals from the per-chunk histograms, then the
+// offsets, the tile table and every chunk's first slot per expert.
+__global__ __launch_bounds__(kScanThreads) void route_scan_kernel(
+    const int32_t* __restrict__ chunk_counts, int nchunks, int L, int tile_m, int32_t* __restrict__ counts,
+    int32_t* __restrict__ offsets, int32_t* __restrict__ bases, int32_t* __restrict__ tile_table) {
+  extern __shared__ int32_t sm[];
+  int32_t* s_cnt = sm;            // [L]
+  int32_t* s_off = sm + L;        // [L]
+  int32_t* s_toff = sm + 2 * L;   // [L]
+  __shared__ int wsum[kScanThreads / 64 + 1];
+  for (int e = threadIdx.x; e < L; e += blockDim.x) {
+    int c = 0;
+    for (int ch = 0; ch < nchunks; ++ch) c += chunk_counts[(size_t)ch * L + e];
+    s_cnt[e] = c;
+  }
+  __syncthreads();
+  scan_experts(s_cnt, L, tile_m, s_off, s_toff, wsum, counts, offsets, tile_table);
+  for (int e = threadIdx.x; e < L; e += blockDim.x) {
+    int run = s_off[e];
+    for (int ch = 0; ch < nchunks; ++ch) {
+      bases[(size_t)ch * L + e] = run;
+      run += chunk_counts[(size_t)ch * L + e];
+    }
+  }
+}
+
+// The whole route in one workgroup when T*k <= kScanThreads (decode-sized
+// batches): histogram, scan and stable scatter, one flat entry per thread,
+// the waves taking turns in flat order on the running slot of each expert.
+__global__ __launch_bounds__(kScanThreads) void route_small_kernel(
+    const int32_t* __restrict__ ids, const float* __restrict__ w, int32_t n, int32_t k, int32_t start, int32_t L,
+    int tile_m, int nbits, int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
+    int32_t* __restrict__ slot_token, int32_t* __restrict__ slot_expert, float* __restrict__ slot_weight,
+    int32_t* __restrict__ token_slot, int32_t* __restrict__ tile_table) {
+  extern __shared__ int32_t sm[];
+  int32_t* s_cnt = sm;            // [L]
+  int32_t* s_off = sm + L;        // [L], then the running slot of each expert
+  int32_t* s_toff = sm + 2 * L;   // [L]
+  __shared__ int wsum[kScanThreads / 64 + 1];
+  for (int e = threadIdx.x; e < L; e += blockDim.x) s_cnt[e] = 0;
+  __syncthreads();
+  const int f = threadIdx.x;
+  int key = L;  // L marks a dropped or absent entry
+  if (f < n) {
+    int64_t l = (int64_t)ids[f] - start;
+    if (l >= 0 && l < L) key = (int)l;
+  }
+  if (key < L) atomicAdd(&s_cnt[key], 1);
+  __syncthreads();
+  const int S = scan_experts(s_cnt, L, tile_m, s_off, s_toff, wsum, counts, offsets, tile_table);
+  if (f < n && f >= S) {
+    slot_token[f] = -1;
+    slot_expert[f] = -1;
+    slot_weight[f] = 0.0f;
+  }
+  __syncthreads();  // every slot_* padding store precedes the scattered stores below
+  int rank, cnt;
+  bool last;
+  wave_key_rank(key, nbits, &rank, &cnt, &last);
+  const int wave = threadIdx.x >> 6;
+  int slot = -1;
+  for (int wv = 0; wv < kScanThreads / 64; ++wv) {
+    if (wave == wv && key < L) {
+      slot = s_off[key] + rank;
+      if (last) s_off[key] += cnt;
+    }
+    __syncthreads();
+  }
+  if (f < n) {
+    token_slot[f] = slot;
+    if (slot >= 0) {
+      slot_token[slot] = f / k;
+      slot_expert[slot] = key;
+      slot_weight[slot] = w[f];
+    }
   }
 }
 
@@ -137,8 +221,7 @@ __global__ __launch_bounds__(256) void route_scatter_kernel(
     }
   }
   __syncthreads();
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const unsigned long long below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  const int wave = threadIdx.x >> 6;
   for (int round = 0; round < kRouteChunk / 256; ++round) {
     const int f = chunk * kRouteChunk + round * 256 + threadIdx.x;
     int key = L;  // L marks a dropped or absent entry
@@ -146,15 +229,9 @@ __global__ __launch_bounds__(256) void route_scatter_kernel(
       int64_t l = (int64_t)ids[f] - start;
       if (l >= 0 && l < L) key = (int)l;
     }
-    unsigned long long match = ~0ull;
-    for (int b = 0; b < nbits; ++b) {
-      int bit = (key >> b) & 1;
-      unsigned long long m = __ballot(bit);
-      match &= bit ? m : ~m;
-    }
-    const int rank = __popcll(match & below);
-    const int cnt = __popcll(match);
-    const bool last = (match >> lane) == 1ull;
+    int rank, cnt;
+    bool last;
+    wave_key_rank(key, nbits, &rank, &cnt, &last);
     int slot = -1;
     for (int wv = 0; wv < 4; ++wv) {
       if (wave == wv && key < L) {
@@ -197,6 +274,13 @@ int nvfp4_launch_route(const int32_t* topk_ids, const float* topk_w, int32_t T, 
   int32_t* bases = reinterpret_cast<int32_t*>(reinterpret_cast<char*>(ws) + per);
   int nbits = 1;
   while ((1 << nbits) <= L) ++nbits;  // keys 0..L must be distinct
+  if (n <= kScanThreads) {
+    hipLaunchKernelGGL(route_small_kernel, dim3(1), dim3(kScanThreads), 3 * L * 4, stream, topk_ids, topk_w, n, k,
+                       expert_start, L, tile_m, nbits, counts, offsets, slot_token, slot_expert, slot_weight,
+                       token_slot, tile_table);
+    NVFP4_CHECK_LAUNCH();
+    return NVFP4_OK;
+  }
   if (nchunks > 0) {
     hipLaunchKernelGGL(route_count_kernel, dim3(nchunks), dim3(256), L * 4, stream, topk_ids, n, expert_start, L,
                        chunk_counts);
@@ -223,7 +307,7 @@ extern "C" int64_t nvfp4_tile_table_len(int64_t slot_capacity, int32_t num_local
   return 1 + 2 * (slot_capacity / tile_m + num_local);
 }
 
-static bool valid_tile_m(int32_t t) { return t == 16 || t == 32 || t == 64 || t == 128 || t == 256; }
+static bool valid_tile_m(int32_t t) { return t >= 16 && t <= 256 && t % 16 == 0; }
 
 extern "C" int moe_route_slots(const int32_t* topk_ids, const float* topk_w, int32_t T, int32_t k,
                                int32_t expert_start, int32_t num_local, int32_t tile_m, int32_t* counts,

@@ -99,6 +99,11 @@ def _router_case(name):
     if name == "none_local":
         ids = rng.integers(0, 96, (50, 8)).astype(np.int32)
         return ids, rng.random((50, 8)).astype(np.float32), 96, 48
+    if name in ("edge_1024", "edge_1025"):
+        # flat sizes on both sides of the single-workgroup route path
+        T, k = (128, 8) if name == "edge_1024" else (205, 5)
+        ids = rng.integers(0, 64, (T, k)).astype(np.int32)
+        return ids, rng.random((T, k)).astype(np.float32), 16, 32
     if name == "big_L":
         ids = rng.integers(0, 3000, (600, 6)).astype(np.int32)
         return ids, rng.random((600, 6)).astype(np.float32), 500, 2100
@@ -106,8 +111,9 @@ def _router_case(name):
 
 
 @pytest.mark.parametrize("case", ["tiny", "mid", "mid_k1", "mid_skew", "decode", "prefill", "skewed",
-                                  "random_out_of_range", "empty", "none_local", "big_L"])
-@pytest.mark.parametrize("tile_m", [32, 128])
+                                  "random_out_of_range", "empty", "none_local", "big_L", "edge_1024",
+                                  "edge_1025"])
+@pytest.mark.parametrize("tile_m", [32, 96, 128])
 def test_route_bit_exact(nv, case, tile_m):
     ids, w, start, L = _router_case(case)
     log(f"route {case} T={ids.shape[0]} k={ids.shape[1]} L={L} tile_m={tile_m}")

@@ -68,7 +68,8 @@ def test_invalid_arguments_are_rejected_before_launch():
     # route: k out of range, tile_m unsupported, NULL outputs
     args = [buf] * 7
     assert nv._route(buf, buf, 4, 0, 0, 8, 32, *args, buf, 1 << 20, s) == 2
-    assert nv._route(buf, buf, 4, 2, 0, 8, 48, *args, buf, 1 << 20, s) == 2
+    assert nv._route(buf, buf, 4, 2, 0, 8, 40, *args, buf, 1 << 20, s) == 2
+    assert nv._route(buf, buf, 4, 2, 0, 8, 272, *args, buf, 1 << 20, s) == 2
     assert nv._route(buf, buf, 4, 2, 0, 8, 32, null, *args[1:], buf, 1 << 20, s) == 1
     # grouped GEMM: K not a multiple of 128, unknown epilogue, odd tile height
     g = [buf] * 8
