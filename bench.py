@@ -77,9 +77,21 @@ def main():
     ap.add_argument("--summarize-traffic", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="write the per-launch HBM traffic of the L1 GEMM from two rocprofv3 --pmc "
                          "csv runs (FETCH_SIZE, WRITE_SIZE) to profiles/ and exit")
+    ap.add_argument("--summarize-trace", metavar="TRACE_DIR",
+                    help="write the per-kernel table of a rocprofv3 --kernel-trace --stats csv run to "
+                         "profiles/ and exit")
+    ap.add_argument("--summarize-mfma", metavar="PMC_DIR",
+                    help="write the MFMA counters of the L1 GEMM from a rocprofv3 --pmc csv run to "
+                         "profiles/ and exit")
     args = ap.parse_args()
     if args.summarize_traffic:
         summarize_traffic(args.config, *args.summarize_traffic)
+        return
+    if args.summarize_trace:
+        summarize_trace(args.config, args.summarize_trace)
+        return
+    if args.summarize_mfma:
+        summarize_mfma(args.config, args.summarize_mfma)
         return
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU; --gpus {args.gpus} is not supported "
@@ -379,8 +391,9 @@ def summarize_traffic(workload, fetch_dir, write_dir):
         f.write(f"# HBM traffic of the L1 grouped GEMM (gate+up, SiLU*up epilogue), {workload} shard\n")
         f.write("# counters from two rocprofv3 runs on the MI355X box, from the repository root:\n")
         for c, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
-            f.write(f"#   timeout -s KILL 120 rocprofv3 --pmc {c} -f csv -d {d} -o run -- python -u bench.py "
-                    f"--config {workload} --steps 2 --warmup 1 --no-decode --no-cpu-baseline --copy-calibration\n")
+            f.write(f"#   timeout -s KILL 180 rocprofv3 --pmc {c} -f csv -d {d} -o run -- python -u bench.py "
+                    f"--config {workload} --steps 2 --warmup 1 --no-decode --no-cpu-baseline --settle-ms 0 "
+                    f"--copy-calibration\n")
         f.write(f"# summarized with: python bench.py --config {workload} --summarize-traffic {fetch_dir} {write_dir}\n")
         f.write("# each counter (KiB per dispatch) is scaled by bytes / counter of a plain 1 GiB copy\n")
         f.write(f"kernel_source_sha = {kernel_source_sha()}\n")
@@ -389,6 +402,67 @@ def summarize_traffic(workload, fetch_dir, write_dir):
             f.write(f"{tag}_kib_per_launch = {o['kib']:.1f}\n{tag}_copy_factor = {o['factor']:.4f}\n"
                     f"{tag}_dispatches = {o['n']}\n{tag}_bytes_per_launch = {o['bytes']:.0f}\n")
         f.write(f"hbm_bytes_per_launch = {out['fetch']['bytes'] + out['write']['bytes']:.0f}\n")
+    print(open(path).read())
+
+
+def _short_kernel_name(n):
+    n = n.split("(")[0].replace("void ", "").replace("nvfp4::", "")
+    return n if len(n) < 90 else n[:87] + "..."
+
+
+def summarize_trace(workload, d):
+    """Per-kernel table (calls, total, average, min, max) of a rocprofv3
+    --kernel-trace --stats csv run."""
+    import csv
+    import glob
+    f = glob.glob(os.path.join(d, "**", "*kernel_stats.csv"), recursive=True)
+    if not f:
+        raise SystemExit(f"no kernel_stats.csv under {d}")
+    rows = list(csv.DictReader(open(f[0])))
+    path = os.path.join(PROFILE_DIR, f"layer_{workload}_kernel_trace.md")
+    with open(path, "w") as o:
+        o.write(f"# Kernel trace of the benchmark ({workload} shard headline, decode shard beside it)\n\n")
+        o.write("Command, from the repository root on the MI355X box:\n\n```\n")
+        o.write(f"rocprofv3 --kernel-trace --stats -f csv -d {d} -o run -- python -u bench.py --config {workload} "
+                f"--steps 5 --warmup 1 --no-cpu-baseline --settle-ms 100\n")
+        o.write(f"python bench.py --config {workload} --summarize-trace {d}\n```\n\n")
+        o.write("Grouped GEMM template arguments: <SUB_M, SUB_N, WAVES, stages in flight, epilogue> "
+                "(epilogue 1 = L1 with SiLU*up, 0 = L2). The settle period, the warmup and the timed "
+                "steps are all in the trace.\n\n")
+        o.write("| kernel | calls | total ms | avg us | min us | max us | share |\n|---|---|---|---|---|---|---|\n")
+        for r in rows:
+            o.write(f"| `{_short_kernel_name(r['Name'])}` | {r['Calls']} | {float(r['TotalDurationNs']) / 1e6:.3f} | "
+                    f"{float(r['AverageNs']) / 1e3:.1f} | {float(r['MinNs']) / 1e3:.1f} | "
+                    f"{float(r['MaxNs']) / 1e3:.1f} | {float(r['Percentage']):.1f}% |\n")
+    print(open(path).read())
+
+
+def summarize_mfma(workload, d):
+    """MFMA work of the L1 GEMM from one rocprofv3 --pmc run: executed MFMA
+    instructions (32x32x16 fp16: 32768 FLOP each) against the algorithmic
+    FLOP, and the MFMA-busy share of the SIMD cycles."""
+    ins = _counter_rows(d, "SQ_INSTS_MFMA")
+    busy = _counter_rows(d, "SQ_VALU_MFMA_BUSY_CYCLES")
+    gui = _counter_rows(d, "GRBM_GUI_ACTIVE")
+    sqb = _counter_rows(d, "SQ_BUSY_CYCLES")
+    sel = lambda rows: [v for n, v in rows if "grouped_gemm_kernel" in n and
+                        n.replace(" ", "").split(">")[0].endswith(",1")]
+    i, b, g, q = (float(np.mean(sel(r))) for r in (ins, busy, gui, sqb))
+    path = os.path.join(PROFILE_DIR, f"l1_gemm_{workload}_mfma.txt")
+    with open(path, "w") as o:
+        o.write(f"# MFMA counters of the L1 grouped GEMM (gate+up, SiLU*up epilogue), {workload} shard\n")
+        o.write("# command, from the repository root on the MI355X box:\n")
+        o.write(f"#   timeout -s KILL 180 rocprofv3 --pmc SQ_INSTS_MFMA SQ_VALU_MFMA_BUSY_CYCLES SQ_BUSY_CYCLES "
+                f"SQ_WAVES GRBM_GUI_ACTIVE -f csv -d {d} -o run -- python -u bench.py --config {workload} "
+                f"--steps 2 --warmup 1 --no-decode --no-cpu-baseline --settle-ms 0\n")
+        o.write(f"# summarized with: python bench.py --config {workload} --summarize-mfma {d}\n")
+        o.write(f"kernel_source_sha = {kernel_source_sha()}\n")
+        o.write(f"dispatches = {len(sel(ins))}\n")
+        o.write(f"mfma_instructions_per_launch = {i:.0f}\n")
+        o.write(f"executed_mfma_flop_per_launch = {i * 32768:.0f}\n")
+        o.write(f"mfma_busy_cycles_per_launch = {b:.0f}   # summed over SIMDs; 32 per 32x32x16 fp16 MFMA\n")
+        o.write(f"grbm_gui_active_per_launch = {g:.0f}\n")
+        o.write(f"sq_busy_cycles_per_launch = {q:.0f}\n")
     print(open(path).read())
 
 
