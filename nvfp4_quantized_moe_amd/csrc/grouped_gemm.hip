@@ -63,33 +63,41 @@ constexpr uint32_t kOutOfRange = 0x80000000u;  // offset that is never in range
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t num_records) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)num_records, (int)kRsrcWord3);
 }
-__device__ __forceinline__ uint4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
-  return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0));
+// Address = per-lane voffset + wave-uniform soffset (an SGPR: per-stage and
+// per-subtile offsets cost no vector instructions). An out-of-range voffset
+// or soffset is >= 2^31, and the other term is below 2^31 whenever it is in
+// range, so their 32-bit sum stays out of range (or, when both are out of
+// range, wraps to a small in-range offset of a lane whose result is discarded).
+__device__ __forceinline__ uint4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+  return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, (int)soff, 0));
 }
-__device__ __forceinline__ uint32_t buf_load4(__amdgpu_buffer_rsrc_t r, uint32_t off) {
-  return __builtin_amdgcn_raw_buffer_load_b32(r, (int)off, 0, 0);
+__device__ __forceinline__ uint32_t buf_load4(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+  return __builtin_amdgcn_raw_buffer_load_b32(r, (int)voff, (int)soff, 0);
 }
-__device__ __forceinline__ uint32_t buf_load2(__amdgpu_buffer_rsrc_t r, uint32_t off) {
-  return __builtin_amdgcn_raw_buffer_load_b16(r, (int)off, 0, 0);
+__device__ __forceinline__ uint32_t buf_load2(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+  return __builtin_amdgcn_raw_buffer_load_b16(r, (int)voff, (int)soff, 0);
 }
 
 __device__ __forceinline__ uint32_t pick_u32(const uint4& v, int i) {
   return i == 0 ? v.x : i == 1 ? v.y : i == 2 ? v.z : v.w;
 }
 
-// E4M3 scale byte SEL of a word -> (s, s) in fp16 (both conversions exact)
-template <int SEL>
-__device__ __forceinline__ half2_t scale_pair(uint32_t sw) {
-  _Float16 s = (_Float16)__builtin_amdgcn_cvt_f32_fp8(sw, SEL);
-  half2_t r;
-  r[0] = s;
-  r[1] = s;
-  return r;
+// Four E4M3 scale bytes of a word -> four fp16 values, two per instruction
+// (v_cvt_scalef32_pk_f16_fp8 with scale 1: exact for every E4M3 value).
+struct Scales4 {
+  half2_t lo, hi;  // (s0, s1), (s2, s3)
+};
+__device__ __forceinline__ Scales4 scales4(uint32_t sw) {
+  return {__builtin_amdgcn_cvt_scalef32_pk_f16_fp8(sw, 1.0f, false),
+          __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(sw, 1.0f, true)};
 }
-
-__device__ __forceinline__ half2_t scale_pair_dyn(uint32_t sw, int sel) {
-  return sel == 0 ? scale_pair<0>(sw) : sel == 1 ? scale_pair<1>(sw) : sel == 2 ? scale_pair<2>(sw)
-                                                                                  : scale_pair<3>(sw);
+// scale i of the four, in both halves of a pair (the multiply broadcasts it)
+__device__ __forceinline__ half2_t scale_pair(const Scales4& s, int i) {
+  const _Float16 v = i == 0 ? s.lo[0] : i == 1 ? s.lo[1] : i == 2 ? s.hi[0] : s.hi[1];
+  half2_t r;
+  r[0] = v;
+  r[1] = v;
+  return r;
 }
 
 // 8 E2M1 values (one dword, element 8d..8d+7 in nibble order) times a scale pair
@@ -198,10 +206,11 @@ __global__ __launch_bounds__(64 * WAVES) void grouped_gemm_kernel(
     // needs no branches around its loads
     auto load_a = [&](int s, int slot_) {
       const bool in = s < nstages;
+      const uint32_t so = in ? (uint32_t)(s * 64) : kOutOfRange, sso = in ? (uint32_t)(s * 8) : kOutOfRange;
 #pragma unroll
       for (int i = 0; i < C::A_PER_T; ++i) {
-        ra[slot_][i] = buf_load16(ra_q, in ? a_off[i] + (uint32_t)(s * 64) : kOutOfRange);
-        rsa[slot_][i] = buf_load2(ra_s, in ? as_off[i] + (uint32_t)(s * 8) : kOutOfRange);
+        ra[slot_][i] = buf_load16(ra_q, a_off[i], so);
+        rsa[slot_][i] = buf_load2(ra_s, as_off[i], sso);
       }
     };
     auto store_a = [&](int buf, int slot_) {
@@ -211,9 +220,10 @@ __global__ __launch_bounds__(64 * WAVES) void grouped_gemm_kernel(
         const int task = tid + i * C::THREADS;
         if (task < C::A_TASKS) {
           uint8_t* dst = base + (task >> 2) * kAPitch + (task & 3) * 64;
+          const Scales4 sa = scales4(rsa[slot_][i]);
 #pragma unroll
           for (int q = 0; q < 4; ++q) {
-            half8_t v = decode8(pick_u32(ra[slot_][i], q), scale_pair_dyn(rsa[slot_][i], q >> 1));
+            half8_t v = decode8(pick_u32(ra[slot_][i], q), scale_pair(sa, q >> 1));
             *reinterpret_cast<half8_t*>(dst + 16 * q) = v;
           }
         }
@@ -224,12 +234,11 @@ __global__ __launch_bounds__(64 * WAVES) void grouped_gemm_kernel(
 #pragma unroll
       for (int j = 0; j < SUB_N; ++j) {
         const bool ok = in && row0[j] >= 0;
-        const uint32_t chunk = ((uint32_t)(row0[j] >> 5) * (uint32_t)nstages + (uint32_t)s) * kPackChunk;
-        const uint32_t o = ok ? chunk + b_lane : kOutOfRange;   // kOutOfRange + 1024 stays out of range
-        const uint32_t os = ok ? chunk + bs_lane : kOutOfRange;
-        rb[slot_][j][0] = buf_load16(rbw, o);
-        rb[slot_][j][1] = buf_load16(rbw, o + 1024);
-        rsb[slot_][j] = buf_load4(rbw, os);
+        const uint32_t chunk = ok ? ((uint32_t)(row0[j] >> 5) * (uint32_t)nstages + (uint32_t)s) * kPackChunk
+                                  : kOutOfRange;  // wave-uniform: a scalar offset
+        rb[slot_][j][0] = buf_load16(rbw, b_lane, chunk);
+        rb[slot_][j][1] = buf_load16(rbw, b_lane + 1024u, chunk);
+        rsb[slot_][j] = buf_load4(rbw, bs_lane, chunk);
       }
     };
 
@@ -261,10 +270,13 @@ __global__ __launch_bounds__(64 * WAVES) void grouped_gemm_kernel(
         // software pipeline over the 8 MFMA steps of the stage: the operands of
         // step t + 1 are read and decoded while the MFMAs of step t execute
         half8_t av[2][SUB_M], bv[2][SUB_N];
+        Scales4 sb[SUB_N];
+#pragma unroll
+        for (int j = 0; j < SUB_N; ++j) sb[j] = scales4(rsb[u][j]);
 #pragma unroll
         for (int i = 0; i < SUB_M; ++i) av[0][i] = *reinterpret_cast<const half8_t*>(abuf + 32 * i * kAPitch);
 #pragma unroll
-        for (int j = 0; j < SUB_N; ++j) bv[0][j] = decode8(rb[u][j][0].x, scale_pair<0>(rsb[u][j]));
+        for (int j = 0; j < SUB_N; ++j) bv[0][j] = decode8(rb[u][j][0].x, scale_pair(sb[j], 0));
 #pragma unroll
         for (int t = 0; t < 8; ++t) {
           const int cur = t & 1, nxt = cur ^ 1;
@@ -274,8 +286,7 @@ __global__ __launch_bounds__(64 * WAVES) void grouped_gemm_kernel(
               av[nxt][i] = *reinterpret_cast<const half8_t*>(abuf + 32 * i * kAPitch + 16 * (t + 1));
 #pragma unroll
             for (int j = 0; j < SUB_N; ++j)
-              bv[nxt][j] = decode8(pick_u32(rb[u][j][(t + 1) >> 2], (t + 1) & 3),
-                                   scale_pair_dyn(rsb[u][j], (t + 1) >> 1));
+              bv[nxt][j] = decode8(pick_u32(rb[u][j][(t + 1) >> 2], (t + 1) & 3), scale_pair(sb[j], (t + 1) >> 1));
           }
 #pragma unroll
           for (int i = 0; i < SUB_M; ++i)
@@ -345,8 +356,13 @@ static int launch_cfg(const uint8_t* a_q, const uint8_t* a_sf, const int32_t* a_
   const int max_tiles = rows_cap / C::BM + num_local;
   const int64_t max_items = (int64_t)max_tiles * n_ntiles;
   auto kern = grouped_gemm_kernel<SUB_M, SUB_N, WAVES, P, EPI>;
-  static int per_cu = 0;  // resident workgroups per CU (host query, once per instance)
+  // resident workgroups per CU and the CU count (host queries, once per instance)
+  static int per_cu = 0, n_cu = 0;
   if (per_cu == 0) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n_cu < 1)
+      return NVFP4_ERR_HIP;
     if (C::LDS > 64 * 1024 &&
         hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
                             C::LDS) != hipSuccess)
@@ -357,7 +373,7 @@ static int launch_cfg(const uint8_t* a_q, const uint8_t* a_sf, const int32_t* a_
       nb = 1;
     per_cu = nb;
   }
-  int64_t grid = 256LL * per_cu;
+  int64_t grid = (int64_t)n_cu * per_cu;
   if (grid > max_items) grid = max_items;
   if (grid >= kXcds) grid -= grid % kXcds;
   if (grid < 1) grid = 1;
@@ -375,7 +391,7 @@ using namespace nvfp4;
 // Row-tile heights with a kernel configuration (measured on MI355X over
 // decode- and prefill-shaped problems):
 //   32  decode-shaped batches: 2 waves, each 32 x 128, 3 stages in flight
-//   64  prefill-shaped: 4 waves, each 64 x 64, 4 stages in flight
+//   64  prefill-shaped: 8 waves, each 64 x 64, 4 stages in flight
 //   128 large groups: 4 waves, each 128 x 64, 3 stages in flight
 int nvfp4_launch_grouped_gemm(const uint8_t* a_q, const uint8_t* a_sf, const int32_t* a_row_index,
                               const float* a_gs, const uint8_t* b_packed, const float* b_gs,
@@ -389,7 +405,7 @@ int nvfp4_launch_grouped_gemm(const uint8_t* a_q, const uint8_t* a_sf, const int
                                         : launch_cfg<SM, SN, W, PF, NVFP4_EPI_BF16>(NVFP4_GEMM_ARGS)
   switch (tile_m) {
     case 32: NVFP4_GEMM_CFG(1, 4, 2, 3);
-    case 64: NVFP4_GEMM_CFG(2, 2, 4, 4);
+    case 64: NVFP4_GEMM_CFG(2, 2, 8, 4);
     case 128: NVFP4_GEMM_CFG(4, 2, 4, 3);
     default: return NVFP4_ERR_SHAPE;
   }
