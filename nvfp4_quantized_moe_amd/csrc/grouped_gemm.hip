@@ -390,7 +390,7 @@ using namespace nvfp4;
 
 // Row-tile heights with a kernel configuration (measured on MI355X over
 // decode- and prefill-shaped problems):
-//   32  decode-shaped batches: 2 waves, each 32 x 128, 3 stages in flight
+//   32  decode-shaped batches: 4 waves, each 32 x 64, 3 stages in flight
 //   64  prefill-shaped: 8 waves, each 64 x 64, 4 stages in flight
 //   128 large groups: 4 waves, each 128 x 64, 3 stages in flight
 int nvfp4_launch_grouped_gemm(const uint8_t* a_q, const uint8_t* a_sf, const int32_t* a_row_index,
@@ -404,7 +404,7 @@ int nvfp4_launch_grouped_gemm(const uint8_t* a_q, const uint8_t* a_sf, const int
   return epilogue == NVFP4_EPI_SILU_MUL ? launch_cfg<SM, SN, W, PF, NVFP4_EPI_SILU_MUL>(NVFP4_GEMM_ARGS) \
                                         : launch_cfg<SM, SN, W, PF, NVFP4_EPI_BF16>(NVFP4_GEMM_ARGS)
   switch (tile_m) {
-    case 32: NVFP4_GEMM_CFG(1, 4, 2, 3);
+    case 32: NVFP4_GEMM_CFG(1, 2, 4, 3);
     case 64: NVFP4_GEMM_CFG(2, 2, 8, 4);
     case 128: NVFP4_GEMM_CFG(4, 2, 4, 3);
     default: return NVFP4_ERR_SHAPE;

@@ -126,18 +126,28 @@ __device__ __forceinline__ void wave_key_rank(int key, int nbits, int* rank, int
 }
 
 // One workgroup. Per-expert totals from the per-chunk histograms, then the
-// offsets, the tile table and every chunk's first slot per expert.
+// offsets, the tile table and every chunk's first slot per expert. When the
+// histograms fit in LDS (stage_cc), all threads first copy them there, so the
+// per-expert passes over the chunks read LDS instead of memory.
 __global__ __launch_bounds__(kScanThreads) void route_scan_kernel(
-    const int32_t* __restrict__ chunk_counts, int nchunks, int L, int tile_m, int32_t* __restrict__ counts,
-    int32_t* __restrict__ offsets, int32_t* __restrict__ bases, int32_t* __restrict__ tile_table) {
+    const int32_t* __restrict__ chunk_counts, int nchunks, int L, int tile_m, int stage_cc,
+    int32_t* __restrict__ counts, int32_t* __restrict__ offsets, int32_t* __restrict__ bases,
+    int32_t* __restrict__ tile_table) {
   extern __shared__ int32_t sm[];
   int32_t* s_cnt = sm;            // [L]
   int32_t* s_off = sm + L;        // [L]
   int32_t* s_toff = sm + 2 * L;   // [L]
+  int32_t* s_cc = sm + 3 * L;     // [nchunks][L] when stage_cc
   __shared__ int wsum[kScanThreads / 64 + 1];
+  const int32_t* cc = chunk_counts;
+  if (stage_cc) {
+    for (int i = threadIdx.x; i < nchunks * L; i += blockDim.x) s_cc[i] = chunk_counts[i];
+    __syncthreads();
+    cc = s_cc;
+  }
   for (int e = threadIdx.x; e < L; e += blockDim.x) {
     int c = 0;
-    for (int ch = 0; ch < nchunks; ++ch) c += chunk_counts[(size_t)ch * L + e];
+    for (int ch = 0; ch < nchunks; ++ch) c += cc[(size_t)ch * L + e];
     s_cnt[e] = c;
   }
   __syncthreads();
@@ -146,7 +156,7 @@ __global__ __launch_bounds__(kScanThreads) void route_scan_kernel(
     int run = s_off[e];
     for (int ch = 0; ch < nchunks; ++ch) {
       bases[(size_t)ch * L + e] = run;
-      run += chunk_counts[(size_t)ch * L + e];
+      run += cc[(size_t)ch * L + e];
     }
   }
 }
@@ -286,8 +296,11 @@ int nvfp4_launch_route(const int32_t* topk_ids, const float* topk_w, int32_t T, 
                        chunk_counts);
     NVFP4_CHECK_LAUNCH();
   }
-  hipLaunchKernelGGL(route_scan_kernel, dim3(1), dim3(kScanThreads), 3 * L * 4, stream, chunk_counts, nchunks, L,
-                     tile_m, counts, offsets, bases, tile_table);
+  // stage the per-chunk histograms in LDS when everything fits in 64 KB
+  const int stage_cc = ((int64_t)nchunks * L + 3 * L) * 4 <= 64 * 1024 ? 1 : 0;
+  const size_t lds = (size_t)(3 * L + (stage_cc ? nchunks * L : 0)) * 4;
+  hipLaunchKernelGGL(route_scan_kernel, dim3(1), dim3(kScanThreads), lds, stream, chunk_counts, nchunks, L, tile_m,
+                     stage_cc, counts, offsets, bases, tile_table);
   NVFP4_CHECK_LAUNCH();
   if (nchunks > 0) {
     hipLaunchKernelGGL(route_scatter_kernel, dim3(nchunks), dim3(256), L * 4, stream, topk_ids, topk_w, n, k,
