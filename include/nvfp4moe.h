@@ -153,13 +153,18 @@ int nvfp4_pack_weights(const uint8_t* q, const uint8_t* sf, int64_t B, int64_t N
  *   g = RN_bf16(G[s, n]), u = RN_bf16(G[s, I + n]), d[s, n] = RN_bf16(silu(g) * u)
  *   with silu(g) = g / (1 + exp(-g)) in float32; amax_out[0] is raised (atomic max)
  *   to max |d| over the rows written, so the caller sets it to 0 first.
+ * epilogue NVFP4_EPI_SILU_MUL_DUAL: as NVFP4_EPI_SILU_MUL for an L1 weight whose gate and
+ *   up halves keep their own global scales (no nvfp4_fold_scales): b_gs is float [L, 2]
+ *   = (gs_gate, gs_up) and the gate columns take alpha = RN_f32(a_gs[0] * b_gs[e][0]), the up
+ *   columns RN_f32(a_gs[0] * b_gs[e][1]) (the alpha commit's global-scale treatment applied to
+ *   each half, instead of the finalize_weights fold).
  * Activation row indices must satisfy (row + 1) * K/2 < 2^31, as must rows_cap * K/2
  * and N * K * 9/16 (32-bit buffer offsets).
  * Only rows of listed tiles are written. Requires K % 128 == 0, N % 64 == 0
  * (N % 128 == 0 for NVFP4_EPI_SILU_MUL), 1 <= L, tile_m 32 (decode-shaped
  * batches), 64 (prefill-shaped) or 128 (large groups).
  */
-enum { NVFP4_EPI_BF16 = 0, NVFP4_EPI_SILU_MUL = 1 };
+enum { NVFP4_EPI_BF16 = 0, NVFP4_EPI_SILU_MUL = 1, NVFP4_EPI_SILU_MUL_DUAL = 2 };
 int nvfp4_grouped_gemm(const uint8_t* a_q, const uint8_t* a_sf, const int32_t* a_row_index,
                        const float* a_gs, const uint8_t* b_packed, const float* b_gs,
                        const int32_t* offsets, const int32_t* tile_table, int32_t num_local,
@@ -196,7 +201,8 @@ int nvfp4_fold_scales(uint8_t* w1_sf, const float* gs_gate, const float* gs_up, 
  * Weights (host struct of device pointers), L = num_local, each packed by
  * nvfp4_pack_weights from its row-major NVFP4 form:
  *   w1: W1 [L, 2I, H] packed (B = L, N = 2I, K = H), w1_gs [L]
- *       gate rows [0,I), up rows [I,2I), gate/up scales folded to one gs (nvfp4_fold_scales)
+ *       gate rows [0,I), up rows [I,2I), gate/up scales folded to one gs (nvfp4_fold_scales);
+ *       or, with w1_dual_gs = 1, unfolded scales and w1_gs [L, 2] = (gs_gate, gs_up)
  *   w2: W2 [L, H, I] packed (B = L, N = H, K = I),   w2_gs [L]
  * x_bf16 [T, H]; topk_ids int32 [T, k] global ids; topk_w float [T, k];
  * out_bf16 [T, H] (tokens with no local expert get zeros).
@@ -210,6 +216,7 @@ typedef struct {
   const float* w1_gs;
   const uint8_t* w2;
   const float* w2_gs;
+  int32_t w1_dual_gs;  /* 0: w1_gs [L] (folded); 1: w1_gs [L, 2] (gate, up) */
 } nvfp4_moe_weights;
 
 enum {

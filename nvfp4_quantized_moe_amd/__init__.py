@@ -15,7 +15,7 @@ import os
 import torch
 
 __all__ = [
-    "lib", "LIB_PATH", "NVFP4Error", "EPI_BF16", "EPI_SILU_MUL", "WS_REGIONS", "nvfp4_quantize",
+    "lib", "LIB_PATH", "NVFP4Error", "EPI_BF16", "EPI_SILU_MUL", "EPI_SILU_MUL_DUAL", "WS_REGIONS", "nvfp4_quantize",
     "nvfp4_quantize_ws_bytes", "moe_route_slots", "moe_route_ws_bytes", "nvfp4_tile_table_len",
     "nvfp4_grouped_gemm", "moe_weighted_scatter", "nvfp4_fold_scales", "nvfp4_packed_bytes",
     "nvfp4_pack_weights", "nvfp4_moe_forward",
@@ -28,7 +28,7 @@ if not os.path.exists(LIB_PATH):
     raise ImportError(f"{LIB_PATH} is not built; run `python __graft_entry__.py` (build()) first")
 lib = ctypes.CDLL(LIB_PATH)
 
-EPI_BF16, EPI_SILU_MUL = 0, 1
+EPI_BF16, EPI_SILU_MUL, EPI_SILU_MUL_DUAL = 0, 1, 2
 WS_REGIONS = ["x_q", "x_sf", "scalars", "counts", "offsets", "slot_token", "slot_expert", "slot_weight",
               "token_slot", "tiles", "route_scratch", "h", "h_q", "h_sf", "y", "quant_scratch", "end"]
 
@@ -37,7 +37,7 @@ _vp, _i32, _i64, _sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c
 
 class _Weights(ctypes.Structure):
     _fields_ = [("num_local", _i32), ("hidden", _i32), ("inter", _i32),
-                ("w1", _vp), ("w1_gs", _vp), ("w2", _vp), ("w2_gs", _vp)]
+                ("w1", _vp), ("w1_gs", _vp), ("w2", _vp), ("w2_gs", _vp), ("w1_dual_gs", _i32)]
 
 
 def _sig(name, res, *args):
@@ -186,7 +186,7 @@ def nvfp4_grouped_gemm(a_q, a_sf, a_row_index, a_gs, b_packed, b_gs, offsets, ti
     L, n32, k128, chunk = b_packed.shape
     N, K = n32 * 32, k128 * 128
     dev = b_packed.device
-    n_out = N // 2 if epilogue == EPI_SILU_MUL else N
+    n_out = N // 2 if epilogue in (EPI_SILU_MUL, EPI_SILU_MUL_DUAL) else N
     d = torch.empty((rows_cap, n_out), dtype=torch.bfloat16, device=dev) if d is None else d
     _check(_gemm(_ptr(a_q), _ptr(a_sf), _ptr(a_row_index), _ptr(a_gs), _ptr(b_packed), _ptr(b_gs),
                  _ptr(offsets), _ptr(tile_table), L, rows_cap, N, K, tile_m, epilogue, _ptr(d), _ptr(amax_out),
@@ -241,24 +241,29 @@ def ws_view(ws, layout, region, dtype, shape):
 
 class MoEWeights:
     """Device NVFP4 layer weights for one rank (L local experts): packed W1
-    (gate rows then up rows, scales folded to w1_gs) and packed W2. With
-    keep_unpacked, prepare_weights also keeps the row-major forms (w1_q,
-    w1_sf, w2_q, w2_sf) for inspection."""
+    (gate rows then up rows) and packed W2. W1's gate/up scales are either
+    folded to one global scale per expert (w1_gs [L]) or kept per half
+    (w1_gs [L, 2] = gs_gate, gs_up). With keep_unpacked, prepare_weights also
+    keeps the row-major forms (w1_q, w1_sf, w2_q, w2_sf) for inspection."""
 
     def __init__(self, w1, w1_gs, w2, w2_gs):
         self.w1, self.w1_gs, self.w2, self.w2_gs = w1, w1_gs, w2, w2_gs
+        self.dual_gs = w1_gs.dim() == 2
         self.num_local = w1.shape[0]
         self.inter = w1.shape[1] * 32 // 2
         self.hidden = w1.shape[2] * 128
         if tuple(w2.shape[:3]) != (self.num_local, self.hidden // 32, self.inter // 128):
             raise ValueError(f"packed W2 shape {tuple(w2.shape)} does not match W1 {tuple(w1.shape)}")
+        if tuple(w1_gs.shape) not in ((self.num_local,), (self.num_local, 2)) or not w1_gs.is_contiguous():
+            raise ValueError(f"w1_gs shape {tuple(w1_gs.shape)}: expected [L] or [L, 2], contiguous")
         self._c = _Weights(self.num_local, self.hidden, self.inter, w1.data_ptr(), w1_gs.data_ptr(),
-                           w2.data_ptr(), w2_gs.data_ptr())
+                           w2.data_ptr(), w2_gs.data_ptr(), 1 if self.dual_gs else 0)
 
 
-def prepare_weights(w_gate, w_up, w_down, keep_unpacked=False) -> MoEWeights:
+def prepare_weights(w_gate, w_up, w_down, keep_unpacked=False, fold=True) -> MoEWeights:
     """Offline weight preparation on the GPU: quantize each (expert, projection)
-    with its own global scale, fold the gate/up scale ratio, and pack both
+    with its own global scale, fold the gate/up scale ratio (or, with
+    fold=False, keep both halves' scales and global scales), and pack both
     matrices for the grouped GEMM.
 
     w_gate, w_up: BF16 [L, I, H]; w_down: BF16 [L, H, I].
@@ -271,7 +276,7 @@ def prepare_weights(w_gate, w_up, w_down, keep_unpacked=False) -> MoEWeights:
     w1_sf = sf1.view(L, 2 * I, H // 16)
     gs_pair = gs_pair.view(L, 2)
     gs_gate, gs_up = gs_pair[:, 0].contiguous(), gs_pair[:, 1].contiguous()
-    w1_gs = nvfp4_fold_scales(w1_sf, gs_gate, gs_up)
+    w1_gs = nvfp4_fold_scales(w1_sf, gs_gate, gs_up) if fold else gs_pair.contiguous()
     w2_q, w2_sf, w2_gs = nvfp4_quantize(w_down.contiguous())
     w = MoEWeights(nvfp4_pack_weights(w1_q, w1_sf), w1_gs, nvfp4_pack_weights(w2_q, w2_sf), w2_gs)
     w.gs_gate, w.gs_up = gs_gate, gs_up

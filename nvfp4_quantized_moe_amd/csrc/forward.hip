@@ -83,6 +83,7 @@ extern "C" int nvfp4_moe_forward(const nvfp4_moe_weights* w, const void* x_bf16,
   if ((int64_t)2 * I * H / 32 * 18 >= (1ll << 31) || (int64_t)T * (H / 2) >= (1ll << 31) ||
       (int64_t)T * k * (I / 2) >= (1ll << 31))
     return NVFP4_ERR_SHAPE;
+  if (w->w1_dual_gs != 0 && w->w1_dual_gs != 1) return NVFP4_ERR_ARG;
   if (!w->w1 || !w->w1_gs || !w->w2 || !w->w2_gs || !ws) return NVFP4_ERR_NULL;
   if (T > 0 && (!x_bf16 || !topk_ids || !topk_w || !out_bf16)) return NVFP4_ERR_NULL;
   if (!nvfp4_aligned16(w->w1) || !nvfp4_aligned16(w->w2) || !nvfp4_aligned16(ws)) return NVFP4_ERR_ALIGN;
@@ -126,8 +127,9 @@ extern "C" int nvfp4_moe_forward(const nvfp4_moe_weights* w, const void* x_bf16,
   if (cap > 0) {
     // a4/a5: L1 with the fused SiLU*up epilogue and amax of h
     if ((st = nvfp4_launch_grouped_gemm(x_q, x_sf, slot_token, &scalars[0], w->w1, w->w1_gs, offsets,
-                                        tiles, L, cap, 2 * I, H, tile_m, NVFP4_EPI_SILU_MUL, h, &scalars[1],
-                                        stream)))
+                                        tiles, L, cap, 2 * I, H, tile_m,
+                                        w->w1_dual_gs ? NVFP4_EPI_SILU_MUL_DUAL : NVFP4_EPI_SILU_MUL, h,
+                                        &scalars[1], stream)))
       return st;
   }
   // a6: re-quantize the S valid rows of h with gs_h = amax_h / 2688

@@ -127,7 +127,7 @@ __global__ __launch_bounds__(64 * WAVES) void grouped_gemm_kernel(
     const uint8_t* __restrict__ a_q, const uint8_t* __restrict__ a_sf, const int32_t* __restrict__ a_row_index,
     const float* __restrict__ a_gs, const uint8_t* __restrict__ b_packed, const float* __restrict__ b_gs,
     const int32_t* __restrict__ offsets, const int32_t* __restrict__ tile_table, int max_tiles, int N, int K,
-    int n_out, int n_ntiles, int col_fastest, uint16_t* __restrict__ d, float* __restrict__ amax_out) {
+    int n_out, int n_ntiles, int col_fastest, int dual_gs, uint16_t* __restrict__ d, float* __restrict__ amax_out) {
   using C = GemmCfg<SUB_M, SUB_N, WAVES, P>;
   extern __shared__ __align__(16) uint8_t lds[];
   const int tid = threadIdx.x;
@@ -159,7 +159,9 @@ __global__ __launch_bounds__(64 * WAVES) void grouped_gemm_kernel(
     const int e = tile_table[1 + 2 * mt];
     const int r0 = tile_table[2 + 2 * mt];
     const int r_end = min(r0 + C::BM, offsets[e + 1]);
-    const float alpha = a_gs[0] * b_gs[e];
+    // one global scale per expert, or (gate, up) pairs for an unfolded L1 weight
+    const float alpha = a_gs[0] * b_gs[dual_gs ? 2 * e : e];
+    const float alpha_up = dual_gs ? a_gs[0] * b_gs[2 * e + 1] : alpha;
     const __amdgpu_buffer_rsrc_t rbw = make_rsrc(b_packed + (size_t)e * b_bytes, b_bytes);
 
     // activation staging tasks of this thread: 16 FP4 bytes + 2 scale bytes per
@@ -321,7 +323,7 @@ __global__ __launch_bounds__(64 * WAVES) void grouped_gemm_kernel(
             const int col = nt * (C::BN / 2) + (ch >> 1) * 32 + lr;
             if (col >= n_out) continue;
             const float g = bf16_to_f32(f32_to_bf16(acc[i][j][v] * alpha));
-            const float u = bf16_to_f32(f32_to_bf16(acc[i][j + 1][v] * alpha));
+            const float u = bf16_to_f32(f32_to_bf16(acc[i][j + 1][v] * alpha_up));
             const uint32_t h = f32_to_bf16(silu_f32(g) * u);
             d[(size_t)row * n_out + col] = (uint16_t)h;
             amax_local = fmaxf(amax_local, fabsf(bf16_to_f32(h)));
@@ -347,7 +349,7 @@ template <int SUB_M, int SUB_N, int WAVES, int P, int EPI>
 static int launch_cfg(const uint8_t* a_q, const uint8_t* a_sf, const int32_t* a_row_index, const float* a_gs,
                       const uint8_t* b_packed, const float* b_gs, const int32_t* offsets,
                       const int32_t* tile_table, int32_t num_local, int32_t rows_cap, int32_t N, int32_t K,
-                      void* d, float* amax_out, hipStream_t stream, int col_fastest = 0) {
+                      void* d, float* amax_out, hipStream_t stream, int dual_gs = 0, int col_fastest = 0) {
   using C = GemmCfg<SUB_M, SUB_N, WAVES, P>;
   static_assert(EPI != NVFP4_EPI_SILU_MUL || SUB_N % 2 == 0, "gate/up pairs live in one wave");
   const int n_out = EPI == NVFP4_EPI_SILU_MUL ? N / 2 : N;
@@ -378,7 +380,7 @@ static int launch_cfg(const uint8_t* a_q, const uint8_t* a_sf, const int32_t* a_
   if (grid >= kXcds) grid -= grid % kXcds;
   if (grid < 1) grid = 1;
   hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(C::THREADS), C::LDS, stream, a_q, a_sf, a_row_index, a_gs,
-                     b_packed, b_gs, offsets, tile_table, max_tiles, N, K, n_out, n_ntiles, col_fastest,
+                     b_packed, b_gs, offsets, tile_table, max_tiles, N, K, n_out, n_ntiles, col_fastest, dual_gs,
                      reinterpret_cast<uint16_t*>(d), amax_out);
   NVFP4_CHECK_LAUNCH();
   return NVFP4_OK;
@@ -399,10 +401,10 @@ int nvfp4_launch_grouped_gemm(const uint8_t* a_q, const uint8_t* a_sf, const int
                               int32_t rows_cap, int32_t N, int32_t K, int32_t tile_m, int32_t epilogue, void* d,
                               float* amax_out, hipStream_t stream) {
 #define NVFP4_GEMM_ARGS a_q, a_sf, a_row_index, a_gs, b_packed, b_gs, offsets, tile_table, num_local, rows_cap, \
-                        N, K, d, amax_out, stream
+                        N, K, d, amax_out, stream, epilogue == NVFP4_EPI_SILU_MUL_DUAL ? 1 : 0
 #define NVFP4_GEMM_CFG(SM, SN, W, PF)                                                          \
-  return epilogue == NVFP4_EPI_SILU_MUL ? launch_cfg<SM, SN, W, PF, NVFP4_EPI_SILU_MUL>(NVFP4_GEMM_ARGS) \
-                                        : launch_cfg<SM, SN, W, PF, NVFP4_EPI_BF16>(NVFP4_GEMM_ARGS)
+  return epilogue != NVFP4_EPI_BF16 ? launch_cfg<SM, SN, W, PF, NVFP4_EPI_SILU_MUL>(NVFP4_GEMM_ARGS) \
+                                    : launch_cfg<SM, SN, W, PF, NVFP4_EPI_BF16>(NVFP4_GEMM_ARGS)
   switch (tile_m) {
     case 32: NVFP4_GEMM_CFG(1, 2, 4, 3);
     case 64: NVFP4_GEMM_CFG(2, 2, 8, 4);
@@ -418,12 +420,14 @@ extern "C" int nvfp4_grouped_gemm(const uint8_t* a_q, const uint8_t* a_sf, const
                                   const int32_t* offsets, const int32_t* tile_table, int32_t num_local,
                                   int32_t rows_cap, int32_t N, int32_t K, int32_t tile_m, int32_t epilogue, void* d,
                                   float* amax_out, void* stream) {
-  if (epilogue != NVFP4_EPI_BF16 && epilogue != NVFP4_EPI_SILU_MUL) return NVFP4_ERR_ARG;
+  if (epilogue != NVFP4_EPI_BF16 && epilogue != NVFP4_EPI_SILU_MUL && epilogue != NVFP4_EPI_SILU_MUL_DUAL)
+    return NVFP4_ERR_ARG;
+  const bool silu = epilogue != NVFP4_EPI_BF16;
   if (num_local < 1 || rows_cap < 0 || N <= 0 || K <= 0 || K % kBK != 0 || N % 64 != 0) return NVFP4_ERR_SHAPE;
-  if (epilogue == NVFP4_EPI_SILU_MUL && N % 128 != 0) return NVFP4_ERR_SHAPE;
+  if (silu && N % 128 != 0) return NVFP4_ERR_SHAPE;
   if (tile_m != 32 && tile_m != 64 && tile_m != 128) return NVFP4_ERR_SHAPE;
   if (!a_q || !a_sf || !a_gs || !b_packed || !b_gs || !offsets || !tile_table || !d) return NVFP4_ERR_NULL;
-  if (epilogue == NVFP4_EPI_SILU_MUL && !amax_out) return NVFP4_ERR_NULL;
+  if (silu && !amax_out) return NVFP4_ERR_NULL;
   if (!nvfp4_aligned16(a_q) || !nvfp4_aligned16(a_sf) || !nvfp4_aligned16(b_packed) || !nvfp4_aligned16(d))
     return NVFP4_ERR_ALIGN;
   // buffer offsets are 32-bit: activation row offsets and one expert's packed weights stay below 2^31

@@ -40,13 +40,19 @@ def fold_gate_up(w1_sf: np.ndarray, gs_gate: np.ndarray, gs_up: np.ndarray, inte
     return sf, gs1
 
 
-def prepare_weights(w_gate: np.ndarray, w_up: np.ndarray, w_down: np.ndarray, map_fn=map) -> dict:
+def prepare_weights(w_gate: np.ndarray, w_up: np.ndarray, w_down: np.ndarray, map_fn=map,
+                    fold: bool = True) -> dict:
     """BF16 bits W_gate, W_up [L, I, H] and W_down [L, H, I] -> NVFP4 layer weights.
 
     Each (expert, projection) is quantized on its own (own gs); the gate/up
     ratio is then folded. map_fn lets a caller spread experts over threads.
     Returns w1_q [L, 2I, H/2], w1_sf [L, 2I, H/16], w1_gs [L] (= gs1),
     w2_q [L, H, I/2], w2_sf [L, H, I/16], w2_gs [L], plus gs_gate and gs_up.
+
+    fold=False keeps both halves' block scales as quantized and returns
+    w1_gs [L, 2] = (gs_gate, gs_up): the L1 GEMM then applies one alpha per
+    half (the alpha commit's treatment of a global scale, applied to gate and
+    up separately) instead of the finalize_weights fold.
     """
     L, I, H = w_gate.shape
     res = list(map_fn(lambda e: (quantize(w_gate[e]), quantize(w_up[e]), quantize(w_down[e])),
@@ -55,7 +61,10 @@ def prepare_weights(w_gate: np.ndarray, w_up: np.ndarray, w_down: np.ndarray, ma
     w1_sf = np.stack([np.concatenate([g[1], u[1]]) for g, u, _ in res])
     gs_gate = np.array([g[2] for g, _, _ in res], np.float32)
     gs_up = np.array([u[2] for _, u, _ in res], np.float32)
-    w1_sf, gs1 = fold_gate_up(w1_sf, gs_gate, gs_up, I)
+    if fold:
+        w1_sf, gs1 = fold_gate_up(w1_sf, gs_gate, gs_up, I)
+    else:
+        gs1 = np.stack([gs_gate, gs_up], axis=1).astype(np.float32)
     w2_q = np.stack([d[0] for _, _, d in res])
     w2_sf = np.stack([d[1] for _, _, d in res])
     w2_gs = np.array([d[2] for _, _, d in res], np.float32)

@@ -47,8 +47,11 @@ def grouped_gemm(a_q, a_sf, a_row_index, a_gs, b_q, b_sf, b_gs, offsets, map_fn=
     Row s in [offsets[e], offsets[e+1]) uses A row a_row_index[s] (or s when
     a_row_index is None) and expert e's weight b_q[e] [N, K/2] / b_sf[e] [N, K/16].
     Returns float32 [S, N] = RN_f32(alpha_e * (A_hat @ W_hat_e^T)) with
-    alpha_e = RN_f32(a_gs * b_gs[e]). Experts are independent; map_fn lets a
-    caller run them on several threads (same result).
+    alpha_e = RN_f32(a_gs * b_gs[e]). With b_gs of shape [L, 2] (gate and up
+    global scales of an unfolded L1 weight), columns [0, N/2) take
+    RN_f32(a_gs * b_gs[e, 0]) and columns [N/2, N) RN_f32(a_gs * b_gs[e, 1]).
+    Experts are independent; map_fn lets a caller run them on several
+    threads (same result).
     """
     offsets = np.asarray(offsets)
     L = len(offsets) - 1
@@ -64,8 +67,13 @@ def grouped_gemm(a_q, a_sf, a_row_index, a_gs, b_q, b_sf, b_gs, offsets, map_fn=
         a_hat = _deq32(a_q[rows], a_sf[rows])
         w_hat = _deq32(b_q[e], b_sf[e])
         acc = np.matmul(a_hat, w_hat.T)
-        alpha = np.float32(np.float32(a_gs) * np.float32(b_gs[e]))
-        out[r0:r1] = acc * alpha
+        gs_e = np.asarray(b_gs[e], np.float32)
+        if gs_e.ndim == 0:
+            out[r0:r1] = acc * np.float32(np.float32(a_gs) * gs_e)
+        else:
+            half = N // 2
+            out[r0:r1, :half] = acc[:, :half] * np.float32(np.float32(a_gs) * gs_e[0])
+            out[r0:r1, half:] = acc[:, half:] * np.float32(np.float32(a_gs) * gs_e[1])
 
     list(map_fn(one, range(L)))
     return out

@@ -209,10 +209,12 @@ GEMM_CASES = {
 
 @pytest.mark.parametrize("case", list(GEMM_CASES))
 @pytest.mark.parametrize("tile_m", [32, 64, 128])
-@pytest.mark.parametrize("epi", [0, 1])
+@pytest.mark.parametrize("epi", [0, 1, 2])
 def test_grouped_gemm(nv, case, tile_m, epi):
     L, N, K, T, counts, gather = GEMM_CASES[case]
     a_q, a_sf, ri, a_gs, b_q, b_sf, b_gs, offsets = _gemm_inputs(len(case), L, N, K, T, counts, gather)
+    if epi == 2:   # gate and up halves with their own global scales
+        b_gs = np.stack([b_gs, np.random.default_rng(L + N).uniform(0.01, 2.0, L).astype(np.float32)], axis=1)
     S = int(offsets[-1])
     cap = max(S, 1) + 7
     counts_np = np.diff(offsets)
@@ -220,19 +222,19 @@ def test_grouped_gemm(nv, case, tile_m, epi):
     tt = np.zeros(nv.nvfp4_tile_table_len(cap, L, tile_m), np.int32)
     tt[0] = len(tiles)
     tt[1:1 + 2 * len(tiles)] = tiles.reshape(-1)
-    n_out = N // 2 if epi == 1 else N
+    n_out = N // 2 if epi in (1, 2) else N
     canary = torch.full((cap, n_out), -7.0, dtype=torch.bfloat16, device=DEV)
     amax = torch.zeros(1, dtype=torch.float32, device=DEV)
     log(f"gemm {case} tile_m={tile_m} epi={epi} S={S}")
     b_packed = nv.nvfp4_pack_weights(to_dev(b_q), to_dev(b_sf))
     d = nv.nvfp4_grouped_gemm(to_dev(a_q), to_dev(a_sf), None if ri is None else to_dev(ri), to_dev(a_gs),
                               b_packed, to_dev(b_gs), to_dev(offsets), to_dev(tt), cap, tile_m,
-                              epilogue=epi, d=canary, amax_out=amax if epi == 1 else None)
+                              epilogue=epi, d=canary, amax_out=amax if epi in (1, 2) else None)
     torch.cuda.synchronize()
     got = d.float().cpu().numpy()
     assert np.all(got[S:] == -7.0), "rows outside the tiles were written"
     g = O.grouped_gemm(a_q, a_sf, ri, a_gs[0], b_q, b_sf, b_gs, offsets)
-    if epi == 1:
+    if epi in (1, 2):
         ref = O.bf16_to_f32(O.silu_mul(g, N // 2))
         h = got[:S]
         assert amax.item() == (float(np.abs(h).max()) if S else 0.0)
@@ -257,18 +259,22 @@ def _layer_inputs(name):
 def _deq_ref(P, cfg, x, ids, w):
     L, I = cfg.num_local, cfg.inter
     f = lambda q, sf, gs: O.f32_to_bf16(O.dequantize(q, sf, gs, np.float32))
-    dg = np.stack([f(P["w1_q"][e, :I], P["w1_sf"][e, :I], P["w1_gs"][e]) for e in range(L)])
-    du = np.stack([f(P["w1_q"][e, I:], P["w1_sf"][e, I:], P["w1_gs"][e]) for e in range(L)])
+    g1 = np.asarray(P["w1_gs"])
+    gs_g = g1[:, 0] if g1.ndim == 2 else g1
+    gs_u = g1[:, 1] if g1.ndim == 2 else g1
+    dg = np.stack([f(P["w1_q"][e, :I], P["w1_sf"][e, :I], gs_g[e]) for e in range(L)])
+    du = np.stack([f(P["w1_q"][e, I:], P["w1_sf"][e, I:], gs_u[e]) for e in range(L)])
     dd = np.stack([f(P["w2_q"][e], P["w2_sf"][e], P["w2_gs"][e]) for e in range(L)])
     return O.bf16_reference_layer(x, ids, w, cfg.expert_start, dg, du, dd)
 
 
-@pytest.mark.parametrize("name", ["tiny", "mid", "mid_k1", "mid_skew"])
-def test_layer(nv, name):
+@pytest.mark.parametrize("name,fold", [("tiny", True), ("mid", True), ("mid_k1", True), ("mid_skew", True),
+                                       ("tiny", False), ("mid_skew", False)])
+def test_layer(nv, name, fold):
     cfg, ids, w, x, wg, wu, wd = _layer_inputs(name)
-    log(f"layer {name} T={cfg.tokens} k={cfg.top_k} L={cfg.num_local} H={cfg.hidden} I={cfg.inter}")
-    weights = nv.prepare_weights(to_bf16(wg), to_bf16(wu), to_bf16(wd), keep_unpacked=True)
-    P = O.prepare_weights(wg, wu, wd)
+    log(f"layer {name} fold={fold} T={cfg.tokens} k={cfg.top_k} L={cfg.num_local} H={cfg.hidden} I={cfg.inter}")
+    weights = nv.prepare_weights(to_bf16(wg), to_bf16(wu), to_bf16(wd), keep_unpacked=True, fold=fold)
+    P = O.prepare_weights(wg, wu, wd, fold=fold)
     for key in ("w1_q", "w1_sf", "w1_gs", "w2_q", "w2_sf", "w2_gs"):
         assert np.array_equal(getattr(weights, key).cpu().numpy(), P[key]), key
     assert np.array_equal(weights.w1.cpu().numpy(), pack_weights_np(P["w1_q"], P["w1_sf"]))

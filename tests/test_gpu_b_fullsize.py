@@ -71,16 +71,22 @@ def nv():
 
 
 class Shard:
-    def __init__(self, nv, weight_cfg):
+    def __init__(self, nv, weight_cfg, fold=True, bf16_from=None):
         t = time.time()
-        self.wg, self.wu, self.wd = W.make_weights(weight_cfg)
+        if bf16_from is None:
+            self.wg, self.wu, self.wd = W.make_weights(weight_cfg)
+        else:
+            self.wg, self.wu, self.wd = bf16_from.wg, bf16_from.wu, bf16_from.wd
         log(f"{weight_cfg.name} weights generated in {time.time() - t:.1f}s")
         t = time.time()
-        self.gpu = nv.prepare_weights(to_bf16(self.wg), to_bf16(self.wu), to_bf16(self.wd), keep_unpacked=True)
+        self.gpu = nv.prepare_weights(to_bf16(self.wg), to_bf16(self.wu), to_bf16(self.wd), keep_unpacked=True,
+                                      fold=fold)
         torch.cuda.synchronize()
         with ThreadPoolExecutor(THREADS) as ex:
-            self.P = O.prepare_weights(self.wg, self.wu, self.wd, map_fn=ProgressMap(ex, "oracle weights"))
-        log(f"{weight_cfg.name} weights prepared (GPU + oracle on {THREADS} threads) in {time.time() - t:.1f}s")
+            self.P = O.prepare_weights(self.wg, self.wu, self.wd, map_fn=ProgressMap(ex, "oracle weights"),
+                                       fold=fold)
+        log(f"{weight_cfg.name} weights (fold={fold}) prepared (GPU + oracle on {THREADS} threads) "
+            f"in {time.time() - t:.1f}s")
 
 
 @pytest.fixture(scope="module")
@@ -91,6 +97,11 @@ def shared(nv):
 @pytest.fixture(scope="module")
 def skewed(nv):
     return Shard(nv, W.get_config("skewed"))
+
+
+@pytest.fixture(scope="module")
+def skewed_unfolded(nv, skewed):
+    return Shard(nv, W.get_config("skewed"), fold=False, bf16_from=skewed)
 
 
 def _check_weights(nv, sh):
@@ -130,7 +141,7 @@ def _cosines(sh, cfg, x, ids, w, got):
     return c_deq, c_bf16
 
 
-def _run(nv, sh, name, cosine=False):
+def _run(nv, sh, name, cosine=False, return_out=False):
     cfg = W.get_config(name)
     ids, w = W.make_router(cfg)
     x = W.make_activations(cfg)
@@ -164,6 +175,8 @@ def _run(nv, sh, name, cosine=False):
         assert c_deq >= 0.98
     out2 = nv.nvfp4_moe_forward(sh.gpu, to_bf16(x), to_dev(ids), to_dev(w), cfg.expert_start, ws=ws)
     assert torch.equal(out2.view(torch.int16), out.view(torch.int16))
+    if return_out:
+        return got
 
 
 def test_full_weights_bit_exact(nv, shared):
@@ -182,3 +195,25 @@ def test_full_skewed(nv, skewed):
     _check_weights(nv, skewed)
     assert np.all(skewed.P["gs_up"] > 20 * skewed.P["gs_gate"])
     _run(nv, skewed, "skewed")
+
+
+def test_full_skewed_unfolded_scales(nv, skewed, skewed_unfolded):
+    """Gate and up keep their own global scales (30x apart) instead of the
+    fold: weights bit for bit, layer output within tolerance of the oracle in
+    the same mode. Logs the accuracy ablation: cosine of both treatments
+    against the layer built from the original BF16 weights."""
+    for key in ("w1_q", "w1_sf", "w1_gs"):
+        assert np.array_equal(getattr(skewed_unfolded.gpu, key).cpu().numpy(), skewed_unfolded.P[key]), key
+    assert np.array_equal(skewed_unfolded.gpu.w1.cpu().numpy(),
+                          pack_weights_np(skewed_unfolded.P["w1_q"], skewed_unfolded.P["w1_sf"]))
+    got_dual = _run(nv, skewed_unfolded, "skewed", return_out=True)
+    got_fold = _run(nv, skewed, "skewed", return_out=True)
+    cfg = W.get_config("skewed")
+    ids, w = W.make_router(cfg)
+    x = W.make_activations(cfg)
+    t = time.time()
+    ref = O.bf16_reference_layer(x, ids, w, cfg.expert_start, skewed.wg, skewed.wu, skewed.wd)
+    c_fold, c_dual = O.cosine(got_fold, ref), O.cosine(got_dual, ref)
+    log(f"skewed ablation (BF16 reference {time.time() - t:.1f}s): cosine vs original BF16 weights "
+        f"{c_fold:.5f} with the gate/up fold, {c_dual:.5f} with per-half global scales")
+    assert c_fold > 0.9 and c_dual > 0.9

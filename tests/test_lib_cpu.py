@@ -75,6 +75,7 @@ def test_invalid_arguments_are_rejected_before_launch():
     g = [buf] * 8
     assert nv._gemm(*g, 8, 64, 256, 96, 32, 0, buf, null, s) == 2
     assert nv._gemm(*g, 8, 64, 256, 256, 32, 7, buf, null, s) == 6
+    assert nv._gemm(*g, 8, 64, 256, 256, 32, 2, buf, null, s) == 1   # dual-scale SiLU also needs amax_out
     assert nv._gemm(*g, 8, 64, 256, 256, 48, 0, buf, null, s) == 2
     assert nv._gemm(*g, 8, 64, 256, 256, 32, 1, buf, null, s) == 1   # SiLU epilogue needs amax_out
     # packed size / pack: N not a multiple of 32, K not a multiple of 128, NULL input, misaligned output
@@ -97,3 +98,5 @@ def test_invalid_arguments_are_rejected_before_launch():
     assert nv._forward(ctypes.byref(w), buf, 4, buf, buf, 2, 0, buf, buf, 1 << 30, s) == 1
     w = nv._Weights(8, 256, 128, 4097, 4096, 4096, 4096)
     assert nv._forward(ctypes.byref(w), buf, 4, buf, buf, 2, 0, buf, buf, 1 << 30, s) == 3
+    w = nv._Weights(8, 256, 128, 4096, 4096, 4096, 4096, 2)     # unknown gate/up scale mode
+    assert nv._forward(ctypes.byref(w), buf, 4, buf, buf, 2, 0, buf, buf, 1 << 30, s) == 6

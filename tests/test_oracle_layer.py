@@ -208,3 +208,59 @@ def test_bf16_reference_layer_dense_case():
     assert np.allclose(got, want, rtol=1e-4, atol=1e-5 * np.abs(want).max())
     # ids outside the local range contribute nothing
     assert not O.bf16_reference_layer(x, ids, w, 6, wg, wu, wd).any()
+
+
+# ----------------------------------------------------- gate/up scales kept per half
+
+def test_dual_scale_gemm_brute_force():
+    """Unfolded L1 weight: columns [0, N/2) take alpha from the gate global
+    scale, [N/2, N) from the up global scale (float64 triple loop)."""
+    rng = np.random.default_rng(3)
+    L, N, K, T = 2, 8, 64, 6
+    a_q, a_sf = W.random_fp4_operands(4, T, K)
+    b_q, b_sf = W.random_fp4_operands(5, L * N, K)
+    b_q, b_sf = b_q.reshape(L, N, K // 2), b_sf.reshape(L, N, K // 16)
+    offsets = np.array([0, 3, 7], np.int32)
+    row_index = rng.integers(0, T, 7).astype(np.int32)
+    a_gs = np.float32(0.5)
+    b_gs = np.array([[0.25, 7.5], [3.0, 0.125]], np.float32)
+    got = O.grouped_gemm(a_q, a_sf, row_index, a_gs, b_q, b_sf, b_gs, offsets)
+    A = _decode_bits_loop(a_q, a_sf)
+    for e in range(L):
+        Bm = _decode_bits_loop(b_q[e], b_sf[e])
+        for s in range(offsets[e], offsets[e + 1]):
+            for n in range(N):
+                acc = sum(A[row_index[s], kk] * Bm[n, kk] for kk in range(K))
+                alpha = float(np.float32(a_gs) * np.float32(b_gs[e, 0 if n < N // 2 else 1]))
+                assert abs(got[s, n] - alpha * acc) <= 1e-5 * max(1.0, abs(alpha * acc))
+
+
+def test_unfolded_equals_folded_when_gate_and_up_scales_match():
+    """With W_up = W_gate every expert's two global scales are equal, the fold
+    changes nothing, and both treatments give the same layer bit for bit."""
+    cfg = W.get_config("tiny")
+    ids, w = W.make_router(cfg)
+    x = W.make_activations(cfg)
+    wg, _, wd = W.make_weights(cfg)
+    P_fold = O.prepare_weights(wg, wg, wd)
+    P_dual = O.prepare_weights(wg, wg, wd, fold=False)
+    assert np.array_equal(P_fold["w1_sf"], P_dual["w1_sf"])
+    assert np.array_equal(P_dual["w1_gs"][:, 0], P_dual["w1_gs"][:, 1])
+    a = O.moe_forward(x, ids, w, cfg.expert_start, P_fold).out
+    b = O.moe_forward(x, ids, w, cfg.expert_start, P_dual).out
+    assert np.array_equal(a, b)
+
+
+def test_unfolded_keeps_the_quantized_scales():
+    """fold=False leaves both halves exactly as quantized: each half
+    dequantizes with its own global scale to within the quantizer's bound."""
+    cfg = W.get_config("mid_skew")
+    wg, wu, wd = W.make_weights(cfg, experts=[0, 1])
+    P = O.prepare_weights(wg, wu, wd, fold=False)
+    I = cfg.inter
+    for e in range(2):
+        for half, src in ((slice(0, I), wg[e]), (slice(I, 2 * I), wu[e])):
+            gs = P["w1_gs"][e, 0 if half.start == 0 else 1]
+            q, sf, gs_ref = O.quantize(src)
+            assert gs == gs_ref
+            assert np.array_equal(P["w1_q"][e, half], q) and np.array_equal(P["w1_sf"][e, half], sf)
