@@ -27,6 +27,7 @@
 // h path) only the quantize kernel runs.
 #include "common.h"
 #include "internal.h"
+#include "amax.h"
 
 namespace nvfp4 {
 
@@ -39,40 +40,11 @@ __global__ void fill_u32_kernel(uint32_t* p, int n, uint32_t v) {
   if (i < n) p[i] = v;
 }
 
-// Per-workgroup partial maxima: partial[b][blockIdx.x] = max |x| over the
-// workgroup's share of x[b], as float32 bits (|x| >= 0, so the unsigned order
-// of the bits is the order of the values). Every workgroup of the fixed grid
-// writes its slot, so nothing has to be cleared first. Workgroup (0, 0) also
-// zeroes clear[0..n_clear), which later kernels of the same stream use as
-// atomic-max targets.
 __global__ __launch_bounds__(256) void amax_kernel(const uint16_t* __restrict__ x, int64_t per_batch,
                                                    const int32_t* __restrict__ rows_dev, int64_t K,
                                                    uint32_t* __restrict__ partial, uint32_t* __restrict__ clear,
                                                    int n_clear) {
-  const int b = blockIdx.y;
-  if (blockIdx.x == 0 && b == 0 && (int)threadIdx.x < n_clear) clear[threadIdx.x] = 0u;
-  int64_t n = per_batch;
-  if (rows_dev) {
-    int64_t r = rows_dev[0];
-    n = min(n, r * K);
-  }
-  const uint4* xv = reinterpret_cast<const uint4*>(x + (int64_t)b * per_batch);
-  int64_t nv = n / 8;
-  uint32_t m = 0;
-  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < nv; i += (int64_t)gridDim.x * blockDim.x) {
-    uint4 v = xv[i];
-    uint32_t w[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      uint32_t lo = w[j] & 0x7FFFu, hi = (w[j] >> 16) & 0x7FFFu;
-      m = max(m, max(lo, hi));
-    }
-  }
-  m = wave_max_u32(m);
-  __shared__ uint32_t red[4];
-  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
-  __syncthreads();
-  if (threadIdx.x == 0) partial[(size_t)b * gridDim.x + blockIdx.x] = max(max(red[0], red[1]), max(red[2], red[3])) << 16;
+  amax_block(x, per_batch, rows_dev, K, partial, clear, n_clear, blockIdx.y, blockIdx.x, gridDim.x);
 }
 
 // amax of tensor b, gs = RN_f32(amax / 2688), and the threshold table of
@@ -214,6 +186,18 @@ int nvfp4_launch_quantize(const void* x_bf16, int64_t B, int64_t M, int64_t K, c
   else
     hipLaunchKernelGGL(quantize_kernel<false>, grid, dim3(256), 0, stream, x, M, K, rows_dev, amax_in, partial, gx,
                        gs_out, q, sf);
+  NVFP4_CHECK_LAUNCH();
+  return NVFP4_OK;
+}
+
+// Quantize one tensor whose amax partials (n_partial of them) are already in ws.
+int nvfp4_launch_quantize_from_partials(const void* x_bf16, int64_t M, int64_t K, const void* ws, int n_partial,
+                                        uint8_t* q, uint8_t* sf, float* gs_out, hipStream_t stream) {
+  const uint32_t* partial = reinterpret_cast<const uint32_t*>(ws);
+  const uint16_t* x = reinterpret_cast<const uint16_t*>(x_bf16);
+  dim3 grid((unsigned)quant_grid(M * (K / 16)), 1u);
+  hipLaunchKernelGGL(quantize_kernel<false>, grid, dim3(256), 0, stream, x, M, K, nullptr, nullptr, partial,
+                     n_partial, gs_out, q, sf);
   NVFP4_CHECK_LAUNCH();
   return NVFP4_OK;
 }

@@ -19,6 +19,7 @@
 // workgroup and one launch (route_small_kernel), with the same result.
 #include "common.h"
 #include "internal.h"
+#include "amax.h"
 
 namespace nvfp4 {
 
@@ -164,7 +165,7 @@ __global__ __launch_bounds__(kScanThreads) void route_scan_kernel(
 // The whole route in one workgroup when T*k <= kScanThreads (decode-sized
 // batches): histogram, scan and stable scatter, one flat entry per thread,
 // the waves taking turns in flat order on the running slot of each expert.
-__global__ __launch_bounds__(kScanThreads) void route_small_kernel(
+__device__ __forceinline__ void route_small_body(
     const int32_t* __restrict__ ids, const float* __restrict__ w, int32_t n, int32_t k, int32_t start, int32_t L,
     int tile_m, int nbits, int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
     int32_t* __restrict__ slot_token, int32_t* __restrict__ slot_expert, float* __restrict__ slot_weight,
@@ -261,6 +262,31 @@ __global__ __launch_bounds__(256) void route_scatter_kernel(
   }
 }
 
+__global__ __launch_bounds__(kScanThreads) void route_small_kernel(
+    const int32_t* __restrict__ ids, const float* __restrict__ w, int32_t n, int32_t k, int32_t start, int32_t L,
+    int tile_m, int nbits, int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
+    int32_t* __restrict__ slot_token, int32_t* __restrict__ slot_expert, float* __restrict__ slot_weight,
+    int32_t* __restrict__ token_slot, int32_t* __restrict__ tile_table) {
+  route_small_body(ids, w, n, k, start, L, tile_m, nbits, counts, offsets, slot_token, slot_expert, slot_weight,
+                   token_slot, tile_table);
+}
+
+// The layer's first launch for decode-sized batches: workgroups [0, gx) take
+// the amax partials of the activation tensor, workgroup gx routes. The two
+// steps are independent, so they share one launch.
+__global__ __launch_bounds__(kScanThreads) void amax_route_kernel(
+    const uint16_t* __restrict__ x, int64_t per, int64_t K, uint32_t* __restrict__ partial, int gx,
+    uint32_t* __restrict__ clear, int n_clear, const int32_t* __restrict__ ids, const float* __restrict__ w,
+    int32_t n, int32_t k, int32_t start, int32_t L, int tile_m, int nbits, int32_t* __restrict__ counts,
+    int32_t* __restrict__ offsets, int32_t* __restrict__ slot_token, int32_t* __restrict__ slot_expert,
+    float* __restrict__ slot_weight, int32_t* __restrict__ token_slot, int32_t* __restrict__ tile_table) {
+  if ((int)blockIdx.x < gx)
+    amax_block(x, per, nullptr, K, partial, clear, n_clear, 0, blockIdx.x, gx);
+  else
+    route_small_body(ids, w, n, k, start, L, tile_m, nbits, counts, offsets, slot_token, slot_expert,
+                     slot_weight, token_slot, tile_table);
+}
+
 }  // namespace nvfp4
 
 using namespace nvfp4;
@@ -307,6 +333,32 @@ int nvfp4_launch_route(const int32_t* topk_ids, const float* topk_w, int32_t T, 
                        expert_start, L, nbits, bases, offsets, slot_token, slot_expert, slot_weight, token_slot);
     NVFP4_CHECK_LAUNCH();
   }
+  return NVFP4_OK;
+}
+
+int nvfp4_amax_route_grid(int64_t per) {
+  int64_t gx = (per / 8 + kScanThreads - 1) / kScanThreads;
+  if (gx > 1024) gx = 1024;
+  if (gx < 1) gx = 1;
+  return (int)gx;
+}
+
+int nvfp4_launch_amax_route(const void* x_bf16, int64_t per, int64_t K, uint32_t* partial, uint32_t* clear,
+                            int n_clear, const int32_t* topk_ids, const float* topk_w, int32_t T, int32_t k,
+                            int32_t expert_start, int32_t num_local, int32_t tile_m, int32_t* counts,
+                            int32_t* offsets, int32_t* slot_token, int32_t* slot_expert, float* slot_weight,
+                            int32_t* token_slot, int32_t* tile_table, hipStream_t stream) {
+  const int n = T * k;
+  if (n > kScanThreads) return NVFP4_ERR_SHAPE;
+  const int L = num_local;
+  int nbits = 1;
+  while ((1 << nbits) <= L) ++nbits;
+  const int gx = nvfp4_amax_route_grid(per);
+  hipLaunchKernelGGL(amax_route_kernel, dim3(gx + 1), dim3(kScanThreads), 3 * L * 4, stream,
+                     reinterpret_cast<const uint16_t*>(x_bf16), per, K, partial, gx, clear, n_clear, topk_ids,
+                     topk_w, n, k, expert_start, L, tile_m, nbits, counts, offsets, slot_token, slot_expert,
+                     slot_weight, token_slot, tile_table);
+  NVFP4_CHECK_LAUNCH();
   return NVFP4_OK;
 }
 
