@@ -30,8 +30,9 @@ __global__ __launch_bounds__(256) void scatter_kernel(const uint16_t* __restrict
     s_w[threadIdx.x] = topk_w[(size_t)t * k + threadIdx.x];
   }
   __syncthreads();
+  // workgroup (t, y) takes every gridDim.y-th run of 256 8-element chunks of row t
   const int nchunk = H / 8;
-  for (int c = threadIdx.x; c < nchunk; c += blockDim.x) {
+  for (int c = blockIdx.y * blockDim.x + threadIdx.x; c < nchunk; c += gridDim.y * blockDim.x) {
     float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
     for (int j = 0; j < k; ++j) {
       const int s = s_slot[j];
@@ -85,7 +86,13 @@ using namespace nvfp4;
 int nvfp4_launch_scatter(const void* y_bf16, const int32_t* token_slot, const float* topk_w, int32_t T, int32_t k,
                          int32_t H, void* out_bf16, hipStream_t stream) {
   if (T == 0) return NVFP4_OK;
-  hipLaunchKernelGGL(scatter_kernel, dim3(T), dim3(256), 0, stream, reinterpret_cast<const uint16_t*>(y_bf16),
+  // small batches split each row over up to one chunk per thread, so that
+  // about 1024 workgroups run; large batches keep one workgroup per row
+  const int64_t gy_max = ((int64_t)H / 8 + 255) / 256;
+  int64_t gy = (1024 + T - 1) / T;
+  if (gy > gy_max) gy = gy_max;
+  if (gy > 65535) return NVFP4_ERR_SHAPE;
+  hipLaunchKernelGGL(scatter_kernel, dim3(T, (unsigned)gy), dim3(256), 0, stream, reinterpret_cast<const uint16_t*>(y_bf16),
                      token_slot, topk_w, T, k, H, reinterpret_cast<uint16_t*>(out_bf16));
   NVFP4_CHECK_LAUNCH();
   return NVFP4_OK;
