@@ -325,3 +325,60 @@ def test_layer_no_local_tokens_and_empty(nv):
     e = nv.nvfp4_moe_forward(weights, to_bf16(x[:0]), to_dev(ids[:0]), to_dev(w[:0]), 0)
     torch.cuda.synchronize()
     assert e.shape == (0, cfg.hidden)
+
+
+# ------------------------------------------------------------ layer edge cases
+
+def _edge_layer(nv, name, ids, w, x, cfg_name="mid"):
+    cfg = W.get_config(cfg_name)
+    wg, wu, wd = W.make_weights(cfg)
+    weights = nv.prepare_weights(to_bf16(wg), to_bf16(wu), to_bf16(wd))
+    P = O.prepare_weights(wg, wu, wd)
+    log(f"layer edge case {name}: T={ids.shape[0]} k={ids.shape[1]}")
+    out = nv.nvfp4_moe_forward(weights, to_bf16(x), to_dev(ids), to_dev(w), cfg.expert_start)
+    torch.cuda.synchronize()
+    tr = O.moe_forward(x, ids, w, cfg.expert_start, P)
+    return out.float().cpu().numpy(), O.bf16_to_f32(tr.out), tr
+
+
+def test_layer_zero_activations(nv):
+    """x = 0: gs_x = 0, every scale and magnitude 0, h = 0, gs_h = 0, out = 0."""
+    cfg = W.get_config("mid")
+    ids, w = W.make_router(cfg)
+    x = np.zeros((cfg.tokens, cfg.hidden), np.uint16)
+    got, ref, tr = _edge_layer(nv, "zero x", ids, w, x)
+    assert tr.gs_x == 0 and tr.gs_h == 0
+    assert np.array_equal(got, ref) and not np.any(got)
+
+
+def test_layer_single_token(nv):
+    cfg = W.get_config("mid")
+    ids, w = W.make_router(cfg)
+    x = W.make_activations(cfg)
+    got, ref, _ = _edge_layer(nv, "one token", ids[:1], w[:1], x[:1])
+    assert rel_err(got, ref) <= TOL
+
+
+def test_layer_all_tokens_one_expert(nv):
+    """Top-1 with every token on the same local expert: one group of T rows
+    (several row tiles), every other expert empty."""
+    cfg = W.get_config("mid")
+    T = 300
+    ids = np.full((T, 1), cfg.expert_start + 5, np.int32)
+    w = np.ones((T, 1), np.float32)
+    x = W.make_activations(cfg)
+    x = np.concatenate([x, x])[:T]
+    got, ref, tr = _edge_layer(nv, "one expert", ids, w, x)
+    assert tr.routing["counts"][5] == T and tr.routing["S"] == T
+    assert rel_err(got, ref) <= TOL
+
+
+def test_layer_duplicate_ids_in_a_token(nv):
+    """The same expert twice in one token's top-k: two slots, summed in j order."""
+    cfg = W.get_config("mid")
+    ids, w = W.make_router(cfg)
+    ids = ids.copy()
+    ids[:, 1] = ids[:, 0]
+    x = W.make_activations(cfg)
+    got, ref, tr = _edge_layer(nv, "duplicate ids", ids, w, x)
+    assert rel_err(got, ref) <= TOL

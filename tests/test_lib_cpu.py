@@ -98,5 +98,13 @@ def test_invalid_arguments_are_rejected_before_launch():
     assert nv._forward(ctypes.byref(w), buf, 4, buf, buf, 2, 0, buf, buf, 1 << 30, s) == 1
     w = nv._Weights(8, 256, 128, 4097, 4096, 4096, 4096)
     assert nv._forward(ctypes.byref(w), buf, 4, buf, buf, 2, 0, buf, buf, 1 << 30, s) == 3
+    # 32-bit offsets: T*H/2, T*k*I/2 and 2I*H*9/16 must stay below 2^31; T*k below 2^30
+    big = nv._Weights(8, 7168, 3072, 4096, 4096, 4096, 4096)
+    # (every call here fails validation: the pointers are fake and must never reach a launch)
+    assert nv._forward(ctypes.byref(big), buf, (1 << 31) // 3584 + 1, buf, buf, 1, 96, buf, buf, 1 << 62, s) == 2
+    assert nv._forward(ctypes.byref(big), buf, 175000, buf, buf, 8, 96, buf, buf, 1 << 62, s) == 2  # T*k*I/2
+    assert nv._forward(ctypes.byref(big), buf, 1 << 27, buf, buf, 8, 96, buf, buf, 1 << 62, s) == 2   # T*k = 2^30
+    huge = nv._Weights(8, 65536, 32768, 4096, 4096, 4096, 4096)                                  # 2I*H*9/16 >= 2^31
+    assert nv._forward(ctypes.byref(huge), buf, 4, buf, buf, 2, 0, buf, buf, 1 << 62, s) == 2
     w = nv._Weights(8, 256, 128, 4096, 4096, 4096, 4096, 2)     # unknown gate/up scale mode
     assert nv._forward(ctypes.byref(w), buf, 4, buf, buf, 2, 0, buf, buf, 1 << 30, s) == 6
