@@ -223,6 +223,7 @@ def main():
         result["decode"]["flushed"] = decode_flushed(nv, weights, W.get_config("decode"), dev)
         result["decode"]["graph"] = decode_graph(nv, weights, W.get_config("decode"), dev, max(args.steps, 50))
         result["quantize"] = quantize_c1(nv, W, dev, args.settle_ms)
+        result["skewed"] = skewed_shard(nv, W, dev, args.settle_ms, max(args.steps, 10))
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(cfg, ids, w, x, wg, wu, wd, T)
     print(json.dumps(result), flush=True)
@@ -230,7 +231,7 @@ def main():
 
 def decode_flushed(nv, weights, dcfg, dev, steps=30):
     """Decode shard with the last-level cache (256 MB) flushed before every step:
-    each step timed alone with events, after a 512 MB write outside the events."""
+    each step timed alone with events, after a 512 MB read outside the events."""
     import torch
     import workloads as W
     ids, w = W.make_router(dcfg)
@@ -241,12 +242,14 @@ def decode_flushed(nv, weights, dcfg, dev, steps=30):
     lay = nv.nvfp4_moe_ws_layout(T, k, dcfg.hidden, dcfg.inter, dcfg.num_local)
     ws = torch.empty(lay["end"], dtype=torch.uint8, device=dev)
     out = torch.empty((T, dcfg.hidden), dtype=torch.bfloat16, device=dev)
-    scratch = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
-    # flush, then the step between two events, all enqueued without host waits,
-    # so the host's launch latency is not inside the events
+    scratch = torch.ones((512 << 20) // 4, dtype=torch.float32, device=dev)
+    sink = torch.empty((), dtype=torch.float32, device=dev)
+    # flush (a 512 MB read, which leaves no dirty lines to write back), then the
+    # step between two events, all enqueued without host waits, so the host's
+    # launch latency is not inside the events
     evs = []
     for i in range(steps + 3):
-        scratch.fill_(i & 0xFF)
+        torch.sum(scratch, dim=0, out=sink)
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record()
         nv.nvfp4_moe_forward(weights, d_x, d_ids, d_w, dcfg.expert_start, out=out, ws=ws)
@@ -310,6 +313,41 @@ def decode_graph(nv, weights, dcfg, dev, steps):
             "layer_weight_GBs": round(bytes_w / (ms * 1e-3) / 1e9, 1),
             "layer_hbm_frac": round(bytes_w / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
             "replay_equals_eager": same}
+
+
+def skewed_shard(nv, W, dev, settle_ms, steps):
+    """Skewed-load shard (16384 tokens, Zipf popularity with empty and hot
+    local experts, W_up 30x): layer throughput and grouped-GEMM FLOP rate."""
+    import torch
+    cfg = W.get_config("skewed")
+    ids, w = W.make_router(cfg)
+    x = W.make_activations(cfg)
+    wg, wu, wd = W.make_weights(cfg)
+    bf = lambda a: torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev)
+    weights = nv.prepare_weights(bf(wg), bf(wu), bf(wd))
+    del wg, wu, wd
+    T, k = ids.shape
+    d_x, d_ids, d_w = bf(x), torch.from_numpy(ids).to(dev), torch.from_numpy(w).to(dev)
+    lay = nv.nvfp4_moe_ws_layout(T, k, cfg.hidden, cfg.inter, cfg.num_local)
+    ws = torch.empty(lay["end"], dtype=torch.uint8, device=dev)
+    out = torch.empty((T, cfg.hidden), dtype=torch.bfloat16, device=dev)
+    step = lambda: nv.nvfp4_moe_forward(weights, d_x, d_ids, d_w, cfg.expert_start, out=out, ws=ws)
+    settle(step, settle_ms)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        step()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    counts = nv.ws_view(ws, lay, "counts", torch.int32, (cfg.num_local,)).cpu().numpy()
+    S = int(counts.sum())
+    H, I = cfg.hidden, cfg.inter
+    return {"workload": f"skewed shard: T={T}, top-{k} of {cfg.num_global}, Zipf(1.2) popularity, local "
+                        f"{cfg.expert_start}..{cfg.expert_start + cfg.num_local - 1}, H={H}, I={I}",
+            "tokens_per_s": round(T / (ms * 1e-3), 1), "ms_per_step": round(ms, 4), "slots": S,
+            "empty_experts": int((counts == 0).sum()), "max_expert_share": round(float(counts.max()) / S, 4),
+            "layer_tflops": round(S * 2.0 * (2 * I * H + H * I) / (ms * 1e-3) / 1e12, 2)}
 
 
 def quantize_c1(nv, W, dev, settle_ms, reps=50):
