@@ -117,16 +117,23 @@ class OracleTrace:
     out: np.ndarray
 
 
-def moe_forward(x_bits, topk_ids, topk_w, expert_start, w: dict, map_fn=map) -> OracleTrace:
-    """Whole layer on one rank's share; w as returned by prepare_weights."""
+def moe_forward(x_bits, topk_ids, topk_w, expert_start, w: dict, map_fn=map, static_gs=None) -> OracleTrace:
+    """Whole layer on one rank's share; w as returned by prepare_weights.
+
+    static_gs: optional (gs_x, gs_h), global scales measured once beforehand
+    (nvfp4_cutedsl.py history, page 2, static-scale commit: warmup measures the
+    L1 input's and the L1 output's gs; inference quantizes with them and no
+    max reduction). By default each activation gets the gs of its own amax.
+    """
     L, I = w["num_local"], w["inter"]
-    x_q, x_sf, gs_x = quantize(x_bits)
+    gs_fix = (None, None) if static_gs is None else (np.float32(static_gs[0]), np.float32(static_gs[1]))
+    x_q, x_sf, gs_x = quantize(x_bits, gs=gs_fix[0])
     r = route(topk_ids, topk_w, expert_start, L)
     S = r["S"]
     g_out = grouped_gemm(x_q, x_sf, r["slot_token"], gs_x, w["w1_q"], w["w1_sf"], w["w1_gs"],
                          r["offsets"], map_fn)
     h = silu_mul(g_out, I)
-    h_q, h_sf, gs_h = quantize(h)
+    h_q, h_sf, gs_h = quantize(h, gs=gs_fix[1])
     y = f32_to_bf16(grouped_gemm(h_q, h_sf, None, gs_h, w["w2_q"], w["w2_sf"], w["w2_gs"],
                                  r["offsets"], map_fn))
     out = scatter(y, r["token_slot"], np.asarray(topk_w, np.float32))

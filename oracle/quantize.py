@@ -12,6 +12,11 @@ Follows, in order:
     by gs); magnitudes snap to the nearest E2M1 value; the sign is kept in
     bit 3 of the nibble.
   * tests history, packing-along-K commit: two nibbles per byte along K.
+  * nvfp4_cutedsl.py history (page 2), static-scale commit: a warmup pass
+    measures gs for each activation once; afterwards the activation is
+    quantized with that fixed gs and no max reduction. With a fixed gs the
+    tensor may exceed 2688 * gs: block scales then saturate at 448 and
+    magnitudes at 6 (the same saturating roundings as above).
 
 Readings where the pages leave a step open (each listed in the design notes):
   * Rounding: the scale and the magnitude are each rounded once from the
@@ -54,11 +59,13 @@ def global_scale(amax) -> np.float32:
     return np.float32(np.float32(amax) / GS_DIVISOR)
 
 
-def quantize(x_bits: np.ndarray, amax=None):
+def quantize(x_bits: np.ndarray, amax=None, gs=None):
     """Quantize one BF16 tensor [M, K] (uint16 bits, K % 16 == 0).
 
     amax: optional externally supplied amax (the h path, whose amax comes from
     the L1 epilogue); by default max |x| over the whole tensor.
+    gs: optional fixed global scale (float32) measured beforehand; it replaces
+    the one derived from amax.
     Returns (q uint8 [M, K/2], sf uint8 [M, K/16], gs float32).
     """
     x_bits = np.asarray(x_bits, dtype=np.uint16)
@@ -67,9 +74,12 @@ def quantize(x_bits: np.ndarray, amax=None):
         raise ValueError("K must be a multiple of 16")
     x = bf16_to_f64(x_bits)
     a = np.abs(x)
-    if amax is None:
-        amax = a.max() if a.size else 0.0
-    gs = global_scale(amax)
+    if gs is not None:
+        gs = np.float32(gs)
+    else:
+        if amax is None:
+            amax = a.max() if a.size else 0.0
+        gs = global_scale(amax)
     blocks = a.reshape(M, K // 16, 16)
     bmax = blocks.max(axis=2) if a.size else np.zeros((M, K // 16))
     if gs == 0:

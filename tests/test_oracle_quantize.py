@@ -50,12 +50,14 @@ def _nearest_code(r: Fraction, grid):
     return best[1]
 
 
-def brute_quantize(x_bits):
+def brute_quantize(x_bits, gs=None):
     x_bits = np.asarray(x_bits, np.uint16)
     M, K = x_bits.shape
     xs = [[Fraction(float(v)) for v in row] for row in O.bf16_to_f64(x_bits)]
-    amax = max((abs(v) for row in xs for v in row), default=Fraction(0))
-    gs = _f32_nearest(amax / 2688)
+    if gs is None:
+        amax = max((abs(v) for row in xs for v in row), default=Fraction(0))
+        gs = _f32_nearest(amax / 2688)
+    gs = np.float32(gs)
     gsf = Fraction(float(gs))
     sf = np.zeros((M, K // 16), np.uint8)
     nib = np.zeros((M, K), np.uint8)
@@ -237,3 +239,39 @@ def test_batched_uses_own_scales():
         qb, sfb, gsb = O.quantize(xb[b])
         assert gs[b] == gsb and np.array_equal(q[b], qb) and np.array_equal(sf[b], sfb)
     assert len(set(gs.tolist())) == 3
+
+
+# ---- fixed (calibrated) global scale: nvfp4_cutedsl.py history, static-scale commit
+
+@pytest.mark.parametrize("seed", range(3))
+def test_static_gs_of_own_amax_equals_dynamic(seed):
+    # the fixed-gs path with gs = RN(amax / 2688) is the dynamic quantizer
+    rng = np.random.default_rng(100 + seed)
+    x = (rng.standard_t(3, (16, 256)) * np.exp2(rng.uniform(-10, 10))).astype(np.float32)
+    xb = _bits(x)
+    q, sf, gs = O.quantize(xb)
+    q2, sf2, gs2 = O.quantize(xb, gs=O.global_scale(np.abs(O.bf16_to_f64(xb)).max()))
+    assert gs2 == gs and np.array_equal(sf2, sf) and np.array_equal(q2, q)
+
+
+@pytest.mark.parametrize("factor", [1 / 64.0, 1 / 3.0, 1.0, 7.5, 2.0 ** 20])
+def test_brute_force_static_gs(factor):
+    # a fixed gs below amax / 2688 saturates scales at 448 and magnitudes at 6;
+    # one above it leaves small (subnormal E4M3) scales
+    rng = np.random.default_rng(21)
+    x = rng.standard_t(3, (3, 64)).astype(np.float32)
+    x[rng.random((3, 64)) < 0.1] = 0
+    xb = _bits(x)
+    gs = np.float32(O.global_scale(np.abs(O.bf16_to_f64(xb)).max()) * np.float32(factor))
+    q, sf, gs_out = O.quantize(xb, gs=gs)
+    bq, bsf, bgs = brute_quantize(xb, gs=gs)
+    assert gs_out == bgs == gs
+    assert np.array_equal(sf, bsf) and np.array_equal(q, bq)
+    if factor < 1:
+        assert (sf == 0x7E).any() and (O.unpack_nibbles(q) & 7 == 7).sum() > 1
+
+
+def test_static_gs_zero_gives_zeros():
+    xb = _bits(np.linspace(-3, 3, 64, dtype=np.float32).reshape(2, 32))
+    q, sf, gs = O.quantize(xb, gs=0.0)
+    assert gs == 0 and not sf.any() and not (O.unpack_nibbles(q) & 7).any()
