@@ -80,6 +80,17 @@ size_t nvfp4_quantize_ws_bytes(int64_t B, int64_t M, int64_t K);
 int nvfp4_quantize(const void* x_bf16, int64_t B, int64_t M, int64_t K, const float* amax_in,
                    uint8_t* q, uint8_t* sf, float* gs_out, void* ws, size_t ws_bytes, void* stream);
 
+/* Quantize with fixed global scales (nvfp4_cutedsl.py history, page 2,
+ * static-scale commit: a warmup pass measures gs once; afterwards activations
+ * are quantized with that gs and no max reduction). As nvfp4_quantize with
+ * gs_b = gs_in[b] (device float [B], finite and >= 0; 0 gives all zeros), no
+ * amax pass and no workspace. Where |x| exceeds 2688 * gs_b the block scale
+ * saturates at 448 and magnitudes at 6. One launch.
+ * Requires 1 <= B <= 65535, M >= 0, K > 0, K % 32 == 0.
+ */
+int nvfp4_quantize_static(const void* x_bf16, int64_t B, int64_t M, int64_t K, const float* gs_in,
+                          uint8_t* q, uint8_t* sf, void* stream);
+
 /* ------------------------------------------------------------------- route
  * Slot routing for one rank's share of experts (nvfp4_mega_moe.py history:
  * local-expert-id commit; src history: one 1-D slot order for both GEMMs;
@@ -171,6 +182,22 @@ int nvfp4_grouped_gemm(const uint8_t* a_q, const uint8_t* a_sf, const int32_t* a
                        int32_t rows_cap, int32_t N, int32_t K, int32_t tile_m, int32_t epilogue,
                        void* d, float* amax_out, void* stream);
 
+/* L1 with h written as NVFP4: the NVFP4_EPI_SILU_MUL (dual_gs = 0) or
+ * NVFP4_EPI_SILU_MUL_DUAL (dual_gs = 1) GEMM, whose BF16 h[s, n] is quantized
+ * in the epilogue with the fixed global scale out_gs[0] (device float [1]) by
+ * exactly the rules of nvfp4_quantize_static: d_q uint8 [rows_cap, N/4],
+ * d_sf uint8 [rows_cap, N/32] (h = [rows_cap, N/2] row-major, 16-column
+ * blocks). This fuses the re-quantization of h into L1 once gs_h is fixed
+ * (nvfp4_cutedsl.py history, static-scale commit); no BF16 h and no amax are
+ * written. Same shapes, tile heights and limits as nvfp4_grouped_gemm with
+ * N % 128 == 0; d_q 16-byte aligned.
+ */
+int nvfp4_grouped_gemm_silu_nvfp4(const uint8_t* a_q, const uint8_t* a_sf, const int32_t* a_row_index,
+                                  const float* a_gs, const uint8_t* b_packed, const float* b_gs, int32_t dual_gs,
+                                  const int32_t* offsets, const int32_t* tile_table, int32_t num_local,
+                                  int32_t rows_cap, int32_t N, int32_t K, int32_t tile_m, const float* out_gs,
+                                  uint8_t* d_q, uint8_t* d_sf, void* stream);
+
 /* ------------------------------------------------------- weighted scatter
  * out[t, :] = RN_bf16( sum over j = 0..k-1 with token_slot[t*k+j] >= 0 of
  *                      topk_w[t, j] * y[token_slot[t*k+j], :] ), float32, increasing j;
@@ -237,6 +264,22 @@ int32_t nvfp4_moe_tile_m(int32_t T, int32_t k, int32_t num_local);
 int nvfp4_moe_forward(const nvfp4_moe_weights* w, const void* x_bf16, int32_t T,
                       const int32_t* topk_ids, const float* topk_w, int32_t k, int32_t expert_start,
                       void* out_bf16, void* ws, size_t ws_bytes, void* stream);
+
+/* The layer with fixed global scales (nvfp4_cutedsl.py history, page 2,
+ * static-scale commit: warmup measures gs for the L1 input and for the L1
+ * output; inference quantizes with them, no max reduction, no host sync).
+ * gs_in: device float [2] = (gs_x, gs_h), e.g. the scalars [0] and [2] that
+ * nvfp4_moe_forward leaves in its workspace for a calibration batch. Steps:
+ * nvfp4_quantize_static of x with gs_x -> route -> L1 whose epilogue writes h
+ * as NVFP4 with gs_h (nvfp4_grouped_gemm_silu_nvfp4) -> L2 (alpha = gs_h *
+ * w2_gs[e]) -> weighted scatter. With the gs values nvfp4_moe_forward measured
+ * for the same inputs, the output equals nvfp4_moe_forward's bit for bit.
+ * Same arguments, workspace and limits as nvfp4_moe_forward; the workspace's
+ * H and SCALARS regions are not used.
+ */
+int nvfp4_moe_forward_static(const nvfp4_moe_weights* w, const void* x_bf16, int32_t T,
+                             const int32_t* topk_ids, const float* topk_w, int32_t k, int32_t expert_start,
+                             const float* gs_in, void* out_bf16, void* ws, size_t ws_bytes, void* stream);
 
 #ifdef __cplusplus
 }

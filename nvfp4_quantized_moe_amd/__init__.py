@@ -18,7 +18,8 @@ __all__ = [
     "lib", "LIB_PATH", "NVFP4Error", "EPI_BF16", "EPI_SILU_MUL", "EPI_SILU_MUL_DUAL", "WS_REGIONS", "nvfp4_quantize",
     "nvfp4_quantize_ws_bytes", "moe_route_slots", "moe_route_ws_bytes", "nvfp4_tile_table_len",
     "nvfp4_grouped_gemm", "moe_weighted_scatter", "nvfp4_fold_scales", "nvfp4_packed_bytes",
-    "nvfp4_pack_weights", "nvfp4_moe_forward",
+    "nvfp4_pack_weights", "nvfp4_moe_forward", "nvfp4_quantize_static", "nvfp4_grouped_gemm_silu_nvfp4",
+    "nvfp4_moe_forward_static", "calibrate_static_gs",
     "nvfp4_moe_ws_bytes", "nvfp4_moe_ws_layout", "nvfp4_moe_tile_m", "MoEWeights", "prepare_weights",
     "ws_view",
 ]
@@ -51,12 +52,15 @@ _status_string = _sig("nvfp4_status_string", ctypes.c_char_p, ctypes.c_int)
 _version = _sig("nvfp4moe_version", ctypes.c_int)
 _quantize_ws = _sig("nvfp4_quantize_ws_bytes", _sz, _i64, _i64, _i64)
 _quantize = _sig("nvfp4_quantize", ctypes.c_int, _vp, _i64, _i64, _i64, _vp, _vp, _vp, _vp, _vp, _sz, _vp)
+_quantize_static = _sig("nvfp4_quantize_static", ctypes.c_int, _vp, _i64, _i64, _i64, _vp, _vp, _vp, _vp)
 _route_ws = _sig("moe_route_ws_bytes", _sz, _i32, _i32, _i32)
 _tile_len = _sig("nvfp4_tile_table_len", _i64, _i64, _i32, _i32)
 _route = _sig("moe_route_slots", ctypes.c_int, _vp, _vp, _i32, _i32, _i32, _i32, _i32,
               _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp)
 _gemm = _sig("nvfp4_grouped_gemm", ctypes.c_int, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
              _i32, _i32, _i32, _i32, _i32, _i32, _vp, _vp, _vp)
+_gemm_nvfp4 = _sig("nvfp4_grouped_gemm_silu_nvfp4", ctypes.c_int, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _vp, _vp,
+                   _i32, _i32, _i32, _i32, _i32, _vp, _vp, _vp, _vp)
 _packed_bytes = _sig("nvfp4_packed_bytes", _i64, _i64, _i64, _i64)
 _pack = _sig("nvfp4_pack_weights", ctypes.c_int, _vp, _vp, _i64, _i64, _i64, _vp, _vp)
 _scatter = _sig("moe_weighted_scatter", ctypes.c_int, _vp, _vp, _vp, _i32, _i32, _i32, _vp, _vp)
@@ -67,6 +71,8 @@ _moe_ws = _sig("nvfp4_moe_ws_bytes", _sz, _i32, _i32, _i32, _i32, _i32)
 _moe_tile_m = _sig("nvfp4_moe_tile_m", _i32, _i32, _i32, _i32)
 _forward = _sig("nvfp4_moe_forward", ctypes.c_int, ctypes.POINTER(_Weights), _vp, _i32, _vp, _vp,
                 _i32, _i32, _vp, _vp, _sz, _vp)
+_forward_static = _sig("nvfp4_moe_forward_static", ctypes.c_int, ctypes.POINTER(_Weights), _vp, _i32, _vp, _vp,
+                       _i32, _i32, _vp, _vp, _vp, _sz, _vp)
 
 
 class NVFP4Error(RuntimeError):
@@ -125,6 +131,22 @@ def nvfp4_quantize(x, amax_in=None, q=None, sf=None, gs=None, ws=None):
     if not batched:
         return q[0], sf[0], gs
     return q, sf, gs
+
+
+def nvfp4_quantize_static(x, gs, q=None, sf=None):
+    """x: BF16 [M, K] or [B, M, K] quantized with the fixed global scales gs
+    (float32 [B], device) -> (q uint8 [..., K/2], sf uint8 [..., K/16])."""
+    _dev(x, torch.bfloat16, "x")
+    _dev(gs, torch.float32, "gs")
+    batched = x.dim() == 3
+    B, M, K = (x.shape if batched else (1, *x.shape))
+    dev = x.device
+    q = torch.empty((B, M, K // 2), dtype=torch.uint8, device=dev) if q is None else q
+    sf = torch.empty((B, M, K // 16), dtype=torch.uint8, device=dev) if sf is None else sf
+    _check(_quantize_static(_ptr(x), B, M, K, _ptr(gs), _ptr(q), _ptr(sf), _stream()), "nvfp4_quantize_static")
+    if not batched:
+        return q[0], sf[0]
+    return q, sf
 
 
 # ------------------------------------------------------------------------- route
@@ -192,6 +214,23 @@ def nvfp4_grouped_gemm(a_q, a_sf, a_row_index, a_gs, b_packed, b_gs, offsets, ti
                  _ptr(offsets), _ptr(tile_table), L, rows_cap, N, K, tile_m, epilogue, _ptr(d), _ptr(amax_out),
                  _stream()), "nvfp4_grouped_gemm")
     return d
+
+
+def nvfp4_grouped_gemm_silu_nvfp4(a_q, a_sf, a_row_index, a_gs, b_packed, b_gs, offsets, tile_table, rows_cap,
+                                  tile_m, out_gs, d_q=None, d_sf=None):
+    """L1 with the SiLU*up epilogue writing h as NVFP4 with the fixed global
+    scale out_gs [1]: returns (h_q uint8 [rows_cap, N/4], h_sf uint8 [rows_cap, N/32]).
+    b_gs [L] (folded W1) or [L, 2] (gate and up global scales)."""
+    L, n32, k128, chunk = b_packed.shape
+    N, K = n32 * 32, k128 * 128
+    dev = b_packed.device
+    d_q = torch.empty((rows_cap, N // 4), dtype=torch.uint8, device=dev) if d_q is None else d_q
+    d_sf = torch.empty((rows_cap, N // 32), dtype=torch.uint8, device=dev) if d_sf is None else d_sf
+    dual = 1 if b_gs.dim() == 2 else 0
+    _check(_gemm_nvfp4(_ptr(a_q), _ptr(a_sf), _ptr(a_row_index), _ptr(a_gs), _ptr(b_packed), _ptr(b_gs), dual,
+                       _ptr(offsets), _ptr(tile_table), L, rows_cap, N, K, tile_m, _ptr(out_gs), _ptr(d_q),
+                       _ptr(d_sf), _stream()), "nvfp4_grouped_gemm_silu_nvfp4")
+    return d_q, d_sf
 
 
 def moe_weighted_scatter(y, token_slot, topk_w, out=None):
@@ -299,3 +338,34 @@ def nvfp4_moe_forward(weights: MoEWeights, x, topk_ids, topk_w, expert_start, ou
     _check(_forward(ctypes.byref(weights._c), _ptr(x), T, _ptr(topk_ids), _ptr(topk_w), k, expert_start,
                     _ptr(out), _ptr(ws), ws.numel(), _stream()), "nvfp4_moe_forward")
     return out
+
+
+def nvfp4_moe_forward_static(weights: MoEWeights, x, topk_ids, topk_w, expert_start, gs, out=None, ws=None):
+    """The layer with fixed global scales gs = float32 [2] (gs_x, gs_h) on the
+    device, e.g. from calibrate_static_gs; no amax passes, h quantized in L1."""
+    _dev(x, torch.bfloat16, "x")
+    _dev(topk_ids, torch.int32, "topk_ids")
+    _dev(topk_w, torch.float32, "topk_w")
+    _dev(gs, torch.float32, "gs")
+    if gs.numel() != 2:
+        raise ValueError(f"gs: expected 2 values (gs_x, gs_h), got {gs.numel()}")
+    T, k = topk_ids.shape
+    H = weights.hidden
+    dev = x.device
+    out = torch.empty((T, H), dtype=torch.bfloat16, device=dev) if out is None else out
+    need = nvfp4_moe_ws_bytes(T, k, H, weights.inter, weights.num_local)
+    ws = _alloc_ws(need, dev) if ws is None else ws
+    _check(_forward_static(ctypes.byref(weights._c), _ptr(x), T, _ptr(topk_ids), _ptr(topk_w), k, expert_start,
+                           _ptr(gs), _ptr(out), _ptr(ws), ws.numel(), _stream()), "nvfp4_moe_forward_static")
+    return out
+
+
+def calibrate_static_gs(weights: MoEWeights, x, topk_ids, topk_w, expert_start):
+    """Global scales (gs_x, gs_h) that nvfp4_moe_forward measures on a
+    calibration batch, as a device float32 [2] for nvfp4_moe_forward_static."""
+    T, k = topk_ids.shape
+    ws = _alloc_ws(nvfp4_moe_ws_bytes(T, k, weights.hidden, weights.inter, weights.num_local), x.device)
+    nvfp4_moe_forward(weights, x, topk_ids, topk_w, expert_start, ws=ws)
+    lay = nvfp4_moe_ws_layout(T, k, weights.hidden, weights.inter, weights.num_local)
+    sc = ws_view(ws, lay, "scalars", torch.float32, (4,))
+    return torch.stack([sc[0], sc[2]]).contiguous()

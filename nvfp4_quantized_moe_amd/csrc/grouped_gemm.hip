@@ -33,6 +33,7 @@
 // so each MFMA step still sums matching K indices.
 #include "common.h"
 #include "internal.h"
+#include "quant_block.h"
 
 namespace nvfp4 {
 
@@ -44,6 +45,10 @@ constexpr int kAPitch = 272;    // LDS bytes per fp16 A row of a stage (256 + 16
 // stage's 64 bytes and scale bytes [4*(l/32), +4) of the stage's 8.
 constexpr int kPackChunk = 2304;
 constexpr int kPackScaleOff = 2048;
+
+// Internal epilogue: the SiLU*up epilogue writing h as NVFP4 with a fixed
+// global scale (h_q, h_sf) instead of BF16 h and its amax.
+constexpr int kEpiSiluNvfp4 = 3;
 
 template <int SUB_M, int SUB_N, int WAVES, int P>
 struct GemmCfg {
@@ -59,6 +64,7 @@ struct GemmCfg {
 // zero, so rows past a group's end and column tiles past N need no branches.
 constexpr uint32_t kRsrcWord3 = 0x00020000u;
 constexpr uint32_t kOutOfRange = 0x80000000u;  // offset that is never in range
+constexpr int kWaitVmcnt0 = 0x0F70;  // s_waitcnt vmcnt(0) expcnt(7) lgkmcnt(15) (gfx9 encoding)
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t num_records) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)num_records, (int)kRsrcWord3);
@@ -126,8 +132,11 @@ template <int SUB_M, int SUB_N, int WAVES, int P, int EPI>
 __global__ __launch_bounds__(64 * WAVES) void grouped_gemm_kernel(
     const uint8_t* __restrict__ a_q, const uint8_t* __restrict__ a_sf, const int32_t* __restrict__ a_row_index,
     const float* __restrict__ a_gs, const uint8_t* __restrict__ b_packed, const float* __restrict__ b_gs,
-    const int32_t* __restrict__ offsets, const int32_t* __restrict__ tile_table, int max_tiles, int N, int K,
-    int n_out, int n_ntiles, int col_fastest, int dual_gs, uint16_t* __restrict__ d, float* __restrict__ amax_out) {
+    const int32_t* __restrict__ offsets, const int32_t* __restrict__ tile_table, int max_tiles, int rows_cap, int N,
+    int K,
+    int n_out, int n_ntiles, int col_fastest, int dual_gs, uint16_t* __restrict__ d, float* __restrict__ amax_out,
+    uint8_t* __restrict__ d_sf, const float* __restrict__ out_gs) {
+  constexpr bool kSilu = EPI != NVFP4_EPI_BF16;  // gate/up pairs, n_out = N / 2
   using C = GemmCfg<SUB_M, SUB_N, WAVES, P>;
   extern __shared__ __align__(16) uint8_t lds[];
   const int tid = threadIdx.x;
@@ -148,103 +157,192 @@ __global__ __launch_bounds__(64 * WAVES) void grouped_gemm_kernel(
   const __amdgpu_buffer_rsrc_t ra_q = make_rsrc(a_q, 0x7FFFFFFFu);
   const __amdgpu_buffer_rsrc_t ra_s = make_rsrc(a_sf, 0x7FFFFFFFu);
   const int half_n = N / 2;
+  const int S = (nstages + P - 1) / P * P;  // loop stages per item (see below)
   float amax_local = 0.0f;
 
-  for (int item = slot; item < items; item += G) {
-    // row-tile order: the row tiles of one column tile are adjacent, so the
-    // row tiles of one expert share its weight tile in L2 at the same time;
-    // column order: adjacent items walk one expert's weights contiguously
-    const int mt = col_fastest ? item / n_ntiles : item % ntiles;
-    const int nt = col_fastest ? item % n_ntiles : item / ntiles;
+  // Sources of one work item's stage loads: its expert's weight resource, this
+  // thread's activation row offsets and the byte offsets of the wave's weight
+  // subtiles at stage 0. A slot past the last item gets sources that read zeros.
+  struct Src {
+    __amdgpu_buffer_rsrc_t rbw;
+    uint32_t a_off[C::A_PER_T], as_off[C::A_PER_T];
+    int row0[SUB_N];
+  };
+  // row-tile order: the row tiles of one column tile are adjacent, so the
+  // row tiles of one expert share its weight tile in L2 at the same time;
+  // column order: adjacent items walk one expert's weights contiguously
+  auto tile_of = [&](int item, int& mt, int& nt) {
+    mt = col_fastest ? item / n_ntiles : item % ntiles;
+    nt = col_fastest ? item % n_ntiles : item / ntiles;
+  };
+  auto make_src = [&](int item, Src& src) {
+    src.rbw = make_rsrc(b_packed, 0u);
+#pragma unroll
+    for (int i = 0; i < C::A_PER_T; ++i) {
+      src.a_off[i] = kOutOfRange;
+      src.as_off[i] = kOutOfRange;
+    }
+#pragma unroll
+    for (int j = 0; j < SUB_N; ++j) src.row0[j] = -1;
+    if (item >= items) return;
+    int mt, nt;
+    tile_of(item, mt, nt);
     const int e = tile_table[1 + 2 * mt];
     const int r0 = tile_table[2 + 2 * mt];
     const int r_end = min(r0 + C::BM, offsets[e + 1]);
-    // one global scale per expert, or (gate, up) pairs for an unfolded L1 weight
-    const float alpha = a_gs[0] * b_gs[dual_gs ? 2 * e : e];
-    const float alpha_up = dual_gs ? a_gs[0] * b_gs[2 * e + 1] : alpha;
-    const __amdgpu_buffer_rsrc_t rbw = make_rsrc(b_packed + (size_t)e * b_bytes, b_bytes);
-
-    // activation staging tasks of this thread: 16 FP4 bytes + 2 scale bytes per
-    // stage at byte offsets a_off / as_off (out of range for rows past the group)
-    uint32_t a_off[C::A_PER_T], as_off[C::A_PER_T];
+    src.rbw = make_rsrc(b_packed + (size_t)e * b_bytes, b_bytes);
+    // activation staging task i of this thread: 16 FP4 bytes + 2 scale bytes of
+    // row rw + lane/4 per stage. The 64 lanes of a wave cover the 16 rows from
+    // rw on; their gather indices are read with scalar loads (clamped to the
+    // group), so the wait for them does not also wait for the stage loads in
+    // flight, which retire in order on the vector memory counter.
 #pragma unroll
     for (int i = 0; i < C::A_PER_T; ++i) {
-      const int task = tid + i * C::THREADS, row = task >> 2, c = task & 3;
-      a_off[i] = kOutOfRange;
-      as_off[i] = kOutOfRange;
-      if (task < C::A_TASKS && r0 + row < r_end) {
-        const uint32_t ar = (uint32_t)(a_row_index ? a_row_index[r0 + row] : r0 + row);
-        a_off[i] = ar * (uint32_t)pitch + 16u * c;
-        as_off[i] = ar * (uint32_t)spitch + 2u * c;
+      const int rw = (i * C::THREADS + 64 * wave) >> 2;  // wave-uniform
+      if (rw >= C::BM) continue;
+      const int row = rw + (lane >> 2);
+      uint32_t ar = (uint32_t)(r0 + row);
+      if (a_row_index && r0 + row < r_end) ar = (uint32_t)a_row_index[r0 + row];
+      if (row < C::BM && r0 + row < r_end) {
+        src.a_off[i] = ar * (uint32_t)pitch + 16u * (lane & 3);
+        src.as_off[i] = ar * (uint32_t)spitch + 2u * (lane & 3);
       }
     }
-    // weight rows: subtile j of this wave covers 32 consecutive rows starting at the
-    // wave-uniform row0[j] (-1 when past the end); lane lr takes row0[j] + lr and
-    // lane half lg holds bytes [32 lg, 32 lg + 32) of each 64-byte stage
-    int row0[SUB_N];
+    // weight rows: subtile j of this wave covers 32 consecutive rows starting at
+    // the wave-uniform row0 (none past the end); lane lr takes row0 + lr and lane
+    // half lg holds bytes [32 lg, 32 lg + 32) of each 64-byte stage
 #pragma unroll
     for (int j = 0; j < SUB_N; ++j) {
       const int ch = wave * SUB_N + j;
-      if (EPI == NVFP4_EPI_SILU_MUL) {
+      int row0;
+      if (kSilu) {
         const int col0 = nt * (C::BN / 2) + (ch >> 1) * 32;
-        row0[j] = col0 < half_n ? ((ch & 1) ? half_n + col0 : col0) : -1;
+        row0 = col0 < half_n ? ((ch & 1) ? half_n + col0 : col0) : -1;
       } else {
         const int col0 = nt * C::BN + ch * 32;
-        row0[j] = col0 < N ? col0 : -1;
+        row0 = col0 < N ? col0 : -1;
       }
+      src.row0[j] = row0;
     }
-    const uint32_t b_lane = 16u * (uint32_t)lane;
-    const uint32_t bs_lane = kPackScaleOff + 4u * (uint32_t)lane;
+  };
+  const uint32_t b_lane = 16u * (uint32_t)lane;
+  const uint32_t bs_lane = kPackScaleOff + 4u * (uint32_t)lane;
 
-    // Register rings of P stages for both operands. Global loads complete in
-    // issue order, so stage s's activation and weight loads are issued
-    // together, P - 1 stages ahead; waiting for one stage never waits for a
-    // later stage's loads.
-    uint4 ra[P][C::A_PER_T];
-    uint32_t rsa[P][C::A_PER_T];
-    uint4 rb[P][SUB_N][2];
-    uint32_t rsb[P][SUB_N];
-    // stages past the end read zeros (out-of-range offsets), so the loop body
-    // needs no branches around its loads
-    auto load_a = [&](int s, int slot_) {
-      const bool in = s < nstages;
-      const uint32_t so = in ? (uint32_t)(s * 64) : kOutOfRange, sso = in ? (uint32_t)(s * 8) : kOutOfRange;
+  // Register rings of P stages for both operands. Global loads complete in
+  // issue order, so stage s's activation and weight loads are issued
+  // together, P - 1 stages ahead; waiting for one stage never waits for a
+  // later stage's loads.
+  uint4 ra[P][C::A_PER_T];
+  uint32_t rsa[P][C::A_PER_T];
+  uint4 rb[P][SUB_N][2];
+  uint32_t rsb[P][SUB_N];
+  // stages past the end read zeros (out-of-range offsets), so the loop body
+  // needs no branches around its loads
+  auto store_a = [&](int buf, int slot_) {
+    uint8_t* base = lds + buf * (C::BM * kAPitch);
 #pragma unroll
-      for (int i = 0; i < C::A_PER_T; ++i) {
-        ra[slot_][i] = buf_load16(ra_q, a_off[i], so);
-        rsa[slot_][i] = buf_load2(ra_s, as_off[i], sso);
-      }
-    };
-    auto store_a = [&](int buf, int slot_) {
-      uint8_t* base = lds + buf * (C::BM * kAPitch);
+    for (int i = 0; i < C::A_PER_T; ++i) {
+      const int task = tid + i * C::THREADS;
+      if (task < C::A_TASKS) {
+        uint8_t* dst = base + (task >> 2) * kAPitch + (task & 3) * 64;
+        const Scales4 sa = scales4(rsa[slot_][i]);
 #pragma unroll
-      for (int i = 0; i < C::A_PER_T; ++i) {
-        const int task = tid + i * C::THREADS;
-        if (task < C::A_TASKS) {
-          uint8_t* dst = base + (task >> 2) * kAPitch + (task & 3) * 64;
-          const Scales4 sa = scales4(rsa[slot_][i]);
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            half8_t v = decode8(pick_u32(ra[slot_][i], q), scale_pair(sa, q >> 1));
-            *reinterpret_cast<half8_t*>(dst + 16 * q) = v;
-          }
+        for (int q = 0; q < 4; ++q) {
+          half8_t v = decode8(pick_u32(ra[slot_][i], q), scale_pair(sa, q >> 1));
+          *reinterpret_cast<half8_t*>(dst + 16 * q) = v;
         }
       }
-    };
-    auto load_b = [&](int s, int slot_) {
-      const bool in = s < nstages;
+    }
+  };
+  // Loads of loop stage t into ring slot slot_: stage t of the current item
+  // for t < nstages, stage t - S of the next item for t >= S, zeros between
+  // (padding stages). The choice is wave-uniform and made with selects.
+  auto load_stage = [&](const Src& cur, const Src& nxt, int t, int slot_) {
+    const bool in_cur = t < nstages, in_nxt = t >= S;
+    const int st = in_cur ? t : t - S;
+    const bool in = in_cur || (in_nxt && st < nstages);
+    const uint32_t so = in ? (uint32_t)(st * 64) : kOutOfRange, sso = in ? (uint32_t)(st * 8) : kOutOfRange;
 #pragma unroll
-      for (int j = 0; j < SUB_N; ++j) {
-        const bool ok = in && row0[j] >= 0;
-        const uint32_t chunk = ok ? ((uint32_t)(row0[j] >> 5) * (uint32_t)nstages + (uint32_t)s) * kPackChunk
-                                  : kOutOfRange;  // wave-uniform: a scalar offset
-        rb[slot_][j][0] = buf_load16(rbw, b_lane, chunk);
-        rb[slot_][j][1] = buf_load16(rbw, b_lane + 1024u, chunk);
-        rsb[slot_][j] = buf_load4(rbw, bs_lane, chunk);
+    for (int i = 0; i < C::A_PER_T; ++i) {
+      ra[slot_][i] = buf_load16(ra_q, in_cur ? cur.a_off[i] : nxt.a_off[i], so);
+      rsa[slot_][i] = buf_load2(ra_s, in_cur ? cur.as_off[i] : nxt.as_off[i], sso);
+    }
+    const __amdgpu_buffer_rsrc_t rbw = in_cur ? cur.rbw : nxt.rbw;
+#pragma unroll
+    for (int j = 0; j < SUB_N; ++j) {
+      // wave-uniform: a scalar offset. A subtile past N has an out-of-range base
+      // (>= 2^31), which stays out of range after adding st * kPackChunk (< 2^31).
+      const int row0 = in_cur ? cur.row0[j] : nxt.row0[j];
+      const uint32_t chunk = in && row0 >= 0 ? ((uint32_t)(row0 >> 5) * (uint32_t)nstages + (uint32_t)st) * kPackChunk
+                                             : kOutOfRange;
+      rb[slot_][j][0] = buf_load16(rbw, b_lane, chunk);
+      rb[slot_][j][1] = buf_load16(rbw, b_lane + 1024u, chunk);
+      rsb[slot_][j] = buf_load4(rbw, bs_lane, chunk);
+    }
+  };
+  float16_t acc[SUB_M][SUB_N];
+  // MFMAs of one stage from ring slot u and LDS buffer buf
+  auto mma_stage = [&](int buf, int u) {
+    const uint8_t* abuf = lds + buf * (C::BM * kAPitch) + lr * kAPitch + 128 * lg;
+    // software pipeline over the 8 MFMA steps of the stage: the operands of
+    // step t + 1 are read and decoded while the MFMAs of step t execute
+    half8_t av[2][SUB_M], bv[2][SUB_N];
+    Scales4 sb[SUB_N];
+#pragma unroll
+    for (int j = 0; j < SUB_N; ++j) sb[j] = scales4(rsb[u][j]);
+#pragma unroll
+    for (int i = 0; i < SUB_M; ++i) av[0][i] = *reinterpret_cast<const half8_t*>(abuf + 32 * i * kAPitch);
+#pragma unroll
+    for (int j = 0; j < SUB_N; ++j) bv[0][j] = decode8(rb[u][j][0].x, scale_pair(sb[j], 0));
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+      const int cur = t & 1, nxt = cur ^ 1;
+      if (t + 1 < 8) {
+#pragma unroll
+        for (int i = 0; i < SUB_M; ++i)
+          av[nxt][i] = *reinterpret_cast<const half8_t*>(abuf + 32 * i * kAPitch + 16 * (t + 1));
+#pragma unroll
+        for (int j = 0; j < SUB_N; ++j)
+          bv[nxt][j] = decode8(pick_u32(rb[u][j][(t + 1) >> 2], (t + 1) & 3), scale_pair(sb[j], (t + 1) >> 1));
       }
-    };
+#pragma unroll
+      for (int i = 0; i < SUB_M; ++i)
+#pragma unroll
+        for (int j = 0; j < SUB_N; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(av[cur][i], bv[cur][j], acc[i][j], 0, 0, 0);
+      // issue order: the next step's LDS reads first, then one MFMA followed by
+      // a share of the next step's VALU decode, repeated
+      __builtin_amdgcn_sched_group_barrier(0x100, SUB_M, 0);
+#pragma unroll
+      for (int m = 0; m < SUB_M * SUB_N; ++m) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, (10 * SUB_N + SUB_M * SUB_N - 1) / (SUB_M * SUB_N), 0);
+      }
+    }
+  };
 
-    float16_t acc[SUB_M][SUB_N];
+  // Each item runs S stages (K's stage count rounded up to a multiple of P; the
+  // extra stages multiply zeros). The loads run P - 1 stages ahead across item
+  // boundaries: the last block of an item loads the first P - 1 stages of the
+  // workgroup's next item and decodes its stage 0 into LDS, so the next item
+  // starts without waiting for memory. Stage s of an item uses LDS buffer
+  // (s + par) & 1, where par flips with every item when S is odd.
+  int par = 0;
+  Src cur;
+  make_src(slot, cur);
+#pragma unroll
+  for (int p = 0; p < P - 1; ++p) load_stage(cur, cur, p, p);
+  store_a(0, 0);
+  // NVFP4 output: the threshold table of the fixed global scale of h
+  uint16_t* h_tile = reinterpret_cast<uint16_t*>(lds + C::LDS);  // [BM][BN/2] BF16 h of one item
+  const uint4* h_lut = reinterpret_cast<const uint4*>(lds + C::LDS + C::BM * C::BN);
+  if (EPI == kEpiSiluNvfp4) build_threshold_lut(out_gs[0], reinterpret_cast<uint16_t*>(lds + C::LDS + C::BM * C::BN),
+                                                tid, C::THREADS);
+  __syncthreads();
+
+  for (int item = slot; item < items; item += G) {
+    Src nxt;
+    make_src(item + G, nxt);
 #pragma unroll
     for (int i = 0; i < SUB_M; ++i)
 #pragma unroll
@@ -252,63 +350,25 @@ __global__ __launch_bounds__(64 * WAVES) void grouped_gemm_kernel(
 #pragma unroll
         for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
 
-    __syncthreads();  // the previous item's waves are done with the LDS buffers
-#pragma unroll
-    for (int p = 0; p < P - 1; ++p) {
-      load_a(p, p);
-      load_b(p, p);
-    }
-    store_a(0, 0);
-    __syncthreads();
-
-    // the stage count is rounded up to a multiple of P; the extra stages multiply zeros
-    for (int s0 = 0; s0 < nstages; s0 += P) {
+    for (int s0 = 0; s0 < S; s0 += P) {
 #pragma unroll
       for (int u = 0; u < P; ++u) {
         const int s = s0 + u;
-        load_a(s + P - 1, (u + P - 1) % P);
-        load_b(s + P - 1, (u + P - 1) % P);
-        const uint8_t* abuf = lds + (s & 1) * (C::BM * kAPitch) + lr * kAPitch + 128 * lg;
-        // software pipeline over the 8 MFMA steps of the stage: the operands of
-        // step t + 1 are read and decoded while the MFMAs of step t execute
-        half8_t av[2][SUB_M], bv[2][SUB_N];
-        Scales4 sb[SUB_N];
-#pragma unroll
-        for (int j = 0; j < SUB_N; ++j) sb[j] = scales4(rsb[u][j]);
-#pragma unroll
-        for (int i = 0; i < SUB_M; ++i) av[0][i] = *reinterpret_cast<const half8_t*>(abuf + 32 * i * kAPitch);
-#pragma unroll
-        for (int j = 0; j < SUB_N; ++j) bv[0][j] = decode8(rb[u][j][0].x, scale_pair(sb[j], 0));
-#pragma unroll
-        for (int t = 0; t < 8; ++t) {
-          const int cur = t & 1, nxt = cur ^ 1;
-          if (t + 1 < 8) {
-#pragma unroll
-            for (int i = 0; i < SUB_M; ++i)
-              av[nxt][i] = *reinterpret_cast<const half8_t*>(abuf + 32 * i * kAPitch + 16 * (t + 1));
-#pragma unroll
-            for (int j = 0; j < SUB_N; ++j)
-              bv[nxt][j] = decode8(pick_u32(rb[u][j][(t + 1) >> 2], (t + 1) & 3), scale_pair(sb[j], (t + 1) >> 1));
-          }
-#pragma unroll
-          for (int i = 0; i < SUB_M; ++i)
-#pragma unroll
-            for (int j = 0; j < SUB_N; ++j)
-              acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(av[cur][i], bv[cur][j], acc[i][j], 0, 0, 0);
-          // issue order: the next step's LDS reads first, then one MFMA followed by
-          // a share of the next step's VALU decode, repeated
-          __builtin_amdgcn_sched_group_barrier(0x100, SUB_M, 0);
-#pragma unroll
-          for (int m = 0; m < SUB_M * SUB_N; ++m) {
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-            __builtin_amdgcn_sched_group_barrier(0x002, (10 * SUB_N + SUB_M * SUB_N - 1) / (SUB_M * SUB_N), 0);
-          }
-        }
-        store_a((s + 1) & 1, (u + 1) % P);
+        load_stage(cur, nxt, s + P - 1, (u + P - 1) % P);
+        mma_stage((s + par) & 1, u);
+        store_a((s + 1 + par) & 1, (u + 1) % P);
         __syncthreads();
       }
     }
 
+    // one global scale per expert, or (gate, up) pairs for an unfolded L1 weight
+    int mt, nt;
+    tile_of(item, mt, nt);
+    const int e = tile_table[1 + 2 * mt];
+    const int r0 = tile_table[2 + 2 * mt];
+    const int r_end = min(r0 + C::BM, offsets[e + 1]);
+    const float alpha = a_gs[0] * b_gs[dual_gs ? 2 * e : e];
+    const float alpha_up = dual_gs ? a_gs[0] * b_gs[2 * e + 1] : alpha;
     // epilogue: lane holds column lr and rows 8*(v/4) + 4*lg + (v%4) of each 32x32 tile
 #pragma unroll
     for (int i = 0; i < SUB_M; ++i) {
@@ -316,17 +376,21 @@ __global__ __launch_bounds__(64 * WAVES) void grouped_gemm_kernel(
       for (int v = 0; v < 16; ++v) {
         const int row = r0 + i * 32 + 8 * (v >> 2) + 4 * lg + (v & 3);
         if (row >= r_end) continue;
-        if (EPI == NVFP4_EPI_SILU_MUL) {
+        if (kSilu) {
 #pragma unroll
           for (int j = 0; j < SUB_N; j += 2) {
             const int ch = wave * SUB_N + j;  // even chunk: gate, next chunk: up
-            const int col = nt * (C::BN / 2) + (ch >> 1) * 32 + lr;
+            const int lc = (ch >> 1) * 32 + lr, col = nt * (C::BN / 2) + lc;
             if (col >= n_out) continue;
             const float g = bf16_to_f32(f32_to_bf16(acc[i][j][v] * alpha));
             const float u = bf16_to_f32(f32_to_bf16(acc[i][j + 1][v] * alpha_up));
             const uint32_t h = f32_to_bf16(silu_f32(g) * u);
-            d[(size_t)row * n_out + col] = (uint16_t)h;
-            amax_local = fmaxf(amax_local, fabsf(bf16_to_f32(h)));
+            if (EPI == kEpiSiluNvfp4) {
+              h_tile[(row - r0) * (C::BN / 2) + lc] = (uint16_t)h;
+            } else {
+              d[(size_t)row * n_out + col] = (uint16_t)h;
+              amax_local = fmaxf(amax_local, fabsf(bf16_to_f32(h)));
+            }
           }
         } else {
 #pragma unroll
@@ -338,6 +402,28 @@ __global__ __launch_bounds__(64 * WAVES) void grouped_gemm_kernel(
         }
       }
     }
+    if (EPI == kEpiSiluNvfp4) {
+      // h of the item is in LDS: each thread quantizes whole 16-column blocks
+      // (exact roundings, the quantizer's own code) and writes them as NVFP4
+      __syncthreads();
+      const float gs_o = out_gs[0];
+      const double six_gs_o = 6.0 * (double)gs_o;
+      uint8_t* d_q = reinterpret_cast<uint8_t*>(d);
+      for (int blk = tid; blk < C::BM * (C::BN / 32); blk += C::THREADS) {
+        const int lrow = blk / (C::BN / 32), lb = blk % (C::BN / 32);
+        const int row = r0 + lrow, col0 = nt * (C::BN / 2) + 16 * lb;
+        if (row >= r_end || col0 >= n_out) continue;
+        const uint4* src = reinterpret_cast<const uint4*>(h_tile + lrow * (C::BN / 2) + 16 * lb);
+        const uint4 v0 = src[0], v1 = src[1];
+        const uint32_t w[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
+        uint2 packed;
+        const uint32_t code = quantize_block16(w, gs_o, six_gs_o, h_lut, &packed);
+        *reinterpret_cast<uint2*>(d_q + (size_t)row * (n_out / 2) + col0 / 2) = packed;
+        d_sf[(size_t)row * (n_out / 16) + col0 / 16] = (uint8_t)code;
+      }
+    }
+    cur = nxt;
+    par = (par + S) & 1;
   }
   if (EPI == NVFP4_EPI_SILU_MUL) {
     const float m = wave_max(amax_local);
@@ -349,11 +435,14 @@ template <int SUB_M, int SUB_N, int WAVES, int P, int EPI>
 static int launch_cfg(const uint8_t* a_q, const uint8_t* a_sf, const int32_t* a_row_index, const float* a_gs,
                       const uint8_t* b_packed, const float* b_gs, const int32_t* offsets,
                       const int32_t* tile_table, int32_t num_local, int32_t rows_cap, int32_t N, int32_t K,
-                      void* d, float* amax_out, hipStream_t stream, int dual_gs = 0, int col_fastest = 0) {
+                      void* d, float* amax_out, hipStream_t stream, int dual_gs = 0, int col_fastest = 0,
+                      uint8_t* d_sf = nullptr, const float* out_gs = nullptr) {
   using C = GemmCfg<SUB_M, SUB_N, WAVES, P>;
-  static_assert(EPI != NVFP4_EPI_SILU_MUL || SUB_N % 2 == 0, "gate/up pairs live in one wave");
-  const int n_out = EPI == NVFP4_EPI_SILU_MUL ? N / 2 : N;
-  const int bn_out = EPI == NVFP4_EPI_SILU_MUL ? C::BN / 2 : C::BN;
+  static_assert(EPI == NVFP4_EPI_BF16 || SUB_N % 2 == 0, "gate/up pairs live in one wave");
+  const int n_out = EPI != NVFP4_EPI_BF16 ? N / 2 : N;
+  const int bn_out = EPI != NVFP4_EPI_BF16 ? C::BN / 2 : C::BN;
+  // NVFP4 output adds the BF16 h tile of one item and the threshold table
+  constexpr int lds_bytes = C::LDS + (EPI == kEpiSiluNvfp4 ? C::BM * C::BN + 128 * 16 : 0);
   const int n_ntiles = (n_out + bn_out - 1) / bn_out;
   const int max_tiles = rows_cap / C::BM + num_local;
   const int64_t max_items = (int64_t)max_tiles * n_ntiles;
@@ -365,13 +454,13 @@ static int launch_cfg(const uint8_t* a_q, const uint8_t* a_sf, const int32_t* a_
     if (hipGetDevice(&dev) != hipSuccess ||
         hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n_cu < 1)
       return NVFP4_ERR_HIP;
-    if (C::LDS > 64 * 1024 &&
+    if (lds_bytes > 64 * 1024 &&
         hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
-                            C::LDS) != hipSuccess)
+                            lds_bytes) != hipSuccess)
       return NVFP4_ERR_HIP;
     int nb = 0;
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, reinterpret_cast<const void*>(kern), C::THREADS,
-                                                     C::LDS) != hipSuccess || nb < 1)
+                                                     lds_bytes) != hipSuccess || nb < 1)
       nb = 1;
     per_cu = nb;
   }
@@ -379,9 +468,9 @@ static int launch_cfg(const uint8_t* a_q, const uint8_t* a_sf, const int32_t* a_
   if (grid > max_items) grid = max_items;
   if (grid >= kXcds) grid -= grid % kXcds;
   if (grid < 1) grid = 1;
-  hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(C::THREADS), C::LDS, stream, a_q, a_sf, a_row_index, a_gs,
-                     b_packed, b_gs, offsets, tile_table, max_tiles, N, K, n_out, n_ntiles, col_fastest, dual_gs,
-                     reinterpret_cast<uint16_t*>(d), amax_out);
+  hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(C::THREADS), lds_bytes, stream, a_q, a_sf, a_row_index, a_gs,
+                     b_packed, b_gs, offsets, tile_table, max_tiles, rows_cap, N, K, n_out, n_ntiles, col_fastest, dual_gs,
+                     reinterpret_cast<uint16_t*>(d), amax_out, d_sf, out_gs);
   NVFP4_CHECK_LAUNCH();
   return NVFP4_OK;
 }
@@ -413,6 +502,46 @@ int nvfp4_launch_grouped_gemm(const uint8_t* a_q, const uint8_t* a_sf, const int
   }
 #undef NVFP4_GEMM_CFG
 #undef NVFP4_GEMM_ARGS
+}
+
+// The L1 GEMM whose SiLU*up epilogue writes h as NVFP4 with the fixed global
+// scale out_gs[0] (d_q [rows_cap, N/4], d_sf [rows_cap, N/32]); same tile
+// configurations as nvfp4_launch_grouped_gemm.
+int nvfp4_launch_grouped_gemm_nvfp4(const uint8_t* a_q, const uint8_t* a_sf, const int32_t* a_row_index,
+                                    const float* a_gs, const uint8_t* b_packed, const float* b_gs, int32_t dual_gs,
+                                    const int32_t* offsets, const int32_t* tile_table, int32_t num_local,
+                                    int32_t rows_cap, int32_t N, int32_t K, int32_t tile_m, const float* out_gs,
+                                    uint8_t* d_q, uint8_t* d_sf, hipStream_t stream) {
+#define NVFP4_GEMM_CFG(SM, SN, W, PF)                                                                             \
+  return launch_cfg<SM, SN, W, PF, kEpiSiluNvfp4>(a_q, a_sf, a_row_index, a_gs, b_packed, b_gs, offsets,        \
+                                                 tile_table, num_local, rows_cap, N, K, d_q, nullptr, stream,  \
+                                                 dual_gs, 0, d_sf, out_gs)
+  switch (tile_m) {
+    case 32: NVFP4_GEMM_CFG(1, 2, 4, 3);
+    case 64: NVFP4_GEMM_CFG(2, 2, 8, 4);
+    case 128: NVFP4_GEMM_CFG(4, 2, 4, 3);
+    default: return NVFP4_ERR_SHAPE;
+  }
+#undef NVFP4_GEMM_CFG
+}
+
+extern "C" int nvfp4_grouped_gemm_silu_nvfp4(const uint8_t* a_q, const uint8_t* a_sf, const int32_t* a_row_index,
+                                             const float* a_gs, const uint8_t* b_packed, const float* b_gs,
+                                             int32_t dual_gs, const int32_t* offsets, const int32_t* tile_table,
+                                             int32_t num_local, int32_t rows_cap, int32_t N, int32_t K,
+                                             int32_t tile_m, const float* out_gs, uint8_t* d_q, uint8_t* d_sf,
+                                             void* stream) {
+  if (dual_gs != 0 && dual_gs != 1) return NVFP4_ERR_ARG;
+  if (num_local < 1 || rows_cap < 0 || N <= 0 || K <= 0 || K % kBK != 0 || N % 128 != 0) return NVFP4_ERR_SHAPE;
+  if (tile_m != 32 && tile_m != 64 && tile_m != 128) return NVFP4_ERR_SHAPE;
+  if (!a_q || !a_sf || !a_gs || !b_packed || !b_gs || !offsets || !tile_table || !out_gs || !d_q || !d_sf)
+    return NVFP4_ERR_NULL;
+  if (!nvfp4_aligned16(a_q) || !nvfp4_aligned16(a_sf) || !nvfp4_aligned16(b_packed) || !nvfp4_aligned16(d_q))
+    return NVFP4_ERR_ALIGN;
+  if ((int64_t)rows_cap * (K / 2) >= (1ll << 31) || (int64_t)N * K / 32 * 18 >= (1ll << 31)) return NVFP4_ERR_SHAPE;
+  if (rows_cap == 0) return NVFP4_OK;
+  return nvfp4_launch_grouped_gemm_nvfp4(a_q, a_sf, a_row_index, a_gs, b_packed, b_gs, dual_gs, offsets, tile_table,
+                                         num_local, rows_cap, N, K, tile_m, out_gs, d_q, d_sf, (hipStream_t)stream);
 }
 
 extern "C" int nvfp4_grouped_gemm(const uint8_t* a_q, const uint8_t* a_sf, const int32_t* a_row_index,

@@ -13,6 +13,10 @@ int nvfp4_launch_quantize(const void* x_bf16, int64_t B, int64_t M, int64_t K, c
                           const int32_t* rows_dev, uint8_t* q, uint8_t* sf, float* gs_out, void* ws,
                           uint32_t* clear, int n_clear, hipStream_t stream);
 
+// Quantize with fixed global scales gs_in[b] (device): one launch, no amax pass.
+int nvfp4_launch_quantize_static(const void* x_bf16, int64_t B, int64_t M, int64_t K, const float* gs_in,
+                                 const int32_t* rows_dev, uint8_t* q, uint8_t* sf, hipStream_t stream);
+
 // Route workspace: per-chunk counts and bases, int32 [nchunks][num_local] each.
 constexpr int kRouteChunk = 1024;
 size_t nvfp4_route_ws(int32_t T, int32_t k, int32_t num_local);
@@ -26,6 +30,13 @@ int nvfp4_launch_grouped_gemm(const uint8_t* a_q, const uint8_t* a_sf, const int
                               const int32_t* offsets, const int32_t* tile_table, int32_t num_local,
                               int32_t rows_cap, int32_t N, int32_t K, int32_t tile_m, int32_t epilogue, void* d,
                               float* amax_out, hipStream_t stream);
+
+// L1 with the SiLU*up epilogue writing h as NVFP4 (fixed global scale out_gs[0]).
+int nvfp4_launch_grouped_gemm_nvfp4(const uint8_t* a_q, const uint8_t* a_sf, const int32_t* a_row_index,
+                                    const float* a_gs, const uint8_t* b_packed, const float* b_gs, int32_t dual_gs,
+                                    const int32_t* offsets, const int32_t* tile_table, int32_t num_local,
+                                    int32_t rows_cap, int32_t N, int32_t K, int32_t tile_m, const float* out_gs,
+                                    uint8_t* d_q, uint8_t* d_sf, hipStream_t stream);
 
 int nvfp4_launch_scatter(const void* y_bf16, const int32_t* token_slot, const float* topk_w, int32_t T, int32_t k,
                          int32_t H, void* out_bf16, hipStream_t stream);

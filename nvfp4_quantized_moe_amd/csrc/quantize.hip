@@ -7,33 +7,22 @@
 //                         sign kept in bit 3 of the nibble
 // tests history, packing-along-K commit: two nibbles per byte along K.
 //
-// Both roundings are decided exactly, as on the real quotients:
-//   sf  = nearest E4M3 (ties even, saturating) to bmax / (6 gs)
-//   m   = nearest E2M1 index (ties even) to |x| / (E4M3(sf) gs)
-// The scale comes from a float64 quotient (an E4M3 value or midpoint has at
-// most 5 significant bits, so the quotient of a BF16 by 6*gs that is not one
-// of them lies >= 2^-32 away relative; float64 rounding cannot move it across).
-// The magnitude is a count of E2M1 midpoints c*E4M3(sf)*gs passed; each
-// midpoint is exact in float64 (3 x 4 x 24 significant bits) and is turned
-// into a BF16 bit-pattern threshold U such that |x| passes it iff
-// bits(|x|) > U. One table of 7 thresholds per scale code (127 codes) is
-// built in LDS by every workgroup, so the per-element work is seven integer
-// compares.
+// The exact per-block rounding (threshold table in LDS, scale from a float64
+// quotient) is in quant_block.h.
 //
 // Kernels: amax (wave reductions, one partial maximum per workgroup on the
 // float bits, order-free) and quantize (each workgroup reduces the partials,
 // derives gs and builds the threshold table in LDS, then quantizes 16-element
 // blocks, one per thread, grid-stride over the tensor). With amax given (the
-// h path) only the quantize kernel runs.
+// h path) or with a fixed global scale (nvfp4_cutedsl.py history, static-scale
+// commit: gs measured once at warmup, then no max reduction) only the
+// quantize kernel runs.
 #include "common.h"
 #include "internal.h"
 #include "amax.h"
+#include "quant_block.h"
 
 namespace nvfp4 {
-
-// E2M1 rounding midpoints and whether an exact tie rounds up (upper code even)
-__constant__ double kMid[7] = {0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0};
-__constant__ int kTieUp[7] = {0, 1, 0, 1, 0, 1, 0};
 
 __global__ void fill_u32_kernel(uint32_t* p, int n, uint32_t v) {
   int i = blockIdx.x * blockDim.x + threadIdx.x;
@@ -47,41 +36,32 @@ __global__ __launch_bounds__(256) void amax_kernel(const uint16_t* __restrict__ 
   amax_block(x, per_batch, rows_dev, K, partial, clear, n_clear, blockIdx.y, blockIdx.x, gridDim.x);
 }
 
-// amax of tensor b, gs = RN_f32(amax / 2688), and the threshold table of
-// every scale code into LDS: lut[code] holds the BF16 bit patterns U_j such
-// that |x| passes E2M1 midpoint j of that code iff bits(|x|) > U_j.
-__device__ __forceinline__ float block_gs_and_lut(const float* __restrict__ amax_in,
+// gs of tensor b (the fixed gs_in[b], or RN_f32(amax / 2688) with amax from
+// amax_in or the partials) and its threshold table in LDS.
+__device__ __forceinline__ float block_gs_and_lut(const float* __restrict__ gs_in, const float* __restrict__ amax_in,
                                                   const uint32_t* __restrict__ partial, int n_partial, int b,
                                                   uint16_t* lut /* [128][8] in LDS */) {
   __shared__ uint32_t red[4];
-  uint32_t m = 0;
-  if (amax_in) {
-    m = __float_as_uint(amax_in[b]);
+  float gs;
+  if (gs_in) {
+    gs = gs_in[b];
   } else {
-    for (int i = threadIdx.x; i < n_partial; i += blockDim.x) m = max(m, partial[(size_t)b * n_partial + i]);
-    m = wave_max_u32(m);
-    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
-    __syncthreads();
-    m = max(max(red[0], red[1]), max(red[2], red[3]));
-  }
-  const float amax = __uint_as_float(m);
-  // float64 quotient rounded to float32: 53 >= 2*24 + 2, so this equals one
-  // correctly rounded float32 division
-  const float gs = (float)((double)amax / 2688.0);
-  for (int i = threadIdx.x; i < 128 * 8; i += blockDim.x) {
-    int code = i >> 3, j = i & 7;
-    uint32_t u = 0xFFFFu;
-    if (j < 7 && code > 0 && code <= 0x7E && gs > 0.0f) {
-      double step = (double)e4m3_to_f32((uint32_t)code) * (double)gs;  // exact
-      double thr = kMid[j] * step;                                       // exact
-      bool exact;
-      uint32_t rd = bf16_round_down_bits(thr, &exact);
-      // strict midpoint: |x| > thr  <=>  bits > bits(RD(thr))
-      // tie-up midpoint: |x| >= thr <=>  bits > bits(RU(thr)) - 1
-      u = (kTieUp[j] && exact) ? rd - 1u : rd;
+    uint32_t m = 0;
+    if (amax_in) {
+      m = __float_as_uint(amax_in[b]);
+    } else {
+      for (int i = threadIdx.x; i < n_partial; i += blockDim.x) m = max(m, partial[(size_t)b * n_partial + i]);
+      m = wave_max_u32(m);
+      if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
+      __syncthreads();
+      m = max(max(red[0], red[1]), max(red[2], red[3]));
     }
-    lut[i] = (uint16_t)u;
+    const float amax = __uint_as_float(m);
+    // float64 quotient rounded to float32: 53 >= 2*24 + 2, so this equals one
+    // correctly rounded float32 division
+    gs = (float)((double)amax / 2688.0);
   }
+  build_threshold_lut(gs, lut, threadIdx.x, blockDim.x);
   __syncthreads();
   return gs;
 }
@@ -89,14 +69,15 @@ __device__ __forceinline__ float block_gs_and_lut(const float* __restrict__ amax
 template <bool kRowsDev>
 __global__ __launch_bounds__(256) void quantize_kernel(const uint16_t* __restrict__ x, int64_t M, int64_t K,
                                                        const int32_t* __restrict__ rows_dev,
+                                                       const float* __restrict__ gs_in,
                                                        const float* __restrict__ amax_in,
                                                        const uint32_t* __restrict__ partial, int n_partial,
                                                        float* __restrict__ gs_out, uint8_t* __restrict__ q,
                                                        uint8_t* __restrict__ sf) {
   const int b = blockIdx.y;
   __shared__ uint4 lut[128];
-  const float gs = block_gs_and_lut(amax_in, partial, n_partial, b, reinterpret_cast<uint16_t*>(lut));
-  if (blockIdx.x == 0 && threadIdx.x == 0) gs_out[b] = gs;
+  const float gs = block_gs_and_lut(gs_in, amax_in, partial, n_partial, b, reinterpret_cast<uint16_t*>(lut));
+  if (gs_out && blockIdx.x == 0 && threadIdx.x == 0) gs_out[b] = gs;
   const double six_gs = 6.0 * (double)gs;  // exact
   int64_t rows = M;
   if (kRowsDev) rows = min(rows, (int64_t)rows_dev[0]);
@@ -107,28 +88,11 @@ __global__ __launch_bounds__(256) void quantize_kernel(const uint16_t* __restric
   for (int64_t blk = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; blk < nblk;
        blk += (int64_t)gridDim.x * blockDim.x) {
     const uint4* src = reinterpret_cast<const uint4*>(xb + blk * 16);
-    uint4 v0 = src[0], v1 = src[1];
-    uint32_t w[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
-    uint32_t bmax = 0;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) bmax = max(bmax, max(w[j] & 0x7FFFu, (w[j] >> 16) & 0x7FFFu));
-    uint32_t code = 0;
-    if (gs > 0.0f) code = e4m3_encode_rne_sat((double)bf16_to_f32(bmax) / six_gs);
-    uint4 tv = lut[code];
-    uint32_t U[7] = {tv.x & 0xFFFFu, tv.x >> 16, tv.y & 0xFFFFu, tv.y >> 16,
-                     tv.z & 0xFFFFu, tv.z >> 16, tv.w & 0xFFFFu};
-    uint32_t packed[2] = {0u, 0u};
-#pragma unroll
-    for (int e = 0; e < 16; ++e) {
-      uint32_t bits = (e & 1) ? (w[e >> 1] >> 16) : (w[e >> 1] & 0xFFFFu);
-      uint32_t a = bits & 0x7FFFu;
-      uint32_t m = 0;
-#pragma unroll
-      for (int j = 0; j < 7; ++j) m += (a > U[j]) ? 1u : 0u;
-      uint32_t nib = ((bits >> 12) & 8u) | m;
-      packed[e >> 3] |= nib << (4 * (e & 7));
-    }
-    *reinterpret_cast<uint2*>(qb + blk * 8) = make_uint2(packed[0], packed[1]);
+    const uint4 v0 = src[0], v1 = src[1];
+    const uint32_t w[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
+    uint2 packed;
+    const uint32_t code = quantize_block16(w, gs, six_gs, lut, &packed);
+    *reinterpret_cast<uint2*>(qb + blk * 8) = packed;
     sfb[blk] = (uint8_t)code;
   }
 }
@@ -181,11 +145,11 @@ int nvfp4_launch_quantize(const void* x_bf16, int64_t B, int64_t M, int64_t K, c
   // M == 0 still launches one workgroup per tensor: it writes gs
   dim3 grid((unsigned)quant_grid(M * (K / 16)), (unsigned)B);
   if (rows_dev)
-    hipLaunchKernelGGL(quantize_kernel<true>, grid, dim3(256), 0, stream, x, M, K, rows_dev, amax_in, partial, gx,
-                       gs_out, q, sf);
+    hipLaunchKernelGGL(quantize_kernel<true>, grid, dim3(256), 0, stream, x, M, K, rows_dev, nullptr, amax_in, partial,
+                       gx, gs_out, q, sf);
   else
-    hipLaunchKernelGGL(quantize_kernel<false>, grid, dim3(256), 0, stream, x, M, K, rows_dev, amax_in, partial, gx,
-                       gs_out, q, sf);
+    hipLaunchKernelGGL(quantize_kernel<false>, grid, dim3(256), 0, stream, x, M, K, rows_dev, nullptr, amax_in, partial,
+                       gx, gs_out, q, sf);
   NVFP4_CHECK_LAUNCH();
   return NVFP4_OK;
 }
@@ -196,10 +160,35 @@ int nvfp4_launch_quantize_from_partials(const void* x_bf16, int64_t M, int64_t K
   const uint32_t* partial = reinterpret_cast<const uint32_t*>(ws);
   const uint16_t* x = reinterpret_cast<const uint16_t*>(x_bf16);
   dim3 grid((unsigned)quant_grid(M * (K / 16)), 1u);
-  hipLaunchKernelGGL(quantize_kernel<false>, grid, dim3(256), 0, stream, x, M, K, nullptr, nullptr, partial,
-                     n_partial, gs_out, q, sf);
+  hipLaunchKernelGGL(quantize_kernel<false>, grid, dim3(256), 0, stream, x, M, K, nullptr, nullptr, nullptr,
+                     partial, n_partial, gs_out, q, sf);
   NVFP4_CHECK_LAUNCH();
   return NVFP4_OK;
+}
+
+// Quantize with fixed global scales gs_in[b]: one launch, no amax pass.
+int nvfp4_launch_quantize_static(const void* x_bf16, int64_t B, int64_t M, int64_t K, const float* gs_in,
+                                 const int32_t* rows_dev, uint8_t* q, uint8_t* sf, hipStream_t stream) {
+  const uint16_t* x = reinterpret_cast<const uint16_t*>(x_bf16);
+  dim3 grid((unsigned)quant_grid(M * (K / 16)), (unsigned)B);
+  if (rows_dev)
+    hipLaunchKernelGGL(quantize_kernel<true>, grid, dim3(256), 0, stream, x, M, K, rows_dev, gs_in, nullptr, nullptr,
+                       0, nullptr, q, sf);
+  else
+    hipLaunchKernelGGL(quantize_kernel<false>, grid, dim3(256), 0, stream, x, M, K, rows_dev, gs_in, nullptr,
+                       nullptr, 0, nullptr, q, sf);
+  NVFP4_CHECK_LAUNCH();
+  return NVFP4_OK;
+}
+
+extern "C" int nvfp4_quantize_static(const void* x_bf16, int64_t B, int64_t M, int64_t K, const float* gs_in,
+                                     uint8_t* q, uint8_t* sf, void* stream) {
+  if (B < 1 || B > 65535 || M < 0 || K <= 0 || K % 32 != 0) return NVFP4_ERR_SHAPE;
+  if (!gs_in) return NVFP4_ERR_NULL;
+  if (M > 0 && (!x_bf16 || !q || !sf)) return NVFP4_ERR_NULL;
+  if (M > 0 && (!nvfp4_aligned16(x_bf16) || !nvfp4_aligned16(q) || !nvfp4_aligned16(sf))) return NVFP4_ERR_ALIGN;
+  if (M == 0) return NVFP4_OK;
+  return nvfp4_launch_quantize_static(x_bf16, B, M, K, gs_in, nullptr, q, sf, (hipStream_t)stream);
 }
 
 extern "C" size_t nvfp4_quantize_ws_bytes(int64_t B, int64_t M, int64_t K) {
@@ -211,7 +200,7 @@ extern "C" size_t nvfp4_quantize_ws_bytes(int64_t B, int64_t M, int64_t K) {
 
 extern "C" int nvfp4_quantize(const void* x_bf16, int64_t B, int64_t M, int64_t K, const float* amax_in,
                               uint8_t* q, uint8_t* sf, float* gs_out, void* ws, size_t ws_bytes, void* stream) {
-  if (B < 1 || M < 0 || K <= 0 || K % 32 != 0) return NVFP4_ERR_SHAPE;
+  if (B < 1 || B > 65535 || M < 0 || K <= 0 || K % 32 != 0) return NVFP4_ERR_SHAPE;
   if (M > 0 && (!x_bf16 || !q || !sf)) return NVFP4_ERR_NULL;
   if (!gs_out || !ws) return NVFP4_ERR_NULL;
   if ((M > 0 && (!nvfp4_aligned16(x_bf16) || !nvfp4_aligned16(q) || !nvfp4_aligned16(sf))) ||

@@ -204,6 +204,10 @@ GEMM_CASES = {
     "prefill_like": (3, 384, 768, 400, [171, 129, 100], True),
     "no_gather_long_k": (2, 128, 2048, 90, [45, 45], False),
     "one_expert_empty": (4, 256, 256, 10, [0, 0, 0, 0], True),
+    # more items than workgroups: every workgroup runs two or more items, so the
+    # loads of one item's last stages run into the next item (3 loop stages per
+    # item with 3 in flight: the LDS buffer parity flips from item to item)
+    "many_items": (4, 8192, 256, 600, [700, 500, 0, 800], True),
 }
 
 

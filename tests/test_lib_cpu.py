@@ -24,7 +24,8 @@ def _declared():
 def test_header_declares_the_boundary():
     names = _declared()
     for n in ("nvfp4_quantize", "moe_route_slots", "nvfp4_grouped_gemm", "nvfp4_moe_forward",
-              "moe_weighted_scatter", "nvfp4_fold_scales", "nvfp4_pack_weights", "nvfp4_packed_bytes"):
+              "moe_weighted_scatter", "nvfp4_fold_scales", "nvfp4_pack_weights", "nvfp4_packed_bytes",
+              "nvfp4_quantize_static", "nvfp4_grouped_gemm_silu_nvfp4", "nvfp4_moe_forward_static"):
         assert n in names
 
 
@@ -43,7 +44,7 @@ def test_status_strings_and_sizes():
     nv = _lib()
     assert nv._status_string(0) == b"ok"
     assert b"workspace" in nv._status_string(4)
-    assert nv.version() == 200
+    assert nv.version() == 300
     assert nv.nvfp4_tile_table_len(512, 48, 32) == 1 + 2 * (16 + 48)
     lay = nv.nvfp4_moe_ws_layout(64, 8, 7168, 3072, 48)
     offs = [lay[r] for r in nv.WS_REGIONS]
@@ -108,3 +109,16 @@ def test_invalid_arguments_are_rejected_before_launch():
     assert nv._forward(ctypes.byref(huge), buf, 4, buf, buf, 2, 0, buf, buf, 1 << 62, s) == 2
     w = nv._Weights(8, 256, 128, 4096, 4096, 4096, 4096, 2)     # unknown gate/up scale mode
     assert nv._forward(ctypes.byref(w), buf, 4, buf, buf, 2, 0, buf, buf, 1 << 30, s) == 6
+    # fixed-scale entry points: NULL scales, bad shapes, unknown gate/up scale mode
+    assert nv._quantize_static(buf, 1, 4, 64, null, buf, buf, s) == 1
+    assert nv._quantize_static(buf, 1, 4, 48, buf, buf, buf, s) == 2
+    assert nv._quantize_static(buf, 65536, 4, 64, buf, buf, buf, s) == 2
+    assert nv._quantize_static(odd, 1, 4, 64, buf, buf, buf, s) == 3
+    gq = [buf] * 6
+    assert nv._gemm_nvfp4(*gq, 2, buf, buf, 8, 64, 256, 256, 32, buf, buf, buf, s) == 6
+    assert nv._gemm_nvfp4(*gq, 0, buf, buf, 8, 64, 192, 256, 32, buf, buf, buf, s) == 2   # N % 128
+    assert nv._gemm_nvfp4(*gq, 0, buf, buf, 8, 64, 256, 256, 48, buf, buf, buf, s) == 2   # tile_m
+    assert nv._gemm_nvfp4(*gq, 0, buf, buf, 8, 64, 256, 256, 32, null, buf, buf, s) == 1  # out_gs
+    w = nv._Weights(8, 256, 128, 4096, 4096, 4096, 4096)
+    assert nv._forward_static(ctypes.byref(w), buf, 4, buf, buf, 2, 0, null, buf, buf, 1 << 30, s) == 1
+    assert nv._forward_static(ctypes.byref(w), buf, 4, buf, buf, 2, 0, buf, buf, buf, 16, s) == 4
