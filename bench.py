@@ -224,6 +224,7 @@ def main():
         result["decode"]["graph"] = decode_graph(nv, weights, W.get_config("decode"), dev, max(args.steps, 50))
         result["quantize"] = quantize_c1(nv, W, dev, args.settle_ms)
         result["skewed"] = skewed_shard(nv, W, dev, args.settle_ms, max(args.steps, 10))
+        result["static_scales"] = static_scales(nv, weights, W, dev, args.settle_ms)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(cfg, ids, w, x, wg, wu, wd, T)
     print(json.dumps(result), flush=True)
@@ -348,6 +349,48 @@ def skewed_shard(nv, W, dev, settle_ms, steps):
             "tokens_per_s": round(T / (ms * 1e-3), 1), "ms_per_step": round(ms, 4), "slots": S,
             "empty_experts": int((counts == 0).sum()), "max_expert_share": round(float(counts.max()) / S, 4),
             "layer_tflops": round(S * 2.0 * (2 * I * H + H * I) / (ms * 1e-3) / 1e12, 2)}
+
+
+def static_scales(nv, weights, W, dev, settle_ms, rounds=5):
+    """The layer with fixed global scales (calibrated on the same batch, so the
+    output must equal the dynamic layer's) beside the dynamic layer, on the
+    prefill and decode shards, timed in alternating blocks on one stream."""
+    import torch
+    res = {}
+    for name, n in (("prefill", 10), ("decode", 50)):
+        cfg = W.get_config(name)
+        ids, w = W.make_router(cfg)
+        x = W.make_activations(cfg)
+        T, k = ids.shape
+        d_x = torch.from_numpy(x.view(np.int16)).view(torch.bfloat16).to(dev)
+        d_ids, d_w = torch.from_numpy(ids).to(dev), torch.from_numpy(w).to(dev)
+        lay = nv.nvfp4_moe_ws_layout(T, k, cfg.hidden, cfg.inter, cfg.num_local)
+        ws = torch.empty(lay["end"], dtype=torch.uint8, device=dev)
+        o_dyn = torch.empty((T, cfg.hidden), dtype=torch.bfloat16, device=dev)
+        o_sta = torch.empty_like(o_dyn)
+        gs = nv.calibrate_static_gs(weights, d_x, d_ids, d_w, cfg.expert_start)
+        fns = {"dynamic": lambda: nv.nvfp4_moe_forward(weights, d_x, d_ids, d_w, cfg.expert_start, out=o_dyn, ws=ws),
+               "static": lambda: nv.nvfp4_moe_forward_static(weights, d_x, d_ids, d_w, cfg.expert_start, gs,
+                                                             out=o_sta, ws=ws)}
+        settle(fns["dynamic"], settle_ms)
+        times = {key: [] for key in fns}
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        for _ in range(rounds):
+            for key, fn in fns.items():
+                e0.record()
+                for _ in range(n):
+                    fn()
+                e1.record()
+                torch.cuda.synchronize()
+                times[key].append(e0.elapsed_time(e1) / n)
+        ms_s, ms_d = float(np.median(times["static"])), float(np.median(times["dynamic"]))
+        res[name] = {"ms_per_step": round(ms_s, 4), "tokens_per_s": round(T / (ms_s * 1e-3), 1),
+                     "dynamic_ms_per_step": round(ms_d, 4), "speedup_vs_dynamic": round(ms_d / ms_s, 4),
+                     "equals_dynamic": bool(torch.equal(o_sta.view(torch.int16), o_dyn.view(torch.int16)))}
+    res["note"] = ("fixed gs_x, gs_h measured once by a dynamic pass (calibrate_static_gs); no amax passes; "
+                   "prefill: h written as NVFP4 by the L1 epilogue, decode: BF16 h + one fixed-scale quantize; "
+                   "medians of alternating blocks")
+    return res
 
 
 def quantize_c1(nv, W, dev, settle_ms, reps=50):

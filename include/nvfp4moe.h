@@ -272,10 +272,11 @@ int nvfp4_moe_forward(const nvfp4_moe_weights* w, const void* x_bf16, int32_t T,
  * nvfp4_moe_forward leaves in its workspace for a calibration batch. Steps:
  * nvfp4_quantize_static of x with gs_x -> route -> L1 whose epilogue writes h
  * as NVFP4 with gs_h (nvfp4_grouped_gemm_silu_nvfp4) -> L2 (alpha = gs_h *
- * w2_gs[e]) -> weighted scatter. With the gs values nvfp4_moe_forward measured
- * for the same inputs, the output equals nvfp4_moe_forward's bit for bit.
- * Same arguments, workspace and limits as nvfp4_moe_forward; the workspace's
- * H and SCALARS regions are not used.
+ * w2_gs[e]) -> weighted scatter. Decode-shaped batches (nvfp4_moe_tile_m ==
+ * 32) write BF16 h and quantize it with gs_h in a launch of its own instead.
+ * With the gs values nvfp4_moe_forward measured for the same inputs, the
+ * output equals nvfp4_moe_forward's bit for bit. Same arguments, workspace
+ * and limits as nvfp4_moe_forward; the SCALARS region is left unspecified.
  */
 int nvfp4_moe_forward_static(const nvfp4_moe_weights* w, const void* x_bf16, int32_t T,
                              const int32_t* topk_ids, const float* topk_w, int32_t k, int32_t expert_start,

@@ -169,9 +169,10 @@ extern "C" int nvfp4_moe_forward(const nvfp4_moe_weights* w, const void* x_bf16,
 // The layer with fixed global scales gs_in = (gs_x, gs_h), measured once
 // beforehand (nvfp4_cutedsl.py history, static-scale commit: warmup measures
 // the L1 input's and the L1 output's gs; inference quantizes with them and
-// no max reduction). Four launches on top of the route: quantize x, L1 whose
-// epilogue writes h as NVFP4 (no BF16 h, no separate re-quantization), L2,
-// scatter.
+// no max reduction). For prefill-shaped batches four launches on top of the
+// route: quantize x, L1 whose epilogue writes h as NVFP4 (no BF16 h, no
+// separate re-quantization), L2, scatter; decode-shaped batches keep BF16 h
+// and quantize it with gs_h in a launch of its own.
 extern "C" int nvfp4_moe_forward_static(const nvfp4_moe_weights* w, const void* x_bf16, int32_t T,
                                         const int32_t* topk_ids, const float* topk_w, int32_t k,
                                         int32_t expert_start, const float* gs_in, void* out_bf16, void* ws,
@@ -196,6 +197,8 @@ extern "C" int nvfp4_moe_forward_static(const nvfp4_moe_weights* w, const void* 
   int32_t* token_slot = reinterpret_cast<int32_t*>(R(NVFP4_WS_TOKEN_SLOT));
   int32_t* tiles = reinterpret_cast<int32_t*>(R(NVFP4_WS_TILES));
   void* route_ws = R(NVFP4_WS_ROUTE_SCRATCH);
+  uint16_t* h = reinterpret_cast<uint16_t*>(R(NVFP4_WS_H));
+  float* scalars = reinterpret_cast<float*>(R(NVFP4_WS_SCALARS));
   uint8_t* h_q = reinterpret_cast<uint8_t*>(R(NVFP4_WS_H_Q));
   uint8_t* h_sf = reinterpret_cast<uint8_t*>(R(NVFP4_WS_H_SF));
   uint16_t* y = reinterpret_cast<uint16_t*>(R(NVFP4_WS_Y));
@@ -209,11 +212,25 @@ extern "C" int nvfp4_moe_forward_static(const nvfp4_moe_weights* w, const void* 
                                slot_expert, slot_weight, token_slot, tiles, route_ws, stream)))
     return st;
   if (cap > 0) {
-    // a4/a5/a6: L1, SiLU*up and NVFP4 h with gs_h in one kernel
-    if ((st = nvfp4_launch_grouped_gemm_nvfp4(x_q, x_sf, slot_token, &gs_in[0], w->w1, w->w1_gs, w->w1_dual_gs,
-                                              offsets, tiles, L, cap, 2 * I, H, tile_m, &gs_in[1], h_q, h_sf,
-                                              stream)))
-      return st;
+    if (tile_m >= 64) {
+      // a4/a5/a6: L1, SiLU*up and NVFP4 h with gs_h in one kernel
+      if ((st = nvfp4_launch_grouped_gemm_nvfp4(x_q, x_sf, slot_token, &gs_in[0], w->w1, w->w1_gs, w->w1_dual_gs,
+                                                offsets, tiles, L, cap, 2 * I, H, tile_m, &gs_in[1], h_q, h_sf,
+                                                stream)))
+        return st;
+    } else {
+      // decode-shaped batches: h is small, and the NVFP4 epilogue's registers
+      // (the next item's stages stay in flight across it) would cost the
+      // weight-streaming GEMM a quarter of its resident workgroups; BF16 h,
+      // then one fixed-scale quantization of its valid rows (the amax the
+      // BF16 epilogue raises goes to the unused scalars region)
+      if ((st = nvfp4_launch_grouped_gemm(x_q, x_sf, slot_token, &gs_in[0], w->w1, w->w1_gs, offsets, tiles, L,
+                                          cap, 2 * I, H, tile_m,
+                                          w->w1_dual_gs ? NVFP4_EPI_SILU_MUL_DUAL : NVFP4_EPI_SILU_MUL, h,
+                                          &scalars[1], stream)))
+        return st;
+      if ((st = nvfp4_launch_quantize_static(h, 1, cap, I, &gs_in[1], &offsets[L], h_q, h_sf, stream))) return st;
+    }
     // a7: L2 in slot order, alpha = gs_h * w2_gs[e]
     if ((st = nvfp4_launch_grouped_gemm(h_q, h_sf, nullptr, &gs_in[1], w->w2, w->w2_gs, offsets, tiles, L, cap, H,
                                         I, tile_m, NVFP4_EPI_BF16, y, nullptr, stream)))

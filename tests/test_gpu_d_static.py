@@ -200,8 +200,9 @@ def test_layer_static_edge_cases(nv):
     assert not z.float().abs().sum().item()
 
 
-def test_layer_static_graph_replay(nv):
-    cfg, ids, w, x, wg, wu, wd = _layer("mid_skew")
+@pytest.mark.parametrize("name", ["tiny", "mid_skew"])   # decode-shaped (BF16 h) and prefill-shaped (NVFP4 epilogue)
+def test_layer_static_graph_replay(nv, name):
+    cfg, ids, w, x, wg, wu, wd = _layer(name)
     weights = nv.prepare_weights(to_bf16(wg), to_bf16(wu), to_bf16(wd))
     T, k = ids.shape
     d_x, d_ids, d_w = to_bf16(x), to_dev(ids), to_dev(w)
