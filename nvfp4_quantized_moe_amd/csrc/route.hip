@@ -126,10 +126,21 @@ __device__ __forceinline__ void wave_key_rank(int key, int nbits, int* rank, int
   *last = (match >> lane) == 1ull;
 }
 
+// Inclusive prefix sum across the 64 lanes of a wave.
+__device__ __forceinline__ int wave_inclusive_scan(int v) {
+  const int lane = threadIdx.x & 63;
+  for (int o = 1; o < 64; o <<= 1) {
+    const int t = __shfl_up(v, o, 64);
+    if (lane >= o) v += t;
+  }
+  return v;
+}
+
 // One workgroup. Per-expert totals from the per-chunk histograms, then the
 // offsets, the tile table and every chunk's first slot per expert. When the
-// histograms fit in LDS (stage_cc), all threads first copy them there, so the
-// per-expert passes over the chunks read LDS instead of memory.
+// histograms fit in LDS (stage_cc), all threads first copy them there. Each
+// wave takes whole experts and its 64 lanes walk the chunks 64 at a time, so
+// a per-expert pass over the chunks is a few wave prefix sums.
 __global__ __launch_bounds__(kScanThreads) void route_scan_kernel(
     const int32_t* __restrict__ chunk_counts, int nchunks, int L, int tile_m, int stage_cc,
     int32_t* __restrict__ counts, int32_t* __restrict__ offsets, int32_t* __restrict__ bases,
@@ -146,18 +157,28 @@ __global__ __launch_bounds__(kScanThreads) void route_scan_kernel(
     __syncthreads();
     cc = s_cc;
   }
-  for (int e = threadIdx.x; e < L; e += blockDim.x) {
-    int c = 0;
-    for (int ch = 0; ch < nchunks; ++ch) c += cc[(size_t)ch * L + e];
-    s_cnt[e] = c;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  constexpr int kWaves = kScanThreads / 64;
+  for (int e = wave; e < L; e += kWaves) {
+    int total = 0;
+    for (int c0 = 0; c0 < nchunks; c0 += 64) {
+      const int ch = c0 + lane;
+      const int incl = wave_inclusive_scan(ch < nchunks ? cc[(size_t)ch * L + e] : 0);
+      total += __shfl(incl, 63, 64);
+    }
+    if (lane == 0) s_cnt[e] = total;
   }
   __syncthreads();
   scan_experts(s_cnt, L, tile_m, s_off, s_toff, wsum, counts, offsets, tile_table);
-  for (int e = threadIdx.x; e < L; e += blockDim.x) {
+  // scan_experts ends with s_off written and synchronised
+  for (int e = wave; e < L; e += kWaves) {
     int run = s_off[e];
-    for (int ch = 0; ch < nchunks; ++ch) {
-      bases[(size_t)ch * L + e] = run;
-      run += cc[(size_t)ch * L + e];
+    for (int c0 = 0; c0 < nchunks; c0 += 64) {
+      const int ch = c0 + lane;
+      const int v = ch < nchunks ? cc[(size_t)ch * L + e] : 0;
+      const int incl = wave_inclusive_scan(v);
+      if (ch < nchunks) bases[(size_t)ch * L + e] = run + incl - v;
+      run += __shfl(incl, 63, 64);
     }
   }
 }
