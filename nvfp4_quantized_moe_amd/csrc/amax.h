@@ -25,16 +25,23 @@ __device__ __forceinline__ void amax_block(const uint16_t* __restrict__ x, int64
   }
   const uint4* xv = reinterpret_cast<const uint4*>(x + (int64_t)b * per_batch);
   const int64_t nv = n / 8;
+  const int64_t stride = (int64_t)nblk * blockDim.x;
   uint32_t m = 0;
-  for (int64_t i = (int64_t)blk * blockDim.x + threadIdx.x; i < nv; i += (int64_t)nblk * blockDim.x) {
-    uint4 v = xv[i];
-    uint32_t w[4] = {v.x, v.y, v.z, v.w};
+  auto fold = [&](const uint4& v) {
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      uint32_t lo = w[j] & 0x7FFFu, hi = (w[j] >> 16) & 0x7FFFu;
-      m = max(m, max(lo, hi));
-    }
+    for (int j = 0; j < 4; ++j) m = max(m, max(w[j] & 0x7FFFu, (w[j] >> 16) & 0x7FFFu));
+  };
+  int64_t i = (int64_t)blk * blockDim.x + threadIdx.x;
+  // eight independent 16-byte loads in flight per thread (the maximum is order-free)
+  for (; i + 7 * stride < nv; i += 8 * stride) {
+    uint4 v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) v[u] = xv[i + u * stride];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) fold(v[u]);
   }
+  for (; i < nv; i += stride) fold(xv[i]);
   m = wave_max_u32(m);
   __shared__ uint32_t red[16];
   const int nwaves = (int)(blockDim.x + 63) / 64;

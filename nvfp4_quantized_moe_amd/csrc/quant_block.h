@@ -26,20 +26,21 @@ namespace nvfp4 {
 // bits(|x|) > U; 0xFFFF where nothing passes, also for gs <= 0 or NaN).
 // Threads tid = 0 .. nthreads-1 fill it together; the caller synchronises.
 __device__ __forceinline__ void build_threshold_lut(float gs, uint16_t* lut, int tid, int nthreads) {
-  // E2M1 rounding midpoints, and whether an exact tie rounds up (upper code even)
-  constexpr double kMid[7] = {0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0};
-  constexpr bool kTieUp[7] = {false, true, false, true, false, true, false};
   for (int i = tid; i < 128 * 8; i += nthreads) {
     const int code = i >> 3, j = i & 7;
     uint32_t u = 0xFFFFu;
     if (j < 7 && code > 0 && code <= 0x7E && gs > 0.0f) {
+      // E2M1 midpoint j (0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5); an exact tie
+      // rounds up at the odd j (0.75, 1.75, 3.5: the upper code is even)
+      const double mid = j < 4 ? 0.25 + 0.5 * j : (j == 6 ? 5.0 : j - 1.5);
+      const bool tie_up = (j & 1) != 0;
       const double step = (double)e4m3_to_f32((uint32_t)code) * (double)gs;  // exact
-      const double thr = kMid[j] * step;                                      // exact
+      const double thr = mid * step;                                          // exact
       bool exact;
       const uint32_t rd = bf16_round_down_bits(thr, &exact);
       // strict midpoint: |x| > thr  <=>  bits > bits(RD(thr))
       // tie-up midpoint: |x| >= thr <=>  bits > bits(RU(thr)) - 1
-      u = (kTieUp[j] && exact) ? rd - 1u : rd;
+      u = (tie_up && exact) ? rd - 1u : rd;
     }
     lut[i] = (uint16_t)u;
   }
@@ -48,6 +49,7 @@ __device__ __forceinline__ void build_threshold_lut(float gs, uint16_t* lut, int
 // One block: w[j] holds elements 2j (low half) and 2j+1 (high half) as BF16.
 // Writes the 16 nibbles (element 2j in the low nibble of byte j) to *out and
 // returns the scale code. six_gs = 6 * (double)gs.
+
 __device__ __forceinline__ uint32_t quantize_block16(const uint32_t w[8], float gs, double six_gs, const uint4* lut,
                                                      uint2* out) {
   uint32_t bmax = 0;

@@ -85,31 +85,49 @@ __global__ __launch_bounds__(256) void quantize_kernel(const uint16_t* __restric
   const uint16_t* xb = x + (size_t)b * M * K;
   uint8_t* qb = q + (size_t)b * M * (K / 2);
   uint8_t* sfb = sf + (size_t)b * M * (K / 16);
-  for (int64_t blk = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; blk < nblk;
-       blk += (int64_t)gridDim.x * blockDim.x) {
-    const uint4* src = reinterpret_cast<const uint4*>(xb + blk * 16);
-    const uint4 v0 = src[0], v1 = src[1];
+  auto one = [&](int64_t blk, const uint4& v0, const uint4& v1) {
     const uint32_t w[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
     uint2 packed;
     const uint32_t code = quantize_block16(w, gs, six_gs, lut, &packed);
     *reinterpret_cast<uint2*>(qb + blk * 8) = packed;
     sfb[blk] = (uint8_t)code;
-  }
+  };
+  const uint4* src = reinterpret_cast<const uint4*>(xb);
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  int64_t blk = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  for (; blk < nblk; blk += stride) one(blk, src[2 * blk], src[2 * blk + 1]);
 }
 
 }  // namespace nvfp4
 
 using namespace nvfp4;
 
+// Workgroups of the quantize kernel: one per 256 blocks, at most as many as
+// the device holds at once (CU count x resident workgroups per CU, queried
+// once), so the grid-stride loop runs in a single round.
 static int quant_grid(int64_t nblk) {
+  static int resident = 0;
+  if (resident == 0) {
+    int dev = 0, n_cu = 0, nb = 0;
+    if (hipGetDevice(&dev) == hipSuccess &&
+        hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess &&
+        hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, reinterpret_cast<const void*>(quantize_kernel<false>), 256,
+                                                     0) == hipSuccess &&
+        n_cu > 0 && nb > 0)
+      resident = n_cu * nb;
+    else
+      resident = 2048;
+  }
   int64_t g = (nblk + 255) / 256;
-  if (g > 2048) g = 2048;
+  if (g > resident) g = resident;
   if (g < 1) g = 1;
   return (int)g;
 }
 
-// workgroups of the amax pass per tensor (fixed by the tensor size, at most kAmaxGrid)
-constexpr int kAmaxGrid = 1024;
+// workgroups of the amax pass per tensor (fixed by the tensor size, at most
+// kAmaxGrid; a 117 MB tensor reads at 5.1 TB/s with 1024 of them, 6.3 TB/s
+// with 4096 on MI355X)
+constexpr int kAmaxGrid = 4096;
 static int amax_grid(int64_t per_batch) {
   int64_t gx = (per_batch / 8 + 255) / 256;
   if (gx > kAmaxGrid) gx = kAmaxGrid;

@@ -28,6 +28,37 @@ def adversarial_rows(rng, n_rows=6):
     return W.bf16_bits(np.asarray(rows, np.float32))
 
 
+def near_midpoint_blocks(seed, n_blocks=96):
+    """One row of two 16-element BF16 blocks per tensor, with a float32 global
+    scale per tensor, such that elements divided by their block's step (E4M3 scale d
+    times gs) land within a few float32 ulps of an E2M1 rounding midpoint m
+    without being on it: gs = RN_f32(x / (d * m)) for a chosen element x, and
+    the block maximum RN_bf16(6 * d * gs) gives the block scale d. Returns
+    (bits uint16 [n_blocks, 1, 32], gs float32 [n_blocks])."""
+    rng = np.random.default_rng(seed)
+    mids = [0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0]
+    scales = [E4M3_VALUES[c] for c in (0x30, 0x38, 0x3F, 0x52)] + [1.125, 1.625, 13.0, 0.8125]
+    blocks, gss = [], []
+    for _ in range(n_blocks):
+        m = float(rng.choice(mids))
+        d = float(rng.choice(scales))
+        xb = W.bf16_bits(np.array([(1 + rng.integers(0, 128) / 128.0) * 2.0 ** int(rng.integers(-6, 6))], np.float32))
+        x = float((xb.astype(np.uint32) << 16).view(np.float32)[0])
+        gs = np.float32(x / (d * m))
+        bmax = np.float32(6.0 * d * float(gs))
+        vals = [bmax, x, -x, x] + [float(rng.uniform(-1, 1)) * float(bmax) for _ in range(12)]
+        # a few more elements placed on other midpoints of the same step (rounded to BF16)
+        for i in range(4, 8):
+            vals[i] = float(rng.choice(mids)) * d * float(gs) * float(rng.choice([-1, 1]))
+        rng.shuffle(vals)
+        second = list(vals)
+        rng.shuffle(second)
+        blocks.append(vals + second)   # two blocks of the same values (same scale): K = 32
+        gss.append(gs)
+    bits = W.bf16_bits(np.asarray(blocks, np.float32)).reshape(n_blocks, 1, 32)
+    return bits, np.asarray(gss, np.float32)
+
+
 def quant_case(name):
     """BF16 bit arrays for the quantizer parity cases."""
     rng = np.random.default_rng(zlib.crc32(name.encode()))

@@ -16,7 +16,7 @@ import torch
 
 import oracle as O
 import workloads as W
-from _cases import quant_case
+from _cases import near_midpoint_blocks, quant_case
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
@@ -80,6 +80,20 @@ def test_quantize_static_batched_and_zero_scale(nv):
         assert np.array_equal(sf[b].cpu().numpy(), osf), b
         assert np.array_equal(q[b].cpu().numpy(), oq), b
     assert not sf[2].any().item() and not (q[2] & 0x77).any().item()
+
+
+@pytest.mark.parametrize("seed", [3, 4])
+def test_quantize_static_near_midpoints(nv, seed):
+    # elements within a few float32 ulps of an E2M1 midpoint: the quantizer's
+    # float32 fast path must hand these blocks to its exact path
+    bits, gs = near_midpoint_blocks(seed)
+    log(f"quantize_static near midpoints seed={seed} blocks={bits.shape[0]}")
+    q, sf = nv.nvfp4_quantize_static(to_bf16(bits), to_dev(gs))
+    torch.cuda.synchronize()
+    q, sf = q.cpu().numpy(), sf.cpu().numpy()
+    for b in range(bits.shape[0]):
+        oq, osf, _ = O.quantize(bits[b], gs=gs[b])
+        assert np.array_equal(sf[b], osf) and np.array_equal(q[b], oq), b
 
 
 # ---------------------------------------------------- L1 with NVFP4 output

@@ -15,7 +15,7 @@ import pytest
 
 import oracle as O
 import workloads as W
-from _cases import adversarial_rows
+from _cases import adversarial_rows, near_midpoint_blocks
 
 GOLD = os.path.join(os.path.dirname(__file__), "golden")
 E4M3_POS = [Fraction(float(v)) for v in O.e4m3_decode(np.arange(0, 0x7F, dtype=np.uint8))]
@@ -275,3 +275,13 @@ def test_static_gs_zero_gives_zeros():
     xb = _bits(np.linspace(-3, 3, 64, dtype=np.float32).reshape(2, 32))
     q, sf, gs = O.quantize(xb, gs=0.0)
     assert gs == 0 and not sf.any() and not (O.unpack_nibbles(q) & 7).any()
+
+
+def test_brute_force_near_midpoints():
+    # elements a few float32 ulps from an E2M1 midpoint (not on it): the exact
+    # rounding must go to the nearer neighbour on the correct side
+    bits, gs = near_midpoint_blocks(3)
+    for b in range(bits.shape[0]):
+        q, sf, _ = O.quantize(bits[b], gs=gs[b])
+        bq, bsf, _ = brute_quantize(bits[b], gs=gs[b])
+        assert np.array_equal(sf, bsf) and np.array_equal(q, bq), b
