@@ -80,6 +80,8 @@ def main():
     ap.add_argument("--summarize-trace", metavar="TRACE_DIR",
                     help="write the per-kernel table of a rocprofv3 --kernel-trace --stats csv run to "
                          "profiles/ and exit")
+    ap.add_argument("--trace-all", action="store_true",
+                    help="with --summarize-trace: the trace is of the whole default run (no --no-decode)")
     ap.add_argument("--summarize-mfma", metavar="PMC_DIR",
                     help="write the MFMA counters of the L1 GEMM from a rocprofv3 --pmc csv run to "
                          "profiles/ and exit")
@@ -88,7 +90,7 @@ def main():
         summarize_traffic(args.config, *args.summarize_traffic)
         return
     if args.summarize_trace:
-        summarize_trace(args.config, args.summarize_trace)
+        summarize_trace(args.config, args.summarize_trace, args.trace_all)
         return
     if args.summarize_mfma:
         summarize_mfma(args.config, args.summarize_mfma)
@@ -491,22 +493,30 @@ def _short_kernel_name(n):
     return n if len(n) < 90 else n[:87] + "..."
 
 
-def summarize_trace(workload, d):
+def summarize_trace(workload, d, all_workloads=False):
     """Per-kernel table (calls, total, average, min, max) of a rocprofv3
-    --kernel-trace --stats csv run."""
+    --kernel-trace --stats csv run: of the headline workload alone
+    (--no-decode), or with all_workloads of the whole default run (decode,
+    skewed and static-scale objects too)."""
     import csv
     import glob
     f = glob.glob(os.path.join(d, "**", "*kernel_stats.csv"), recursive=True)
     if not f:
         raise SystemExit(f"no kernel_stats.csv under {d}")
     rows = list(csv.DictReader(open(f[0])))
-    path = os.path.join(PROFILE_DIR, f"layer_{workload}_kernel_trace.md")
+    name = "layer_all_workloads_kernel_trace.md" if all_workloads else f"layer_{workload}_kernel_trace.md"
+    path = os.path.join(PROFILE_DIR, name)
     with open(path, "w") as o:
-        o.write(f"# Kernel trace of the benchmark ({workload} shard headline, decode shard beside it)\n\n")
+        if all_workloads:
+            o.write(f"# Kernel trace of the whole benchmark run ({workload} headline; decode, skewed and "
+                    "static-scale objects beside it)\n\n")
+        else:
+            o.write(f"# Kernel trace of the benchmark, {workload} shard alone\n\n")
         o.write("Command, from the repository root on the MI355X box:\n\n```\n")
         o.write(f"rocprofv3 --kernel-trace --stats -f csv -d {d} -o run -- python -u bench.py --config {workload} "
-                f"--steps 5 --warmup 1 --no-cpu-baseline --settle-ms 100\n")
-        o.write(f"python bench.py --config {workload} --summarize-trace {d}\n```\n\n")
+                f"--steps 5 --warmup 1 --no-cpu-baseline --settle-ms 100{'' if all_workloads else ' --no-decode'}\n")
+        o.write(f"python bench.py --config {workload} --summarize-trace {d}{' --trace-all' if all_workloads else ''}"
+                "\n```\n\n")
         o.write("Grouped GEMM template arguments: <SUB_M, SUB_N, WAVES, stages in flight, epilogue> "
                 "(epilogue 1 = L1 with SiLU*up, 0 = L2). The settle period, the warmup and the timed "
                 "steps are all in the trace.\n\n")

@@ -208,6 +208,8 @@ GEMM_CASES = {
     # loads of one item's last stages run into the next item (3 loop stages per
     # item with 3 in flight: the LDS buffer parity flips from item to item)
     "many_items": (4, 8192, 256, 600, [700, 500, 0, 800], True),
+    # one K stage: fewer stages than the ring runs ahead (the rest read zeros)
+    "single_stage": (3, 256, 128, 40, [20, 0, 33], True),
 }
 
 

@@ -104,6 +104,7 @@ GEMM_CASES = {
     "decode_like": (8, 512, 1024, 24, [1, 2, 0, 0, 3, 1, 0, 1]),
     "prefill_like": (3, 768, 768, 400, [171, 129, 100]),
     "many_items": (4, 4096, 256, 600, [700, 500, 0, 800]),   # two or more items per workgroup
+    "single_stage": (3, 256, 128, 40, [20, 0, 33]),           # K = 128: one stage per item
 }
 
 
