@@ -90,6 +90,9 @@ CONFIGS = {
     "mid_skew": LayerConfig("mid_skew", 12, tokens=640, top_k=8, num_global=384, num_local=48,
                             expert_start=96, hidden=256, inter=128, logits="zipf",
                             up_scale=30.0),
+    # more than 1024 slot entries (the chunked route) with decode-height (32-row) tiles
+    "mid_route3": LayerConfig("mid_route3", 13, tokens=200, top_k=8, num_global=384, num_local=48,
+                              expert_start=96, hidden=256, inter=128),
 }
 
 
