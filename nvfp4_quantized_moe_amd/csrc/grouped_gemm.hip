@@ -64,7 +64,6 @@ struct GemmCfg {
 // zero, so rows past a group's end and column tiles past N need no branches.
 constexpr uint32_t kRsrcWord3 = 0x00020000u;
 constexpr uint32_t kOutOfRange = 0x80000000u;  // offset that is never in range
-constexpr int kWaitVmcnt0 = 0x0F70;  // s_waitcnt vmcnt(0) expcnt(7) lgkmcnt(15) (gfx9 encoding)
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t num_records) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)num_records, (int)kRsrcWord3);
@@ -132,8 +131,7 @@ template <int SUB_M, int SUB_N, int WAVES, int P, int EPI>
 __global__ __launch_bounds__(64 * WAVES) void grouped_gemm_kernel(
     const uint8_t* __restrict__ a_q, const uint8_t* __restrict__ a_sf, const int32_t* __restrict__ a_row_index,
     const float* __restrict__ a_gs, const uint8_t* __restrict__ b_packed, const float* __restrict__ b_gs,
-    const int32_t* __restrict__ offsets, const int32_t* __restrict__ tile_table, int max_tiles, int rows_cap, int N,
-    int K,
+    const int32_t* __restrict__ offsets, const int32_t* __restrict__ tile_table, int max_tiles, int N, int K,
     int n_out, int n_ntiles, int col_fastest, int dual_gs, uint16_t* __restrict__ d, float* __restrict__ amax_out,
     uint8_t* __restrict__ d_sf, const float* __restrict__ out_gs) {
   constexpr bool kSilu = EPI != NVFP4_EPI_BF16;  // gate/up pairs, n_out = N / 2
@@ -469,7 +467,7 @@ static int launch_cfg(const uint8_t* a_q, const uint8_t* a_sf, const int32_t* a_
   if (grid >= kXcds) grid -= grid % kXcds;
   if (grid < 1) grid = 1;
   hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(C::THREADS), lds_bytes, stream, a_q, a_sf, a_row_index, a_gs,
-                     b_packed, b_gs, offsets, tile_table, max_tiles, rows_cap, N, K, n_out, n_ntiles, col_fastest, dual_gs,
+                     b_packed, b_gs, offsets, tile_table, max_tiles, N, K, n_out, n_ntiles, col_fastest, dual_gs,
                      reinterpret_cast<uint16_t*>(d), amax_out, d_sf, out_gs);
   NVFP4_CHECK_LAUNCH();
   return NVFP4_OK;
