@@ -40,8 +40,15 @@ def log(msg):
 
 
 def kernel_source_sha() -> str:
+    """Hash of grouped_gemm.hip's code: // comments, trailing blanks and blank
+    lines removed, so that a comment edit keeps the measured traffic valid."""
     p = os.path.join(ROOT, "nvfp4_quantized_moe_amd", "csrc", "grouped_gemm.hip")
-    return hashlib.sha256(open(p, "rb").read()).hexdigest()[:16]
+    code = []
+    for line in open(p, encoding="utf-8"):
+        line = line.split("//", 1)[0].rstrip()
+        if line:
+            code.append(line)
+    return hashlib.sha256("\n".join(code).encode()).hexdigest()[:16]
 
 
 def read_traffic(workload: str):

@@ -21,8 +21,9 @@
 //
 // Structure: a persistent grid walks work items (row tile from the device
 // tile table x column tile); block ids are remapped so that each XCD (own L2)
-// takes a contiguous run of items, which share the row tile's activations.
-// Each item streams K in stages of 128. The row tile's activations (row-major
+// takes a contiguous run of items, whose row tiles share the expert's weight
+// tile. Each item streams K in stages of 128, and the loads run ahead across
+// the items of a workgroup. The row tile's activations (row-major
 // NVFP4, gathered through the slot's token) go global -> registers -> LDS as
 // fp16, double buffered; every wave reads its A fragments from LDS. Weights
 // are stored pre-packed in MFMA fragment order (nvfp4_pack_weights), so each
@@ -321,9 +322,10 @@ __global__ __launch_bounds__(64 * WAVES) void grouped_gemm_kernel(
 
   // Each item runs S stages (K's stage count rounded up to a multiple of P; the
   // extra stages multiply zeros). The loads run P - 1 stages ahead across item
-  // boundaries: the last block of an item loads the first P - 1 stages of the
-  // workgroup's next item and decodes its stage 0 into LDS, so the next item
-  // starts without waiting for memory. Stage s of an item uses LDS buffer
+  // boundaries: the last P - 1 stages of an item load the first P - 1 stages of
+  // the workgroup's next item (load_stage selects the source per stage), and the
+  // item's last stage decodes the next item's stage 0 into LDS, so the next
+  // item starts without waiting for memory. Stage s of an item uses LDS buffer
   // (s + par) & 1, where par flips with every item when S is odd.
   int par = 0;
   Src cur;
