@@ -173,7 +173,7 @@ int nvfp4_pack_weights(const uint8_t* q, const uint8_t* sf, int64_t B, int64_t N
  * and N * K * 9/16 (32-bit buffer offsets).
  * Only rows of listed tiles are written. Requires K % 128 == 0, N % 64 == 0
  * (N % 128 == 0 for NVFP4_EPI_SILU_MUL), 1 <= L, tile_m 32 (decode-shaped
- * batches), 64 (prefill-shaped) or 128 (large groups).
+ * batches), 64, 96 (prefill-shaped) or 128 (large groups).
  */
 enum { NVFP4_EPI_BF16 = 0, NVFP4_EPI_SILU_MUL = 1, NVFP4_EPI_SILU_MUL_DUAL = 2 };
 int nvfp4_grouped_gemm(const uint8_t* a_q, const uint8_t* a_sf, const int32_t* a_row_index,
@@ -259,7 +259,8 @@ enum {
 size_t nvfp4_moe_ws_layout(int32_t T, int32_t k, int32_t hidden, int32_t inter, int32_t num_local,
                            int32_t tile_m, size_t* offsets_out);
 size_t nvfp4_moe_ws_bytes(int32_t T, int32_t k, int32_t hidden, int32_t inter, int32_t num_local);
-/* GEMM row-tile height the layer uses for a given batch (decode- or prefill-shaped). */
+/* GEMM row-tile height the layer uses for a given batch: 32 when decode-shaped, 96 when
+ * prefill-shaped (slot capacity T*k of at least 64 rows per local expert). */
 int32_t nvfp4_moe_tile_m(int32_t T, int32_t k, int32_t num_local);
 int nvfp4_moe_forward(const nvfp4_moe_weights* w, const void* x_bf16, int32_t T,
                       const int32_t* topk_ids, const float* topk_w, int32_t k, int32_t expert_start,

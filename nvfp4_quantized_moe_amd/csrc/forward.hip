@@ -31,8 +31,9 @@ extern "C" const char* nvfp4_status_string(int status) {
 extern "C" int nvfp4moe_version(void) { return 300; }
 
 extern "C" int32_t nvfp4_moe_tile_m(int32_t T, int32_t k, int32_t num_local) {
-  // prefill-shaped when the slot capacity averages >= 64 rows per local expert
-  return ((int64_t)T * k >= (int64_t)64 * num_local) ? 64 : 32;
+  // prefill-shaped (96-row tiles) when the slot capacity averages >= 64 rows
+  // per local expert, else decode-shaped (32-row tiles)
+  return ((int64_t)T * k >= (int64_t)64 * num_local) ? 96 : 32;
 }
 
 extern "C" size_t nvfp4_moe_ws_layout(int32_t T, int32_t k, int32_t hidden, int32_t inter, int32_t num_local,

@@ -482,7 +482,10 @@ using namespace nvfp4;
 // Row-tile heights with a kernel configuration (measured on MI355X over
 // decode- and prefill-shaped problems):
 //   32  decode-shaped batches: 4 waves, each 32 x 64, 3 stages in flight
-//   64  prefill-shaped: 8 waves, each 64 x 64, 4 stages in flight
+//   64  8 waves, each 64 x 64, 4 stages in flight
+//   96  prefill-shaped: 8 waves, each 96 x 64, 2 stages in flight (a third
+//       less weight decode per MFMA than 64 rows; with experts of ~170 or
+//       ~256 rows it pads no more than 64-row tiles do)
 //   128 large groups: 4 waves, each 128 x 64, 3 stages in flight
 int nvfp4_launch_grouped_gemm(const uint8_t* a_q, const uint8_t* a_sf, const int32_t* a_row_index,
                               const float* a_gs, const uint8_t* b_packed, const float* b_gs,
@@ -497,6 +500,7 @@ int nvfp4_launch_grouped_gemm(const uint8_t* a_q, const uint8_t* a_sf, const int
   switch (tile_m) {
     case 32: NVFP4_GEMM_CFG(1, 2, 4, 3);
     case 64: NVFP4_GEMM_CFG(2, 2, 8, 4);
+    case 96: NVFP4_GEMM_CFG(3, 2, 8, 2);
     case 128: NVFP4_GEMM_CFG(4, 2, 4, 3);
     default: return NVFP4_ERR_SHAPE;
   }
@@ -519,6 +523,7 @@ int nvfp4_launch_grouped_gemm_nvfp4(const uint8_t* a_q, const uint8_t* a_sf, con
   switch (tile_m) {
     case 32: NVFP4_GEMM_CFG(1, 2, 4, 3);
     case 64: NVFP4_GEMM_CFG(2, 2, 8, 4);
+    case 96: NVFP4_GEMM_CFG(3, 2, 8, 2);
     case 128: NVFP4_GEMM_CFG(4, 2, 4, 3);
     default: return NVFP4_ERR_SHAPE;
   }
@@ -533,7 +538,7 @@ extern "C" int nvfp4_grouped_gemm_silu_nvfp4(const uint8_t* a_q, const uint8_t* 
                                              void* stream) {
   if (dual_gs != 0 && dual_gs != 1) return NVFP4_ERR_ARG;
   if (num_local < 1 || rows_cap < 0 || N <= 0 || K <= 0 || K % kBK != 0 || N % 128 != 0) return NVFP4_ERR_SHAPE;
-  if (tile_m != 32 && tile_m != 64 && tile_m != 128) return NVFP4_ERR_SHAPE;
+  if (tile_m != 32 && tile_m != 64 && tile_m != 96 && tile_m != 128) return NVFP4_ERR_SHAPE;
   if (!a_q || !a_sf || !a_gs || !b_packed || !b_gs || !offsets || !tile_table || !out_gs || !d_q || !d_sf)
     return NVFP4_ERR_NULL;
   if (!nvfp4_aligned16(a_q) || !nvfp4_aligned16(a_sf) || !nvfp4_aligned16(b_packed) || !nvfp4_aligned16(d_q))
@@ -554,7 +559,7 @@ extern "C" int nvfp4_grouped_gemm(const uint8_t* a_q, const uint8_t* a_sf, const
   const bool silu = epilogue != NVFP4_EPI_BF16;
   if (num_local < 1 || rows_cap < 0 || N <= 0 || K <= 0 || K % kBK != 0 || N % 64 != 0) return NVFP4_ERR_SHAPE;
   if (silu && N % 128 != 0) return NVFP4_ERR_SHAPE;
-  if (tile_m != 32 && tile_m != 64 && tile_m != 128) return NVFP4_ERR_SHAPE;
+  if (tile_m != 32 && tile_m != 64 && tile_m != 96 && tile_m != 128) return NVFP4_ERR_SHAPE;
   if (!a_q || !a_sf || !a_gs || !b_packed || !b_gs || !offsets || !tile_table || !d) return NVFP4_ERR_NULL;
   if (silu && !amax_out) return NVFP4_ERR_NULL;
   if (!nvfp4_aligned16(a_q) || !nvfp4_aligned16(a_sf) || !nvfp4_aligned16(b_packed) || !nvfp4_aligned16(d))

@@ -214,7 +214,7 @@ GEMM_CASES = {
 
 
 @pytest.mark.parametrize("case", list(GEMM_CASES))
-@pytest.mark.parametrize("tile_m", [32, 64, 128])
+@pytest.mark.parametrize("tile_m", [32, 64, 96, 128])
 @pytest.mark.parametrize("epi", [0, 1, 2])
 def test_grouped_gemm(nv, case, tile_m, epi):
     L, N, K, T, counts, gather = GEMM_CASES[case]

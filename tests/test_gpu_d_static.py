@@ -109,7 +109,7 @@ GEMM_CASES = {
 
 
 @pytest.mark.parametrize("case", list(GEMM_CASES))
-@pytest.mark.parametrize("tile_m", [32, 64, 128])
+@pytest.mark.parametrize("tile_m", [32, 64, 96, 128])
 @pytest.mark.parametrize("dual", [0, 1])
 def test_gemm_silu_nvfp4(nv, case, tile_m, dual):
     L, N, K, T, counts = GEMM_CASES[case]

@@ -51,7 +51,7 @@ def test_status_strings_and_sizes():
     assert offs == sorted(offs) and all(o % 256 == 0 for o in offs)
     assert lay["end"] == nv.nvfp4_moe_ws_bytes(64, 8, 7168, 3072, 48)
     assert lay["y"] - lay["h_sf"] >= 512 * 3072 // 16
-    assert nv.nvfp4_moe_tile_m(64, 8, 48) == 32 and nv.nvfp4_moe_tile_m(8192, 8, 48) == 64
+    assert nv.nvfp4_moe_tile_m(64, 8, 48) == 32 and nv.nvfp4_moe_tile_m(8192, 8, 48) == 96
 
 
 def test_invalid_arguments_are_rejected_before_launch():
