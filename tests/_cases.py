@@ -59,6 +59,30 @@ def near_midpoint_blocks(seed, n_blocks=96):
     return bits, np.asarray(gss, np.float32)
 
 
+# midpoints between adjacent E4M3 values (codes c and c + 1): 0x01/0x02,
+# 0x07/0x08 (subnormal/normal), 0x30/0x31, 0x38/0x39, 0x3F/0x40 (binade),
+# 0x52/0x53, 0x7D/0x7E (top)
+E4M3_MIDPOINTS = [1.5 * 2.0 ** -9, 7.5 * 2.0 ** -9, 0.53125, 1.0625, 1.9375, 10.5, 432.0]
+
+
+def scale_tie_rows(rng, n_rows=4):
+    """BF16 rows with gs = 1 (one element 2688) whose blocks have their maximum
+    at 6 x an E4M3 midpoint (an exact tie of the block scale) or at the BF16
+    value just above or below it."""
+    rows = []
+    for _ in range(n_rows):
+        row = [2688.0] + [0.0] * 15
+        for m in E4M3_MIDPOINTS:
+            tie = W.bf16_bits(np.array([6.0 * m], np.float32))[0]       # exact in BF16
+            for bits in (tie, tie + 1, tie - 1):                          # the tie and its BF16 neighbours
+                b = float(np.array([int(bits) << 16], np.uint32).view(np.float32)[0])
+                blk = [b] + list(rng.uniform(-1, 1, 15) * b)
+                rng.shuffle(blk)
+                row += blk
+        rows.append(row)
+    return W.bf16_bits(np.asarray(rows, np.float32))
+
+
 def quant_case(name):
     """BF16 bit arrays for the quantizer parity cases."""
     rng = np.random.default_rng(zlib.crc32(name.encode()))
@@ -72,6 +96,8 @@ def quant_case(name):
         return W.bf16_bits(x)
     if name == "ties":
         return adversarial_rows(rng, 8)
+    if name == "scale_ties":
+        return scale_tie_rows(rng)
     if name == "subnormal":
         return W.bf16_bits((rng.standard_normal((4, 256)) * 2.0 ** -128).astype(np.float32))
     if name == "zeros":

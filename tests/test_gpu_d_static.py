@@ -54,7 +54,7 @@ def _own_gs(xb):
 
 # ------------------------------------------------------------- quantizer
 
-@pytest.mark.parametrize("case", ["tiny_x", "t3_outliers", "ties", "subnormal", "zeros", "ragged_rows"])
+@pytest.mark.parametrize("case", ["tiny_x", "t3_outliers", "ties", "scale_ties", "subnormal", "zeros", "ragged_rows"])
 @pytest.mark.parametrize("factor", [1 / 64.0, 1.0, 7.5])
 def test_quantize_static_bit_exact(nv, case, factor):
     xb = quant_case(case)

@@ -15,7 +15,7 @@ import pytest
 
 import oracle as O
 import workloads as W
-from _cases import adversarial_rows, near_midpoint_blocks
+from _cases import adversarial_rows, near_midpoint_blocks, quant_case
 
 GOLD = os.path.join(os.path.dirname(__file__), "golden")
 E4M3_POS = [Fraction(float(v)) for v in O.e4m3_decode(np.arange(0, 0x7F, dtype=np.uint8))]
@@ -285,3 +285,13 @@ def test_brute_force_near_midpoints():
         q, sf, _ = O.quantize(bits[b], gs=gs[b])
         bq, bsf, _ = brute_quantize(bits[b], gs=gs[b])
         assert np.array_equal(sf, bsf) and np.array_equal(q, bq), b
+
+
+def test_brute_force_scale_ties():
+    # block maxima at 6 x an E4M3 midpoint (gs = 1) and at the BF16 values next
+    # to it: the scale rounds to the even code on the tie, to the side elsewhere
+    xb = quant_case("scale_ties")
+    q, sf, gs = O.quantize(xb)
+    bq, bsf, bgs = brute_quantize(xb)
+    assert gs == 1.0 == bgs
+    assert np.array_equal(sf, bsf) and np.array_equal(q, bq)
