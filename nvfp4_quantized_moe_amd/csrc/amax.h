@@ -32,16 +32,19 @@ __device__ __forceinline__ void amax_block(const uint16_t* __restrict__ x, int64
 #pragma unroll
     for (int j = 0; j < 4; ++j) m = max(m, max(w[j] & 0x7FFFu, (w[j] >> 16) & 0x7FFFu));
   };
-  int64_t i = (int64_t)blk * blockDim.x + threadIdx.x;
-  // eight independent 16-byte loads in flight per thread (the maximum is order-free)
-  for (; i + 7 * stride < nv; i += 8 * stride) {
+  // eight independent 16-byte loads in flight per thread (the maximum is
+  // order-free); a load past the end re-reads the thread's first vector of
+  // the round, so every round issues all eight at once
+  for (int64_t i = (int64_t)blk * blockDim.x + threadIdx.x; i < nv; i += 8 * stride) {
     uint4 v[8];
 #pragma unroll
-    for (int u = 0; u < 8; ++u) v[u] = xv[i + u * stride];
+    for (int u = 0; u < 8; ++u) {
+      const int64_t k = i + u * stride;
+      v[u] = xv[k < nv ? k : i];
+    }
 #pragma unroll
     for (int u = 0; u < 8; ++u) fold(v[u]);
   }
-  for (; i < nv; i += stride) fold(xv[i]);
   m = wave_max_u32(m);
   __shared__ uint32_t red[16];
   const int nwaves = (int)(blockDim.x + 63) / 64;

@@ -336,7 +336,7 @@ __global__ __launch_bounds__(64 * WAVES) void grouped_gemm_kernel(
   // NVFP4 output: the threshold table of the fixed global scale of h
   uint16_t* h_tile = reinterpret_cast<uint16_t*>(lds + C::LDS);  // [BM][BN/2] BF16 h of one item
   const uint4* h_lut = reinterpret_cast<const uint4*>(lds + C::LDS + C::BM * C::BN);
-  if (EPI == kEpiSiluNvfp4) build_threshold_lut(out_gs[0], reinterpret_cast<uint16_t*>(lds + C::LDS + C::BM * C::BN),
+  if (EPI == kEpiSiluNvfp4) build_threshold_lut(out_gs[0], reinterpret_cast<uint32_t*>(lds + C::LDS + C::BM * C::BN),
                                                 tid, C::THREADS);
   __syncthreads();
 
@@ -442,7 +442,7 @@ static int launch_cfg(const uint8_t* a_q, const uint8_t* a_sf, const int32_t* a_
   const int n_out = EPI != NVFP4_EPI_BF16 ? N / 2 : N;
   const int bn_out = EPI != NVFP4_EPI_BF16 ? C::BN / 2 : C::BN;
   // NVFP4 output adds the BF16 h tile of one item and the threshold table
-  constexpr int lds_bytes = C::LDS + (EPI == kEpiSiluNvfp4 ? C::BM * C::BN + 128 * 16 : 0);
+  constexpr int lds_bytes = C::LDS + (EPI == kEpiSiluNvfp4 ? C::BM * C::BN + kLutBytes : 0);
   const int n_ntiles = (n_out + bn_out - 1) / bn_out;
   const int max_tiles = rows_cap / C::BM + num_local;
   const int64_t max_items = (int64_t)max_tiles * n_ntiles;

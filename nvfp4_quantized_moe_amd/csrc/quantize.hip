@@ -40,7 +40,7 @@ __global__ __launch_bounds__(256) void amax_kernel(const uint16_t* __restrict__ 
 // amax_in or the partials) and its threshold table in LDS.
 __device__ __forceinline__ float block_gs_and_lut(const float* __restrict__ gs_in, const float* __restrict__ amax_in,
                                                   const uint32_t* __restrict__ partial, int n_partial, int b,
-                                                  uint16_t* lut /* [128][8] in LDS */) {
+                                                  uint32_t* lut /* [128][8] in LDS */) {
   __shared__ uint32_t red[4];
   float gs;
   if (gs_in) {
@@ -75,8 +75,8 @@ __global__ __launch_bounds__(256) void quantize_kernel(const uint16_t* __restric
                                                        float* __restrict__ gs_out, uint8_t* __restrict__ q,
                                                        uint8_t* __restrict__ sf) {
   const int b = blockIdx.y;
-  __shared__ uint4 lut[128];
-  const float gs = block_gs_and_lut(gs_in, amax_in, partial, n_partial, b, reinterpret_cast<uint16_t*>(lut));
+  __shared__ uint4 lut[kLutWords / 4];
+  const float gs = block_gs_and_lut(gs_in, amax_in, partial, n_partial, b, reinterpret_cast<uint32_t*>(lut));
   if (gs_out && blockIdx.x == 0 && threadIdx.x == 0) gs_out[b] = gs;
   const double six_gs = 6.0 * (double)gs;  // exact
   int64_t rows = M;
@@ -124,12 +124,11 @@ static int quant_grid(int64_t nblk) {
   return (int)g;
 }
 
-// workgroups of the amax pass per tensor (fixed by the tensor size, at most
-// kAmaxGrid; a 117 MB tensor reads at 5.1 TB/s with 1024 of them, 6.3 TB/s
-// with 4096 on MI355X)
+// workgroups of the amax pass per tensor: one round of eight 16-byte loads
+// per thread, at most kAmaxGrid workgroups (fixed by the tensor size)
 constexpr int kAmaxGrid = 4096;
 static int amax_grid(int64_t per_batch) {
-  int64_t gx = (per_batch / 8 + 255) / 256;
+  int64_t gx = (per_batch / 8 + 256 * 8 - 1) / (256 * 8);
   if (gx > kAmaxGrid) gx = kAmaxGrid;
   if (gx < 1) gx = 1;
   return (int)gx;
