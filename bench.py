@@ -72,7 +72,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--config", default="prefill", choices=["prefill", "decode", "skewed"])
+    ap.add_argument("--config", default="prefill", choices=["prefill", "decode", "skewed", "quantize"],
+                    help="headline workload (quantize: only with --summarize-trace of a --quantize-only run)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--settle-ms", type=float, default=300.0,
                     help="untimed GPU time spent on the workload before the warmup steps, so that "
@@ -89,6 +90,9 @@ def main():
                          "profiles/ and exit")
     ap.add_argument("--trace-all", action="store_true",
                     help="with --summarize-trace: the trace is of the whole default run (no --no-decode)")
+    ap.add_argument("--quantize-only", action="store_true",
+                    help="time only the activation quantizer on the 4096 x 7168 tensor and print its object "
+                         "(for a kernel trace of the quantizer alone); not the benchmark line")
     ap.add_argument("--summarize-mfma", metavar="PMC_DIR",
                     help="write the MFMA counters of the L1 GEMM from a rocprofv3 --pmc csv run to "
                          "profiles/ and exit")
@@ -102,6 +106,8 @@ def main():
     if args.summarize_mfma:
         summarize_mfma(args.config, args.summarize_mfma)
         return
+    if args.config == "quantize" and not args.quantize_only:
+        raise SystemExit("bench.py: --config quantize only names the trace of a --quantize-only run")
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU; --gpus {args.gpus} is not supported "
               f"(expert-parallel sharding across GPUs is described in DESIGN.md, not built)", file=sys.stderr)
@@ -113,6 +119,9 @@ def main():
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.quantize_only:
+        print(json.dumps({"quantize": quantize_c1(nv, W, dev, args.settle_ms)}), flush=True)
+        return
     cfg = W.get_config(args.config)
     t0 = time.time()
     ids, w = W.make_router(cfg)
@@ -511,9 +520,27 @@ def summarize_trace(workload, d, all_workloads=False):
     if not f:
         raise SystemExit(f"no kernel_stats.csv under {d}")
     rows = list(csv.DictReader(open(f[0])))
-    name = "layer_all_workloads_kernel_trace.md" if all_workloads else f"layer_{workload}_kernel_trace.md"
+    if workload == "quantize":
+        name = "quantize_activation_kernel_trace.md"
+    else:
+        name = "layer_all_workloads_kernel_trace.md" if all_workloads else f"layer_{workload}_kernel_trace.md"
     path = os.path.join(PROFILE_DIR, name)
     with open(path, "w") as o:
+        if workload == "quantize":
+            o.write("# Kernel trace of the activation quantizer alone (4096 x 7168 BF16, Student-t(3) with 0.1% "
+                    "at +-2000): amax pass, then quantize\n\n")
+            o.write("Command, from the repository root on the MI355X box:\n\n```\n")
+            o.write(f"rocprofv3 --kernel-trace --stats -f csv -d {d} -o run -- python -u bench.py --quantize-only\n")
+            o.write(f"python bench.py --config quantize --summarize-trace {d}\n```\n\n")
+            o.write("The settle period (75 ms of back-to-back calls) and the 50 timed calls are all in the "
+                    "trace.\n\n")
+            o.write("| kernel | calls | total ms | avg us | min us | max us | share |\n|---|---|---|---|---|---|---|\n")
+            for r in rows:
+                o.write(f"| `{_short_kernel_name(r['Name'])}` | {r['Calls']} | {float(r['TotalDurationNs']) / 1e6:.3f} | "
+                        f"{float(r['AverageNs']) / 1e3:.1f} | {float(r['MinNs']) / 1e3:.1f} | "
+                        f"{float(r['MaxNs']) / 1e3:.1f} | {float(r['Percentage']):.1f}% |\n")
+            print(open(path).read())
+            return
         if all_workloads:
             o.write(f"# Kernel trace of the whole benchmark run ({workload} headline; decode, skewed and "
                     "static-scale objects beside it)\n\n")

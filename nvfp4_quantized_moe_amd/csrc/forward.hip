@@ -60,7 +60,9 @@ extern "C" size_t nvfp4_moe_ws_layout(int32_t T, int32_t k, int32_t hidden, int3
   put(NVFP4_WS_H_Q, cap * inter / 2);
   put(NVFP4_WS_H_SF, cap * inter / 16);
   put(NVFP4_WS_Y, cap * hidden * 2);
-  put(NVFP4_WS_QUANT_SCRATCH, nvfp4_quant_ws_layout(1));
+  // amax partials: of the quantizer's amax pass, or of the fused amax + route launch
+  const size_t qs = nvfp4_quant_ws_layout(1);
+  put(NVFP4_WS_QUANT_SCRATCH, qs > (size_t)kAmaxRouteMaxGrid * 4 ? qs : (size_t)kAmaxRouteMaxGrid * 4);
   o[NVFP4_WS_END] = p;
   if (off)
     for (int r = 0; r < NVFP4_WS_NREGIONS; ++r) off[r] = o[r];

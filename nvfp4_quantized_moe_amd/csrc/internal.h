@@ -45,6 +45,7 @@ int nvfp4_launch_fill_u32(uint32_t* p, int n, uint32_t v, hipStream_t stream);
 // Decode-sized batches (T*k <= 1024): one launch for the amax partials of x
 // (nvfp4_amax_route_grid(T*H) of them, in partial) and the whole route.
 int nvfp4_amax_route_grid(int64_t per);
+constexpr int kAmaxRouteMaxGrid = 1024;  // most partials nvfp4_amax_route_grid returns
 int nvfp4_launch_amax_route(const void* x_bf16, int64_t per, int64_t K, uint32_t* partial, uint32_t* clear,
                             int n_clear, const int32_t* topk_ids, const float* topk_w, int32_t T, int32_t k,
                             int32_t expert_start, int32_t num_local, int32_t tile_m, int32_t* counts,

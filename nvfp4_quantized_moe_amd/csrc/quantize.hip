@@ -29,7 +29,10 @@ __global__ void fill_u32_kernel(uint32_t* p, int n, uint32_t v) {
   if (i < n) p[i] = v;
 }
 
-__global__ __launch_bounds__(256) void amax_kernel(const uint16_t* __restrict__ x, int64_t per_batch,
+constexpr int kAmaxThreads = 1024;  // threads per amax workgroup
+constexpr int kQuantPerCu = 8;      // quantize workgroups per CU (at most the resident count)
+
+__global__ __launch_bounds__(kAmaxThreads) void amax_kernel(const uint16_t* __restrict__ x, int64_t per_batch,
                                                    const int32_t* __restrict__ rows_dev, int64_t K,
                                                    uint32_t* __restrict__ partial, uint32_t* __restrict__ clear,
                                                    int n_clear) {
@@ -114,7 +117,7 @@ static int quant_grid(int64_t nblk) {
         hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, reinterpret_cast<const void*>(quantize_kernel<false>), 256,
                                                      0) == hipSuccess &&
         n_cu > 0 && nb > 0)
-      resident = n_cu * nb;
+      resident = n_cu * (nb < kQuantPerCu ? nb : kQuantPerCu);
     else
       resident = 2048;
   }
@@ -125,10 +128,11 @@ static int quant_grid(int64_t nblk) {
 }
 
 // workgroups of the amax pass per tensor: one round of eight 16-byte loads
-// per thread, at most kAmaxGrid workgroups (fixed by the tensor size)
-constexpr int kAmaxGrid = 4096;
+// per thread, at most kAmaxGrid workgroups (fixed by the tensor size); every
+// quantize workgroup reduces the partials of its tensor, so they are few
+constexpr int kAmaxGrid = 512;
 static int amax_grid(int64_t per_batch) {
-  int64_t gx = (per_batch / 8 + 256 * 8 - 1) / (256 * 8);
+  int64_t gx = (per_batch / 8 + kAmaxThreads * 8 - 1) / (kAmaxThreads * 8);
   if (gx > kAmaxGrid) gx = kAmaxGrid;
   if (gx < 1) gx = 1;
   return (int)gx;
@@ -152,7 +156,7 @@ int nvfp4_launch_quantize(const void* x_bf16, int64_t B, int64_t M, int64_t K, c
   const int64_t per = M * K;
   const int gx = amax_grid(per);
   if (!amax_in) {
-    hipLaunchKernelGGL(amax_kernel, dim3((unsigned)gx, (unsigned)B), dim3(256), 0, stream, x, per, rows_dev, K,
+    hipLaunchKernelGGL(amax_kernel, dim3((unsigned)gx, (unsigned)B), dim3(kAmaxThreads), 0, stream, x, per, rows_dev, K,
                        partial, clear, clear ? n_clear : 0);
     NVFP4_CHECK_LAUNCH();
   } else if (clear && n_clear > 0) {

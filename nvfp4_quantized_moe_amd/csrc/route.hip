@@ -359,7 +359,7 @@ int nvfp4_launch_route(const int32_t* topk_ids, const float* topk_w, int32_t T, 
 
 int nvfp4_amax_route_grid(int64_t per) {
   int64_t gx = (per / 8 + kScanThreads - 1) / kScanThreads;
-  if (gx > 1024) gx = 1024;
+  if (gx > kAmaxRouteMaxGrid) gx = kAmaxRouteMaxGrid;
   if (gx < 1) gx = 1;
   return (int)gx;
 }
