@@ -5,6 +5,8 @@
 
 namespace nvfp4 {
 
+constexpr int kAmaxThreads = 1024;  // threads per workgroup of the amax passes over large tensors
+
 // Workgroup blk of nblk over tensor b: partial[b * nblk + blk] = max |x| over
 // the workgroup's grid-stride share of the first min(per_batch, rows_dev[0] * K)
 // elements of x[b], as float32 bits (|x| >= 0, so the unsigned order of the

@@ -137,14 +137,19 @@ extern "C" int nvfp4_moe_forward(const nvfp4_moe_weights* w, const void* x_bf16,
     if ((st = nvfp4_launch_quantize_from_partials(x_bf16, T, H, qws, gx, x_q, x_sf, &scalars[0], stream)))
       return st;
   } else {
-    // a1/a2: quantize x with its own global scale; the amax pass also zeroes the
-    // scalars (gs_x, amax_h, gs_h, reserved) before anything reads them
-    if ((st = nvfp4_launch_quantize(x_bf16, 1, T, H, nullptr, nullptr, x_q, x_sf, &scalars[0], qws,
-                                    reinterpret_cast<uint32_t*>(scalars), 4, stream)))
+    // a1 (amax partials of x, which also zero the scalars gs_x, amax_h, gs_h,
+    // reserved) and a3's per-chunk histograms share one launch; then a2, then
+    // the rest of a3
+    if ((st = nvfp4_launch_amax_count(x_bf16, (int64_t)T * H, H, reinterpret_cast<uint32_t*>(qws),
+                                      reinterpret_cast<uint32_t*>(scalars), 4, topk_ids, T, k, expert_start, L,
+                                      route_ws, stream)))
       return st;
-    // a3: route
-    if ((st = nvfp4_launch_route(topk_ids, topk_w, T, k, expert_start, L, tile_m, counts, offsets, slot_token,
-                                 slot_expert, slot_weight, token_slot, tiles, route_ws, stream)))
+    if ((st = nvfp4_launch_quantize_from_partials(x_bf16, T, H, qws, nvfp4_amax_grid((int64_t)T * H), x_q, x_sf,
+                                                  &scalars[0], stream)))
+      return st;
+    if ((st = nvfp4_launch_route_from_counts(topk_ids, topk_w, T, k, expert_start, L, tile_m, counts, offsets,
+                                             slot_token, slot_expert, slot_weight, token_slot, tiles, route_ws,
+                                             stream)))
       return st;
   }
   if (cap > 0) {

@@ -51,5 +51,16 @@ int nvfp4_launch_amax_route(const void* x_bf16, int64_t per, int64_t K, uint32_t
                             int32_t expert_start, int32_t num_local, int32_t tile_m, int32_t* counts,
                             int32_t* offsets, int32_t* slot_token, int32_t* slot_expert, float* slot_weight,
                             int32_t* token_slot, int32_t* tile_table, hipStream_t stream);
+// Larger batches: one launch for the amax partials of x (nvfp4_amax_grid(T*H)
+// of them, in partial) and the route's per-chunk histograms (in route_ws);
+// nvfp4_launch_route_from_counts then finishes the route.
+int nvfp4_amax_grid(int64_t per);
+int nvfp4_launch_amax_count(const void* x_bf16, int64_t per, int64_t K, uint32_t* partial, uint32_t* clear,
+                            int n_clear, const int32_t* topk_ids, int32_t T, int32_t k, int32_t expert_start,
+                            int32_t num_local, void* route_ws, hipStream_t stream);
+int nvfp4_launch_route_from_counts(const int32_t* topk_ids, const float* topk_w, int32_t T, int32_t k,
+                                   int32_t expert_start, int32_t num_local, int32_t tile_m, int32_t* counts,
+                                   int32_t* offsets, int32_t* slot_token, int32_t* slot_expert, float* slot_weight,
+                                   int32_t* token_slot, int32_t* tile_table, void* route_ws, hipStream_t stream);
 int nvfp4_launch_quantize_from_partials(const void* x_bf16, int64_t M, int64_t K, const void* ws, int n_partial,
                                         uint8_t* q, uint8_t* sf, float* gs_out, hipStream_t stream);

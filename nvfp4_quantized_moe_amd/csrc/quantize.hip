@@ -29,7 +29,6 @@ __global__ void fill_u32_kernel(uint32_t* p, int n, uint32_t v) {
   if (i < n) p[i] = v;
 }
 
-constexpr int kAmaxThreads = 1024;  // threads per amax workgroup
 constexpr int kQuantPerCu = 8;      // quantize workgroups per CU (at most the resident count)
 
 __global__ __launch_bounds__(kAmaxThreads) void amax_kernel(const uint16_t* __restrict__ x, int64_t per_batch,
@@ -131,7 +130,7 @@ static int quant_grid(int64_t nblk) {
 // per thread, at most kAmaxGrid workgroups (fixed by the tensor size); every
 // quantize workgroup reduces the partials of its tensor, so they are few
 constexpr int kAmaxGrid = 512;
-static int amax_grid(int64_t per_batch) {
+int nvfp4_amax_grid(int64_t per_batch) {
   int64_t gx = (per_batch / 8 + kAmaxThreads * 8 - 1) / (kAmaxThreads * 8);
   if (gx > kAmaxGrid) gx = kAmaxGrid;
   if (gx < 1) gx = 1;
@@ -154,7 +153,7 @@ int nvfp4_launch_quantize(const void* x_bf16, int64_t B, int64_t M, int64_t K, c
   uint32_t* partial = reinterpret_cast<uint32_t*>(ws);
   const uint16_t* x = reinterpret_cast<const uint16_t*>(x_bf16);
   const int64_t per = M * K;
-  const int gx = amax_grid(per);
+  const int gx = nvfp4_amax_grid(per);
   if (!amax_in) {
     hipLaunchKernelGGL(amax_kernel, dim3((unsigned)gx, (unsigned)B), dim3(kAmaxThreads), 0, stream, x, per, rows_dev, K,
                        partial, clear, clear ? n_clear : 0);

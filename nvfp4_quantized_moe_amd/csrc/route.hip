@@ -25,13 +25,13 @@ namespace nvfp4 {
 
 constexpr int kScanThreads = 1024;
 
-__global__ __launch_bounds__(256) void route_count_kernel(const int32_t* __restrict__ ids, int32_t n,
-                                                          int32_t start, int32_t L,
-                                                          int32_t* __restrict__ chunk_counts) {
+// Histogram of chunk `chunk`'s local expert ids (any workgroup size).
+__device__ __forceinline__ void route_count_body(const int32_t* __restrict__ ids, int32_t n, int32_t start, int32_t L,
+                                                 int32_t* __restrict__ chunk_counts, int chunk) {
   extern __shared__ int32_t hist[];
   for (int e = threadIdx.x; e < L; e += blockDim.x) hist[e] = 0;
   __syncthreads();
-  const int base = blockIdx.x * kRouteChunk;
+  const int base = chunk * kRouteChunk;
   for (int i = threadIdx.x; i < kRouteChunk; i += blockDim.x) {
     int f = base + i;
     if (f < n) {
@@ -40,7 +40,27 @@ __global__ __launch_bounds__(256) void route_count_kernel(const int32_t* __restr
     }
   }
   __syncthreads();
-  for (int e = threadIdx.x; e < L; e += blockDim.x) chunk_counts[(size_t)blockIdx.x * L + e] = hist[e];
+  for (int e = threadIdx.x; e < L; e += blockDim.x) chunk_counts[(size_t)chunk * L + e] = hist[e];
+}
+
+__global__ __launch_bounds__(256) void route_count_kernel(const int32_t* __restrict__ ids, int32_t n,
+                                                          int32_t start, int32_t L,
+                                                          int32_t* __restrict__ chunk_counts) {
+  route_count_body(ids, n, start, L, chunk_counts, blockIdx.x);
+}
+
+// The layer's first launch for larger batches: workgroups [0, gx) take the
+// amax partials of the activation tensor, the others the per-chunk
+// histograms of the route. The two steps are independent, so they share one
+// launch.
+__global__ __launch_bounds__(kAmaxThreads) void amax_count_kernel(
+    const uint16_t* __restrict__ x, int64_t per, int64_t K, uint32_t* __restrict__ partial, int gx,
+    uint32_t* __restrict__ clear, int n_clear, const int32_t* __restrict__ ids, int32_t n, int32_t start, int32_t L,
+    int32_t* __restrict__ chunk_counts) {
+  if ((int)blockIdx.x < gx)
+    amax_block(x, per, nullptr, K, partial, clear, n_clear, 0, blockIdx.x, gx);
+  else
+    route_count_body(ids, n, start, L, chunk_counts, (int)blockIdx.x - gx);
 }
 
 // Exclusive prefix sum over a 1024-thread workgroup; *total receives the sum.
@@ -319,30 +339,23 @@ size_t nvfp4_route_ws(int32_t T, int32_t k, int32_t num_local) {
   return 2 * per + 256;
 }
 
-int nvfp4_launch_route(const int32_t* topk_ids, const float* topk_w, int32_t T, int32_t k, int32_t expert_start,
-                       int32_t num_local, int32_t tile_m, int32_t* counts, int32_t* offsets, int32_t* slot_token,
-                       int32_t* slot_expert, float* slot_weight, int32_t* token_slot, int32_t* tile_table,
-                       void* ws, hipStream_t stream) {
+static int route_nbits(int L) {
+  int nbits = 1;
+  while ((1 << nbits) <= L) ++nbits;  // keys 0..L must be distinct
+  return nbits;
+}
+
+// Scan and scatter of a route whose per-chunk histograms are in ws (T*k > kScanThreads).
+int nvfp4_launch_route_from_counts(const int32_t* topk_ids, const float* topk_w, int32_t T, int32_t k,
+                                   int32_t expert_start, int32_t num_local, int32_t tile_m, int32_t* counts,
+                                   int32_t* offsets, int32_t* slot_token, int32_t* slot_expert, float* slot_weight,
+                                   int32_t* token_slot, int32_t* tile_table, void* ws, hipStream_t stream) {
   const int n = T * k;
   const int nchunks = route_nchunks(T, k);
   const int L = num_local;
   size_t per = nvfp4_align256((size_t)nchunks * L * 4);
   int32_t* chunk_counts = reinterpret_cast<int32_t*>(ws);
   int32_t* bases = reinterpret_cast<int32_t*>(reinterpret_cast<char*>(ws) + per);
-  int nbits = 1;
-  while ((1 << nbits) <= L) ++nbits;  // keys 0..L must be distinct
-  if (n <= kScanThreads) {
-    hipLaunchKernelGGL(route_small_kernel, dim3(1), dim3(kScanThreads), 3 * L * 4, stream, topk_ids, topk_w, n, k,
-                       expert_start, L, tile_m, nbits, counts, offsets, slot_token, slot_expert, slot_weight,
-                       token_slot, tile_table);
-    NVFP4_CHECK_LAUNCH();
-    return NVFP4_OK;
-  }
-  if (nchunks > 0) {
-    hipLaunchKernelGGL(route_count_kernel, dim3(nchunks), dim3(256), L * 4, stream, topk_ids, n, expert_start, L,
-                       chunk_counts);
-    NVFP4_CHECK_LAUNCH();
-  }
   // stage the per-chunk histograms in LDS when everything fits in 64 KB
   const int stage_cc = ((int64_t)nchunks * L + 3 * L) * 4 <= 64 * 1024 ? 1 : 0;
   const size_t lds = (size_t)(3 * L + (stage_cc ? nchunks * L : 0)) * 4;
@@ -351,9 +364,45 @@ int nvfp4_launch_route(const int32_t* topk_ids, const float* topk_w, int32_t T, 
   NVFP4_CHECK_LAUNCH();
   if (nchunks > 0) {
     hipLaunchKernelGGL(route_scatter_kernel, dim3(nchunks), dim3(256), L * 4, stream, topk_ids, topk_w, n, k,
-                       expert_start, L, nbits, bases, offsets, slot_token, slot_expert, slot_weight, token_slot);
+                       expert_start, L, route_nbits(L), bases, offsets, slot_token, slot_expert, slot_weight,
+                       token_slot);
     NVFP4_CHECK_LAUNCH();
   }
+  return NVFP4_OK;
+}
+
+int nvfp4_launch_route(const int32_t* topk_ids, const float* topk_w, int32_t T, int32_t k, int32_t expert_start,
+                       int32_t num_local, int32_t tile_m, int32_t* counts, int32_t* offsets, int32_t* slot_token,
+                       int32_t* slot_expert, float* slot_weight, int32_t* token_slot, int32_t* tile_table,
+                       void* ws, hipStream_t stream) {
+  const int n = T * k;
+  const int nchunks = route_nchunks(T, k);
+  const int L = num_local;
+  if (n <= kScanThreads) {
+    hipLaunchKernelGGL(route_small_kernel, dim3(1), dim3(kScanThreads), 3 * L * 4, stream, topk_ids, topk_w, n, k,
+                       expert_start, L, tile_m, route_nbits(L), counts, offsets, slot_token, slot_expert,
+                       slot_weight, token_slot, tile_table);
+    NVFP4_CHECK_LAUNCH();
+    return NVFP4_OK;
+  }
+  if (nchunks > 0) {
+    hipLaunchKernelGGL(route_count_kernel, dim3(nchunks), dim3(256), L * 4, stream, topk_ids, n, expert_start, L,
+                       reinterpret_cast<int32_t*>(ws));
+    NVFP4_CHECK_LAUNCH();
+  }
+  return nvfp4_launch_route_from_counts(topk_ids, topk_w, T, k, expert_start, num_local, tile_m, counts, offsets,
+                                        slot_token, slot_expert, slot_weight, token_slot, tile_table, ws, stream);
+}
+
+int nvfp4_launch_amax_count(const void* x_bf16, int64_t per, int64_t K, uint32_t* partial, uint32_t* clear,
+                            int n_clear, const int32_t* topk_ids, int32_t T, int32_t k, int32_t expert_start,
+                            int32_t num_local, void* route_ws, hipStream_t stream) {
+  const int gx = nvfp4_amax_grid(per);
+  const int nchunks = route_nchunks(T, k);
+  hipLaunchKernelGGL(amax_count_kernel, dim3((unsigned)(gx + nchunks)), dim3(kAmaxThreads), num_local * 4, stream,
+                     reinterpret_cast<const uint16_t*>(x_bf16), per, K, partial, gx, clear, n_clear, topk_ids, T * k,
+                     expert_start, num_local, reinterpret_cast<int32_t*>(route_ws));
+  NVFP4_CHECK_LAUNCH();
   return NVFP4_OK;
 }
 
@@ -372,8 +421,7 @@ int nvfp4_launch_amax_route(const void* x_bf16, int64_t per, int64_t K, uint32_t
   const int n = T * k;
   if (n > kScanThreads) return NVFP4_ERR_SHAPE;
   const int L = num_local;
-  int nbits = 1;
-  while ((1 << nbits) <= L) ++nbits;
+  const int nbits = route_nbits(L);
   const int gx = nvfp4_amax_route_grid(per);
   hipLaunchKernelGGL(amax_route_kernel, dim3(gx + 1), dim3(kScanThreads), 3 * L * 4, stream,
                      reinterpret_cast<const uint16_t*>(x_bf16), per, K, partial, gx, clear, n_clear, topk_ids,
