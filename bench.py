@@ -559,6 +559,20 @@ def summarize_trace(workload, d, all_workloads=False):
             o.write(f"| `{_short_kernel_name(r['Name'])}` | {r['Calls']} | {float(r['TotalDurationNs']) / 1e6:.3f} | "
                     f"{float(r['AverageNs']) / 1e3:.1f} | {float(r['MinNs']) / 1e3:.1f} | "
                     f"{float(r['MaxNs']) / 1e3:.1f} | {float(r['Percentage']):.1f}% |\n")
+        if not all_workloads:
+            # the benchmark's last GPU work is the L1 GEMM timed alone with events (5 launches in the command
+            # above): the same launches, read from the per-dispatch trace
+            t = glob.glob(os.path.join(d, "**", "*kernel_trace.csv"), recursive=True)
+            if t:
+                l1 = sorted((int(r["Start_Timestamp"]), int(r["End_Timestamp"]))
+                            for r in csv.DictReader(open(t[0]))
+                            if "grouped_gemm_kernel<" in r["Kernel_Name"]
+                            and _short_kernel_name(r["Kernel_Name"]).rstrip(">").endswith(", 1"))
+                last = [(e - b) / 1e3 for b, e in l1[-5:]]
+                if last:
+                    o.write(f"\nL1 GEMM, the last {len(last)} dispatches (the launches the benchmark times with HIP "
+                            f"events for `roofline.avg_launch_ms`): {np.mean(last):.1f} us on average "
+                            f"(min {min(last):.1f}, max {max(last):.1f}).\n")
     print(open(path).read())
 
 

@@ -49,7 +49,7 @@ __device__ __forceinline__ uint32_t e4m3_encode_rne_sat(double v) {
 }
 
 // Largest BF16 value <= t (t > 0, double), as its bit pattern, and whether it equals t.
-__device__ __forceinline__ uint32_t bf16_round_down_bits(double t, bool* exact) {
+__host__ __device__ __forceinline__ uint32_t bf16_round_down_bits(double t, bool* exact) {
   int e;
   (void)__builtin_frexp(t, &e);                         // t in [2^(e-1), 2^e)
   int ulp_exp = e - 8;                                  // BF16: 8 significant bits
@@ -57,7 +57,7 @@ __device__ __forceinline__ uint32_t bf16_round_down_bits(double t, bool* exact) 
   double n = __builtin_floor(__builtin_ldexp(t, -ulp_exp));
   double rd = __builtin_ldexp(n, ulp_exp);              // exactly representable in BF16
   *exact = (rd == t);
-  return __float_as_uint((float)rd) >> 16;
+  return __builtin_bit_cast(uint32_t, (float)rd) >> 16;
 }
 
 __device__ __forceinline__ float wave_max(float v) {

@@ -12,9 +12,9 @@
 // most 5 significant bits, so the quotient of a BF16 by 6*gs that is not one
 // of them lies >= 2^-32 away relative; float64 rounding cannot move it across).
 // The magnitude is a count of E2M1 midpoints c*E4M3(sf)*gs passed; each
-// midpoint is exact in float64 (3 x 4 x 24 significant bits) and is turned
-// into a BF16 bit-pattern threshold U such that |x| passes it iff
-// bits(|x|) > U.
+// midpoint (3 x 4 x 24 significant bits) is turned exactly, from a float32
+// product and its fma residual, into a BF16 bit-pattern threshold U such that
+// |x| passes it iff bits(|x|) > U.
 //
 // Two elements per 32-bit word: a BF16 magnitude a has bits <= 0x7FFF, so
 // with C = 0x7FFF - U (<= 0x7FFF) the sum a + C stays below 2^16 and has bit
@@ -38,6 +38,24 @@ __host__ __device__ __forceinline__ uint32_t threshold_offset_pair(uint32_t u) {
   return c | (c << 16);
 }
 
+// Largest BF16 value <= m * gs (m a float32 with at most 7 significant bits,
+// gs > 0 finite, both positive), as its bit pattern, and whether it equals
+// m * gs. The float32 product hi and its exact residual fma(m, gs, -hi) give
+// the real product; hi with its low 16 bits cleared is a BF16 value <= hi,
+// and below the real product unless it equals hi and the residual is
+// negative. Products under 2^-100 (where the residual may not be exact) or
+// past the float32 range take the float64 route.
+__host__ __device__ __forceinline__ uint32_t bf16_round_down_product(float m, float gs, bool* exact) {
+  const float hi = m * gs;
+  if (!(hi >= 0x1p-100f && hi <= 0x1.fffffep127f))
+    return bf16_round_down_bits((double)m * (double)gs, exact);  // exact in float64
+  const float lo = __builtin_fmaf(m, gs, -hi);
+  const uint32_t hb = __builtin_bit_cast(uint32_t, hi);
+  const bool on_bf16 = (hb & 0xFFFFu) == 0u;
+  *exact = on_bf16 && lo == 0.0f;
+  return (hb >> 16) - (on_bf16 && lo < 0.0f ? 1u : 0u);
+}
+
 // Threshold table for global scale gs: entry `code`, word j < 7, holds the
 // offset pair of E2M1 midpoint j of that scale code (all zero, so that
 // nothing passes, for code 0 and for gs <= 0 or NaN). Threads tid = 0 ..
@@ -49,12 +67,12 @@ __device__ __forceinline__ void build_threshold_lut(float gs, uint32_t* lut, int
     if (j < 7 && code > 0 && code <= 0x7E && gs > 0.0f) {
       // E2M1 midpoint j (0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5); an exact tie
       // rounds up at the odd j (0.75, 1.75, 3.5: the upper code is even)
-      const double mid = j < 4 ? 0.25 + 0.5 * j : (j == 6 ? 5.0 : j - 1.5);
+      const float mid = j < 4 ? 0.25f + 0.5f * j : (j == 6 ? 5.0f : j - 1.5f);
       const bool tie_up = (j & 1) != 0;
-      const double step = (double)e4m3_to_f32((uint32_t)code) * (double)gs;  // exact
-      const double thr = mid * step;                                          // exact
+      // midpoint times the scale value: 3 x 4 significant bits, exact in float32
+      const float ms = mid * e4m3_to_f32((uint32_t)code);
       bool exact;
-      const uint32_t rd = bf16_round_down_bits(thr, &exact);
+      const uint32_t rd = bf16_round_down_product(ms, gs, &exact);
       // strict midpoint: |x| > thr  <=>  bits > bits(RD(thr))
       // tie-up midpoint: |x| >= thr <=>  bits > bits(RU(thr)) - 1
       u = (tie_up && exact) ? rd - 1u : rd;
