@@ -18,8 +18,11 @@
  *
  * Conventions for every entry point:
  *   - Pointers are device pointers unless marked (host). The caller owns all
- *     memory; the library never allocates, frees, caches or keeps state, and
- *     reads no environment variables.
+ *     memory; the library never allocates or frees memory, holds no data from
+ *     one call to the next, and reads no environment variables. Its only
+ *     process-wide state is launch sizes that depend on the device alone (CU
+ *     count times resident workgroups per CU), queried on the first call on
+ *     each device and kept per device.
  *   - Calls are asynchronous on `stream` (a hipStream_t; NULL = the default
  *     stream) and never synchronize with the host.
  *   - Arguments are validated on the host before anything is launched; a

@@ -447,12 +447,15 @@ static int launch_cfg(const uint8_t* a_q, const uint8_t* a_sf, const int32_t* a_
   const int max_tiles = rows_cap / C::BM + num_local;
   const int64_t max_items = (int64_t)max_tiles * n_ntiles;
   auto kern = grouped_gemm_kernel<SUB_M, SUB_N, WAVES, P, EPI>;
-  // resident workgroups per CU and the CU count (host queries, once per instance)
-  static int per_cu = 0, n_cu = 0;
-  if (per_cu == 0) {
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess ||
-        hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n_cu < 1)
+  // resident workgroups on the device: CU count x workgroups per CU (host
+  // queries, once per device and configuration)
+  static std::atomic<int> resident_wgs[kMaxDevices];
+  const int dev = nvfp4_current_device();
+  if (dev < 0) return NVFP4_ERR_HIP;
+  int resident = resident_wgs[dev].load(std::memory_order_relaxed);
+  if (resident == 0) {
+    int n_cu = 0;
+    if (hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n_cu < 1)
       return NVFP4_ERR_HIP;
     if (lds_bytes > 64 * 1024 &&
         hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
@@ -462,9 +465,10 @@ static int launch_cfg(const uint8_t* a_q, const uint8_t* a_sf, const int32_t* a_
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, reinterpret_cast<const void*>(kern), C::THREADS,
                                                      lds_bytes) != hipSuccess || nb < 1)
       nb = 1;
-    per_cu = nb;
+    resident = n_cu * nb;
+    resident_wgs[dev].store(resident, std::memory_order_relaxed);
   }
-  int64_t grid = (int64_t)n_cu * per_cu;
+  int64_t grid = resident;
   if (grid > max_items) grid = max_items;
   if (grid >= kXcds) grid -= grid % kXcds;
   if (grid < 1) grid = 1;

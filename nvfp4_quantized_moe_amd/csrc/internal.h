@@ -4,6 +4,18 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include <atomic>
+
+// Launch sizes that depend only on the device (CU count times resident
+// workgroups per CU) are queried once per device and kept in a table of
+// atomics, one slot per device: concurrent first calls compute the same value,
+// and a value is read or written whole. 0 = not yet known.
+constexpr int kMaxDevices = 64;
+inline int nvfp4_current_device() {
+  int dev = 0;
+  return (hipGetDevice(&dev) == hipSuccess && dev >= 0 && dev < kMaxDevices) ? dev : -1;
+}
+
 // Quantizer workspace: per-workgroup amax partials, uint32 [B][1024].
 size_t nvfp4_quant_ws_layout(int64_t B);
 // rows_dev (optional, device): the number of valid rows is min(M, rows_dev[0]).

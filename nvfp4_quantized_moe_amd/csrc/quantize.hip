@@ -106,19 +106,23 @@ using namespace nvfp4;
 
 // Workgroups of the quantize kernel: one per 256 blocks, at most as many as
 // the device holds at once (CU count x resident workgroups per CU, queried
-// once), so the grid-stride loop runs in a single round.
+// once per device), so the grid-stride loop runs in a single round.
+static std::atomic<int> g_quant_resident[kMaxDevices];
+
 static int quant_grid(int64_t nblk) {
-  static int resident = 0;
+  const int dev = nvfp4_current_device();
+  int resident = dev >= 0 ? g_quant_resident[dev].load(std::memory_order_relaxed) : 0;
   if (resident == 0) {
-    int dev = 0, n_cu = 0, nb = 0;
-    if (hipGetDevice(&dev) == hipSuccess &&
-        hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess &&
+    int n_cu = 0, nb = 0;
+    if (dev >= 0 && hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess &&
         hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, reinterpret_cast<const void*>(quantize_kernel<false>), 256,
                                                      0) == hipSuccess &&
-        n_cu > 0 && nb > 0)
+        n_cu > 0 && nb > 0) {
       resident = n_cu * (nb < kQuantPerCu ? nb : kQuantPerCu);
-    else
+      g_quant_resident[dev].store(resident, std::memory_order_relaxed);
+    } else {
       resident = 2048;
+    }
   }
   int64_t g = (nblk + 255) / 256;
   if (g > resident) g = resident;
