@@ -95,8 +95,29 @@ def _stream():
 
 
 def _dev(t, dtype, name):
+    """t must be a contiguous tensor of dtype on the current device (the
+    device whose current stream the call is issued on)."""
     if not (t.is_cuda and t.dtype == dtype and t.is_contiguous()):
         raise ValueError(f"{name}: expected a contiguous CUDA {dtype} tensor, got {t.dtype} on {t.device}")
+    if t.device.index != torch.cuda.current_device():
+        raise ValueError(f"{name}: on {t.device}, but the current device is cuda:{torch.cuda.current_device()}")
+    return t
+
+
+def _buf(t, dtype, numel, name):
+    """A caller-provided buffer (or None): as _dev, holding at least numel
+    elements, since the library sees only its address."""
+    if t is None:
+        return None
+    _dev(t, dtype, name)
+    if t.numel() < numel:
+        raise ValueError(f"{name}: needs at least {numel} elements, got {t.numel()}")
+    return t
+
+
+def _shape(t, shape, name):
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name}: expected shape {tuple(shape)}, got {tuple(t.shape)}")
     return t
 
 
@@ -117,15 +138,17 @@ def nvfp4_quantize_ws_bytes(B, M, K) -> int:
 def nvfp4_quantize(x, amax_in=None, q=None, sf=None, gs=None, ws=None):
     """x: BF16 [M, K] or [B, M, K] -> (q uint8 [..., K/2], sf uint8 [..., K/16], gs float32 [B])."""
     _dev(x, torch.bfloat16, "x")
+    if x.dim() not in (2, 3):
+        raise ValueError(f"x: expected [M, K] or [B, M, K], got shape {tuple(x.shape)}")
     batched = x.dim() == 3
     B, M, K = (x.shape if batched else (1, *x.shape))
     dev = x.device
-    q = torch.empty((B, M, K // 2), dtype=torch.uint8, device=dev) if q is None else q
-    sf = torch.empty((B, M, K // 16), dtype=torch.uint8, device=dev) if sf is None else sf
-    gs = torch.empty((B,), dtype=torch.float32, device=dev) if gs is None else gs
-    ws = _alloc_ws(nvfp4_quantize_ws_bytes(B, M, K), dev) if ws is None else ws
-    if amax_in is not None:
-        _dev(amax_in, torch.float32, "amax_in")
+    q = torch.empty((B, M, K // 2), dtype=torch.uint8, device=dev) if q is None else _buf(q, torch.uint8, B * M * K // 2, "q")
+    sf = (torch.empty((B, M, K // 16), dtype=torch.uint8, device=dev) if sf is None
+          else _buf(sf, torch.uint8, B * M * K // 16, "sf"))
+    gs = torch.empty((B,), dtype=torch.float32, device=dev) if gs is None else _buf(gs, torch.float32, B, "gs")
+    ws = _alloc_ws(nvfp4_quantize_ws_bytes(B, M, K), dev) if ws is None else _buf(ws, torch.uint8, 0, "ws")
+    _buf(amax_in, torch.float32, B, "amax_in")
     _check(_quantize(_ptr(x), B, M, K, _ptr(amax_in), _ptr(q), _ptr(sf), _ptr(gs), _ptr(ws),
                      ws.numel(), _stream()), "nvfp4_quantize")
     if not batched:
@@ -137,12 +160,15 @@ def nvfp4_quantize_static(x, gs, q=None, sf=None):
     """x: BF16 [M, K] or [B, M, K] quantized with the fixed global scales gs
     (float32 [B], device) -> (q uint8 [..., K/2], sf uint8 [..., K/16])."""
     _dev(x, torch.bfloat16, "x")
-    _dev(gs, torch.float32, "gs")
+    if x.dim() not in (2, 3):
+        raise ValueError(f"x: expected [M, K] or [B, M, K], got shape {tuple(x.shape)}")
     batched = x.dim() == 3
     B, M, K = (x.shape if batched else (1, *x.shape))
+    _buf(gs, torch.float32, B, "gs")
     dev = x.device
-    q = torch.empty((B, M, K // 2), dtype=torch.uint8, device=dev) if q is None else q
-    sf = torch.empty((B, M, K // 16), dtype=torch.uint8, device=dev) if sf is None else sf
+    q = torch.empty((B, M, K // 2), dtype=torch.uint8, device=dev) if q is None else _buf(q, torch.uint8, B * M * K // 2, "q")
+    sf = (torch.empty((B, M, K // 16), dtype=torch.uint8, device=dev) if sf is None
+          else _buf(sf, torch.uint8, B * M * K // 16, "sf"))
     _check(_quantize_static(_ptr(x), B, M, K, _ptr(gs), _ptr(q), _ptr(sf), _stream()), "nvfp4_quantize_static")
     if not batched:
         return q[0], sf[0]
@@ -163,6 +189,7 @@ def moe_route_slots(topk_ids, topk_w, expert_start, num_local, tile_m):
     _dev(topk_ids, torch.int32, "topk_ids")
     _dev(topk_w, torch.float32, "topk_w")
     T, k = topk_ids.shape
+    _shape(topk_w, (T, k), "topk_w")
     dev = topk_ids.device
     cap = T * k
     i32 = dict(dtype=torch.int32, device=dev)
@@ -197,19 +224,42 @@ def nvfp4_pack_weights(q, sf, out=None):
         raise ValueError(f"sf shape {tuple(sf.shape)} does not match q {tuple(q.shape)}")
     if N % 32 or K % 128:
         raise ValueError(f"packing needs N % 32 == 0 and K % 128 == 0, got N={N}, K={K}")
-    out = torch.empty((B, N // 32, K // 128, 2304), dtype=torch.uint8, device=q.device) if out is None else out
+    out = (torch.empty((B, N // 32, K // 128, 2304), dtype=torch.uint8, device=q.device) if out is None
+           else _buf(out, torch.uint8, B * N * K // 32 * 18, "out"))
     _check(_pack(_ptr(q), _ptr(sf), B, N, K, _ptr(out), _stream()), "nvfp4_pack_weights")
     return out
 
 
+def _check_gemm_operands(a_q, a_sf, a_row_index, a_gs, b_gs, offsets, tile_table, rows_cap, tile_m, L, K, n_b_gs):
+    _dev(a_q, torch.uint8, "a_q")
+    _dev(a_sf, torch.uint8, "a_sf")
+    if a_q.dim() != 2 or a_q.shape[1] != K // 2 or tuple(a_sf.shape) != (a_q.shape[0], K // 16):
+        raise ValueError(f"a_q {tuple(a_q.shape)} / a_sf {tuple(a_sf.shape)}: expected [rows, {K // 2}] / "
+                         f"[rows, {K // 16}]")
+    # rows read: slot s, or a_row_index[s], for the slots below offsets[L] (device data, at most rows_cap), so
+    # their count is the caller's contract
+    _buf(a_row_index, torch.int32, 0, "a_row_index")
+    _buf(a_gs, torch.float32, 1, "a_gs")
+    _buf(b_gs, torch.float32, n_b_gs, "b_gs")
+    _buf(offsets, torch.int32, L + 1, "offsets")
+    _buf(tile_table, torch.int32, nvfp4_tile_table_len(rows_cap, L, tile_m), "tile_table")
+
+
 def nvfp4_grouped_gemm(a_q, a_sf, a_row_index, a_gs, b_packed, b_gs, offsets, tile_table, rows_cap,
                        tile_m, epilogue=EPI_BF16, d=None, amax_out=None):
-    """b_packed: uint8 [L, N/32, K/128, 2304] from nvfp4_pack_weights."""
+    """b_packed: uint8 [L, N/32, K/128, 2304] from nvfp4_pack_weights. A rows:
+    a_row_index[s] for slot s when given (device indices < a_q's row count,
+    the caller's contract), else s."""
+    _dev(b_packed, torch.uint8, "b_packed")
     L, n32, k128, chunk = b_packed.shape
     N, K = n32 * 32, k128 * 128
     dev = b_packed.device
     n_out = N // 2 if epilogue in (EPI_SILU_MUL, EPI_SILU_MUL_DUAL) else N
-    d = torch.empty((rows_cap, n_out), dtype=torch.bfloat16, device=dev) if d is None else d
+    _check_gemm_operands(a_q, a_sf, a_row_index, a_gs, b_gs, offsets, tile_table, rows_cap, tile_m, L, K,
+                         2 * L if epilogue == EPI_SILU_MUL_DUAL else L)
+    d = (torch.empty((rows_cap, n_out), dtype=torch.bfloat16, device=dev) if d is None
+         else _buf(d, torch.bfloat16, rows_cap * n_out, "d"))
+    _buf(amax_out, torch.float32, 1, "amax_out")
     _check(_gemm(_ptr(a_q), _ptr(a_sf), _ptr(a_row_index), _ptr(a_gs), _ptr(b_packed), _ptr(b_gs),
                  _ptr(offsets), _ptr(tile_table), L, rows_cap, N, K, tile_m, epilogue, _ptr(d), _ptr(amax_out),
                  _stream()), "nvfp4_grouped_gemm")
@@ -221,12 +271,18 @@ def nvfp4_grouped_gemm_silu_nvfp4(a_q, a_sf, a_row_index, a_gs, b_packed, b_gs, 
     """L1 with the SiLU*up epilogue writing h as NVFP4 with the fixed global
     scale out_gs [1]: returns (h_q uint8 [rows_cap, N/4], h_sf uint8 [rows_cap, N/32]).
     b_gs [L] (folded W1) or [L, 2] (gate and up global scales)."""
+    _dev(b_packed, torch.uint8, "b_packed")
     L, n32, k128, chunk = b_packed.shape
     N, K = n32 * 32, k128 * 128
     dev = b_packed.device
-    d_q = torch.empty((rows_cap, N // 4), dtype=torch.uint8, device=dev) if d_q is None else d_q
-    d_sf = torch.empty((rows_cap, N // 32), dtype=torch.uint8, device=dev) if d_sf is None else d_sf
     dual = 1 if b_gs.dim() == 2 else 0
+    _check_gemm_operands(a_q, a_sf, a_row_index, a_gs, b_gs, offsets, tile_table, rows_cap, tile_m, L, K,
+                         2 * L if dual else L)
+    _buf(out_gs, torch.float32, 1, "out_gs")
+    d_q = (torch.empty((rows_cap, N // 4), dtype=torch.uint8, device=dev) if d_q is None
+           else _buf(d_q, torch.uint8, rows_cap * (N // 4), "d_q"))
+    d_sf = (torch.empty((rows_cap, N // 32), dtype=torch.uint8, device=dev) if d_sf is None
+            else _buf(d_sf, torch.uint8, rows_cap * (N // 32), "d_sf"))
     _check(_gemm_nvfp4(_ptr(a_q), _ptr(a_sf), _ptr(a_row_index), _ptr(a_gs), _ptr(b_packed), _ptr(b_gs), dual,
                        _ptr(offsets), _ptr(tile_table), L, rows_cap, N, K, tile_m, _ptr(out_gs), _ptr(d_q),
                        _ptr(d_sf), _stream()), "nvfp4_grouped_gemm_silu_nvfp4")
@@ -234,9 +290,15 @@ def nvfp4_grouped_gemm_silu_nvfp4(a_q, a_sf, a_row_index, a_gs, b_packed, b_gs, 
 
 
 def moe_weighted_scatter(y, token_slot, topk_w, out=None):
+    """out[t] = sum over j of topk_w[t, j] * y[token_slot[t*k + j]] (slots >= 0),
+    y BF16 [rows, H] with every slot index < rows (the caller's contract)."""
+    _dev(y, torch.bfloat16, "y")
+    _dev(topk_w, torch.float32, "topk_w")
     T, k = topk_w.shape
     H = y.shape[1]
-    out = torch.empty((T, H), dtype=torch.bfloat16, device=y.device) if out is None else out
+    _buf(token_slot, torch.int32, T * k, "token_slot")
+    out = (torch.empty((T, H), dtype=torch.bfloat16, device=y.device) if out is None
+           else _buf(out, torch.bfloat16, T * H, "out"))
     _check(_scatter(_ptr(y), _ptr(token_slot), _ptr(topk_w), T, k, H, _ptr(out), _stream()),
            "moe_weighted_scatter")
     return out
@@ -244,8 +306,11 @@ def moe_weighted_scatter(y, token_slot, topk_w, out=None):
 
 def nvfp4_fold_scales(w1_sf, gs_gate, gs_up, gs1=None):
     """In place on w1_sf [L, 2I, K/16]; returns gs1 [L]."""
+    _dev(w1_sf, torch.uint8, "w1_sf")
     L, two_i, k16 = w1_sf.shape
-    gs1 = torch.empty(L, dtype=torch.float32, device=w1_sf.device) if gs1 is None else gs1
+    _buf(gs_gate, torch.float32, L, "gs_gate")
+    _buf(gs_up, torch.float32, L, "gs_up")
+    gs1 = torch.empty(L, dtype=torch.float32, device=w1_sf.device) if gs1 is None else _buf(gs1, torch.float32, L, "gs1")
     _check(_fold(_ptr(w1_sf), _ptr(gs_gate), _ptr(gs_up), _ptr(gs1), L, two_i // 2, k16 * 16, _stream()),
            "nvfp4_fold_scales")
     return gs1
@@ -324,6 +389,13 @@ def prepare_weights(w_gate, w_up, w_down, keep_unpacked=False, fold=True) -> MoE
     return w
 
 
+def _check_layer_inputs(weights, x, topk_w, T, k):
+    _shape(x, (T, weights.hidden), "x")
+    _shape(topk_w, (T, k), "topk_w")
+    for name in ("w1", "w1_gs", "w2", "w2_gs"):
+        _dev(getattr(weights, name), getattr(weights, name).dtype, f"weights.{name}")
+
+
 def nvfp4_moe_forward(weights: MoEWeights, x, topk_ids, topk_w, expert_start, out=None, ws=None):
     """One rank's partial output BF16 [T, H] of the expert FFN."""
     _dev(x, torch.bfloat16, "x")
@@ -331,10 +403,11 @@ def nvfp4_moe_forward(weights: MoEWeights, x, topk_ids, topk_w, expert_start, ou
     _dev(topk_w, torch.float32, "topk_w")
     T, k = topk_ids.shape
     H = weights.hidden
+    _check_layer_inputs(weights, x, topk_w, T, k)
     dev = x.device
-    out = torch.empty((T, H), dtype=torch.bfloat16, device=dev) if out is None else out
+    out = torch.empty((T, H), dtype=torch.bfloat16, device=dev) if out is None else _buf(out, torch.bfloat16, T * H, "out")
     need = nvfp4_moe_ws_bytes(T, k, H, weights.inter, weights.num_local)
-    ws = _alloc_ws(need, dev) if ws is None else ws
+    ws = _alloc_ws(need, dev) if ws is None else _buf(ws, torch.uint8, 0, "ws")
     _check(_forward(ctypes.byref(weights._c), _ptr(x), T, _ptr(topk_ids), _ptr(topk_w), k, expert_start,
                     _ptr(out), _ptr(ws), ws.numel(), _stream()), "nvfp4_moe_forward")
     return out
@@ -351,10 +424,11 @@ def nvfp4_moe_forward_static(weights: MoEWeights, x, topk_ids, topk_w, expert_st
         raise ValueError(f"gs: expected 2 values (gs_x, gs_h), got {gs.numel()}")
     T, k = topk_ids.shape
     H = weights.hidden
+    _check_layer_inputs(weights, x, topk_w, T, k)
     dev = x.device
-    out = torch.empty((T, H), dtype=torch.bfloat16, device=dev) if out is None else out
+    out = torch.empty((T, H), dtype=torch.bfloat16, device=dev) if out is None else _buf(out, torch.bfloat16, T * H, "out")
     need = nvfp4_moe_ws_bytes(T, k, H, weights.inter, weights.num_local)
-    ws = _alloc_ws(need, dev) if ws is None else ws
+    ws = _alloc_ws(need, dev) if ws is None else _buf(ws, torch.uint8, 0, "ws")
     _check(_forward_static(ctypes.byref(weights._c), _ptr(x), T, _ptr(topk_ids), _ptr(topk_w), k, expert_start,
                            _ptr(gs), _ptr(out), _ptr(ws), ws.numel(), _stream()), "nvfp4_moe_forward_static")
     return out

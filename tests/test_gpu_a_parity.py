@@ -388,3 +388,51 @@ def test_layer_duplicate_ids_in_a_token(nv):
     x = W.make_activations(cfg)
     got, ref, tr = _edge_layer(nv, "duplicate ids", ids, w, x)
     assert rel_err(got, ref) <= TOL
+
+
+# ------------------------------------------------------- binding validation
+
+def test_binding_rejects_bad_buffers(nv):
+    """The library sees only addresses, so the binding checks the shapes,
+    dtypes and sizes of the tensors it passes; a bad one raises before any
+    launch."""
+    T, k, L, H, I = 6, 2, 2, 256, 128
+    w = nv.prepare_weights(torch.zeros((L, I, H), dtype=torch.bfloat16, device=DEV),
+                           torch.zeros((L, I, H), dtype=torch.bfloat16, device=DEV),
+                           torch.zeros((L, H, I), dtype=torch.bfloat16, device=DEV))
+    x = torch.zeros((T, H), dtype=torch.bfloat16, device=DEV)
+    ids = torch.zeros((T, k), dtype=torch.int32, device=DEV)
+    tw = torch.ones((T, k), dtype=torch.float32, device=DEV)
+    with pytest.raises(ValueError, match="x"):
+        nv.nvfp4_moe_forward(w, x[:, :128].contiguous(), ids, tw, 0)
+    with pytest.raises(ValueError, match="topk_w"):
+        nv.nvfp4_moe_forward(w, x, ids, tw[:, :1].contiguous(), 0)
+    with pytest.raises(ValueError, match="out"):
+        nv.nvfp4_moe_forward(w, x, ids, tw, 0, out=torch.empty((T - 1, H), dtype=torch.bfloat16, device=DEV))
+    with pytest.raises(ValueError, match="out"):
+        nv.nvfp4_moe_forward(w, x, ids, tw, 0, out=torch.empty((T, H), dtype=torch.float32, device=DEV))
+    with pytest.raises(ValueError, match="ws"):
+        nv.nvfp4_moe_forward(w, x, ids, tw, 0, ws=torch.empty(1024, dtype=torch.int32, device=DEV))
+    with pytest.raises(ValueError, match="topk_w"):
+        nv.moe_route_slots(ids, tw[:-1].contiguous(), 0, L, 32)
+    with pytest.raises(ValueError, match="q"):
+        nv.nvfp4_quantize(x, q=torch.empty((T, H // 2 - 1), dtype=torch.uint8, device=DEV))
+    with pytest.raises(ValueError, match="gs"):
+        nv.nvfp4_quantize_static(x.view(2, T // 2, H), torch.ones(1, dtype=torch.float32, device=DEV))
+    with pytest.raises(ValueError, match="x"):
+        nv.nvfp4_quantize(x.t())          # not contiguous
+    r = nv.moe_route_slots(ids, tw, 0, L, 32)
+    xq, xsf, gs = nv.nvfp4_quantize(x)
+    cap = T * k
+    with pytest.raises(ValueError, match="d"):
+        nv.nvfp4_grouped_gemm(xq, xsf, r["slot_token"], gs, w.w1, w.w1_gs, r["offsets"], r["tile_table"], cap, 32,
+                              epilogue=nv.EPI_SILU_MUL, d=torch.empty((cap - 1, I), dtype=torch.bfloat16, device=DEV),
+                              amax_out=torch.zeros(1, dtype=torch.float32, device=DEV))
+    with pytest.raises(ValueError, match="tile_table"):
+        nv.nvfp4_grouped_gemm(xq, xsf, r["slot_token"], gs, w.w1, w.w1_gs, r["offsets"], r["tile_table"][:3].contiguous(),
+                              cap, 32, epilogue=nv.EPI_SILU_MUL, amax_out=torch.zeros(1, dtype=torch.float32, device=DEV))
+    with pytest.raises(ValueError, match="a_q"):
+        nv.nvfp4_grouped_gemm(xq[:, :64].contiguous(), xsf, r["slot_token"], gs, w.w1, w.w1_gs, r["offsets"],
+                              r["tile_table"], cap, 32, epilogue=nv.EPI_SILU_MUL,
+                              amax_out=torch.zeros(1, dtype=torch.float32, device=DEV))
+    torch.cuda.synchronize()
