@@ -109,8 +109,9 @@ def main():
     if args.config == "quantize" and not args.quantize_only:
         raise SystemExit("bench.py: --config quantize only names the trace of a --quantize-only run")
     if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU; --gpus {args.gpus} is not supported "
-              f"(expert-parallel sharding across GPUs is described in DESIGN.md, not built)", file=sys.stderr)
+        print(f"bench.py: the layer runs one rank's share of the experts on one GPU; --gpus {args.gpus} is not "
+              f"supported (expert-parallel sharding across GPUs and its all-reduce are not implemented)",
+              file=sys.stderr)
         sys.exit(2)
 
     import torch
