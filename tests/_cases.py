@@ -112,6 +112,11 @@ def quant_case(name):
         return W.bf16_bits(rng.standard_normal((333, 96)).astype(np.float32))
     if name == "quant_full":
         return W.make_quant_input(W.get_config("quant"))
+    if name == "large_outliers":
+        # a 73 MB tensor with sparse outliers past 2688 (block scales saturate unless gs is applied)
+        x = rng.standard_t(3, (5120, 7168)).astype(np.float32)
+        x[rng.integers(0, 5120, 64), rng.integers(0, 7168, 64)] = 3000.0
+        return W.bf16_bits(x)
     raise KeyError(name)
 
 

@@ -52,7 +52,7 @@ def rel_err(got, ref):
 # ------------------------------------------------------------------- quantizer
 
 @pytest.mark.parametrize("case", ["tiny_x", "mid_x", "t3_outliers", "ties", "scale_ties", "subnormal", "zeros",
-                                  "wide", "ragged_rows", "quant_full"])
+                                  "wide", "ragged_rows", "quant_full", "large_outliers"])
 def test_quantize_bit_exact(nv, case):
     xb = quant_case(case)
     log(f"quantize {case} shape={xb.shape}")
