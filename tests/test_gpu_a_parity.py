@@ -288,13 +288,16 @@ def test_layer(nv, name, fold):
     T, k = ids.shape
     H = cfg.hidden
     lay = nv.nvfp4_moe_ws_layout(T, k, H, cfg.inter, cfg.num_local)
-    ws = torch.empty(lay["end"], dtype=torch.uint8, device=DEV)
+    guard = 4096
+    ws_buf = torch.full((lay["end"] + guard,), 0xA5, dtype=torch.uint8, device=DEV)   # canary bytes past the workspace
+    ws = ws_buf[:lay["end"]]
     buf = torch.full((T + 2, H), -3.0, dtype=torch.bfloat16, device=DEV)   # canary rows around out
     out = nv.nvfp4_moe_forward(weights, to_bf16(x), to_dev(ids), to_dev(w), cfg.expert_start,
                                out=buf[1:T + 1], ws=ws)
     torch.cuda.synchronize()
     b = buf.float().cpu().numpy()
     assert np.all(b[0] == -3.0) and np.all(b[T + 1] == -3.0)
+    assert bool((ws_buf[lay["end"]:] == 0xA5).all()), "bytes past the workspace were written"
     tr = O.moe_forward(x, ids, w, cfg.expert_start, P)
     # stage checks from the workspace: activation quantization and routing are exact
     assert np.array_equal(nv.ws_view(ws, lay, "x_q", torch.uint8, (T, H // 2)).cpu().numpy(), tr.x_q)

@@ -190,9 +190,11 @@ def test_layer_static(nv, name, fold):
         xs = W.bf16_bits(O.bf16_to_f32(x) * np.float32(scale))
         T, k = ids.shape
         lay = nv.nvfp4_moe_ws_layout(T, k, cfg.hidden, cfg.inter, cfg.num_local)
-        ws = torch.empty(lay["end"], dtype=torch.uint8, device=DEV)
+        ws_buf = torch.full((lay["end"] + 4096,), 0xA5, dtype=torch.uint8, device=DEV)   # canary bytes past the end
+        ws = ws_buf[:lay["end"]]
         out = nv.nvfp4_moe_forward_static(weights, to_bf16(xs), d_ids, d_w, cfg.expert_start, to_dev(gs_o), ws=ws)
         torch.cuda.synchronize()
+        assert bool((ws_buf[lay["end"]:] == 0xA5).all()), "bytes past the workspace were written"
         ref = O.moe_forward(xs, ids, w, cfg.expert_start, P, static_gs=(gs_o[0], gs_o[1]))
         H = cfg.hidden
         assert np.array_equal(nv.ws_view(ws, lay, "x_q", torch.uint8, (T, H // 2)).cpu().numpy(), ref.x_q)
