@@ -191,33 +191,45 @@ def test_full_prefill(nv, shared):
     _run(nv, shared, "prefill")
 
 
-@pytest.mark.parametrize("name", ["decode", "prefill"])
-def test_full_static_scales(nv, shared, name):
-    # fixed (calibrated) global scales at full size, in both forms of the static
-    # layer (decode: BF16 h then a fixed-scale quantization; prefill: h written
-    # as NVFP4 by the L1 epilogue): with the scales the dynamic pass measures,
-    # the static pass is that pass, bit for bit
+def _static_equals_dynamic(nv, sh, name):
+    """With the scales the dynamic pass measures, the static pass is that pass,
+    bit for bit; the calibrated gs_x is the oracle's, and the activation
+    quantization with it matches the oracle's fixed-scale quantizer."""
     cfg = W.get_config(name)
     ids, w = W.make_router(cfg)
     x = W.make_activations(cfg)
     d_x, d_ids, d_w = to_bf16(x), to_dev(ids), to_dev(w)
-    log(f"{name}: static scales, T={cfg.tokens}")
-    dyn = nv.nvfp4_moe_forward(shared.gpu, d_x, d_ids, d_w, cfg.expert_start)
-    gs = nv.calibrate_static_gs(shared.gpu, d_x, d_ids, d_w, cfg.expert_start)
+    log(f"{name}: static scales, T={cfg.tokens}, per-half gate/up scales {sh.gpu.dual_gs}")
+    dyn = nv.nvfp4_moe_forward(sh.gpu, d_x, d_ids, d_w, cfg.expert_start)
+    gs = nv.calibrate_static_gs(sh.gpu, d_x, d_ids, d_w, cfg.expert_start)
     T, k = ids.shape
     lay = nv.nvfp4_moe_ws_layout(T, k, cfg.hidden, cfg.inter, cfg.num_local)
     ws = torch.empty(lay["end"], dtype=torch.uint8, device=DEV)
-    st = nv.nvfp4_moe_forward_static(shared.gpu, d_x, d_ids, d_w, cfg.expert_start, gs, ws=ws)
+    st = nv.nvfp4_moe_forward_static(sh.gpu, d_x, d_ids, d_w, cfg.expert_start, gs, ws=ws)
     torch.cuda.synchronize()
     assert torch.equal(st.view(torch.int16), dyn.view(torch.int16))
-    # the calibrated gs_x is the oracle's, and the activation quantization with
-    # it matches the oracle's fixed-scale quantizer
     H = cfg.hidden
     gs_x = O.global_scale(np.abs(O.bf16_to_f64(x)).max())
     assert gs[0].item() == gs_x
     q, sf, _ = O.quantize(x, gs=gs_x)
     assert np.array_equal(nv.ws_view(ws, lay, "x_q", torch.uint8, (T, H // 2)).cpu().numpy(), q)
     assert np.array_equal(nv.ws_view(ws, lay, "x_sf", torch.uint8, (T, H // 16)).cpu().numpy(), sf)
+
+
+@pytest.mark.parametrize("name", ["decode", "prefill"])
+def test_full_static_scales(nv, shared, name):
+    # fixed (calibrated) global scales at full size, in both forms of the static
+    # layer (decode: BF16 h then a fixed-scale quantization; prefill: h written
+    # as NVFP4 by the L1 epilogue)
+    _static_equals_dynamic(nv, shared, name)
+
+
+def test_full_static_scales_skewed(nv, skewed, skewed_unfolded):
+    # the skewed shard (empty experts, one expert with most slots, gate and up
+    # scales 30x apart) through the static layer's NVFP4 epilogue, with the
+    # gate/up fold and with per-half global scales
+    _static_equals_dynamic(nv, skewed, "skewed")
+    _static_equals_dynamic(nv, skewed_unfolded, "skewed")
 
 
 def test_full_skewed(nv, skewed):
