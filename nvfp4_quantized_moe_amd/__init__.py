@@ -236,8 +236,10 @@ def _check_gemm_operands(a_q, a_sf, a_row_index, a_gs, b_gs, offsets, tile_table
     if a_q.dim() != 2 or a_q.shape[1] != K // 2 or tuple(a_sf.shape) != (a_q.shape[0], K // 16):
         raise ValueError(f"a_q {tuple(a_q.shape)} / a_sf {tuple(a_sf.shape)}: expected [rows, {K // 2}] / "
                          f"[rows, {K // 16}]")
-    # rows read: slot s, or a_row_index[s], for the slots below offsets[L] (device data, at most rows_cap), so
-    # their count is the caller's contract
+    # rows read: slot s, or a_row_index[s], for the slots below offsets[L] (device data, at most rows_cap); with
+    # a row index the indices' range is the caller's contract, without one every slot row must exist
+    if a_row_index is None and a_q.shape[0] < rows_cap:
+        raise ValueError(f"a_q: {a_q.shape[0]} rows, but slots up to rows_cap = {rows_cap} read their own row")
     _buf(a_row_index, torch.int32, 0, "a_row_index")
     _buf(a_gs, torch.float32, 1, "a_gs")
     _buf(b_gs, torch.float32, n_b_gs, "b_gs")
@@ -245,14 +247,21 @@ def _check_gemm_operands(a_q, a_sf, a_row_index, a_gs, b_gs, offsets, tile_table
     _buf(tile_table, torch.int32, nvfp4_tile_table_len(rows_cap, L, tile_m), "tile_table")
 
 
+def _packed_dims(b_packed, name="b_packed"):
+    """(L, N, K) of packed weights uint8 [L, N/32, K/128, 2304]."""
+    _dev(b_packed, torch.uint8, name)
+    if b_packed.dim() != 4 or b_packed.shape[3] != 2304:
+        raise ValueError(f"{name}: expected packed weights [L, N/32, K/128, 2304], got {tuple(b_packed.shape)}")
+    L, n32, k128, _ = b_packed.shape
+    return L, n32 * 32, k128 * 128
+
+
 def nvfp4_grouped_gemm(a_q, a_sf, a_row_index, a_gs, b_packed, b_gs, offsets, tile_table, rows_cap,
                        tile_m, epilogue=EPI_BF16, d=None, amax_out=None):
     """b_packed: uint8 [L, N/32, K/128, 2304] from nvfp4_pack_weights. A rows:
     a_row_index[s] for slot s when given (device indices < a_q's row count,
-    the caller's contract), else s."""
-    _dev(b_packed, torch.uint8, "b_packed")
-    L, n32, k128, chunk = b_packed.shape
-    N, K = n32 * 32, k128 * 128
+    the caller's contract), else s (a_q then needs rows_cap rows)."""
+    L, N, K = _packed_dims(b_packed)
     dev = b_packed.device
     n_out = N // 2 if epilogue in (EPI_SILU_MUL, EPI_SILU_MUL_DUAL) else N
     _check_gemm_operands(a_q, a_sf, a_row_index, a_gs, b_gs, offsets, tile_table, rows_cap, tile_m, L, K,
@@ -271,9 +280,7 @@ def nvfp4_grouped_gemm_silu_nvfp4(a_q, a_sf, a_row_index, a_gs, b_packed, b_gs, 
     """L1 with the SiLU*up epilogue writing h as NVFP4 with the fixed global
     scale out_gs [1]: returns (h_q uint8 [rows_cap, N/4], h_sf uint8 [rows_cap, N/32]).
     b_gs [L] (folded W1) or [L, 2] (gate and up global scales)."""
-    _dev(b_packed, torch.uint8, "b_packed")
-    L, n32, k128, chunk = b_packed.shape
-    N, K = n32 * 32, k128 * 128
+    L, N, K = _packed_dims(b_packed)
     dev = b_packed.device
     dual = 1 if b_gs.dim() == 2 else 0
     _check_gemm_operands(a_q, a_sf, a_row_index, a_gs, b_gs, offsets, tile_table, rows_cap, tile_m, L, K,
@@ -353,13 +360,16 @@ class MoEWeights:
     def __init__(self, w1, w1_gs, w2, w2_gs):
         self.w1, self.w1_gs, self.w2, self.w2_gs = w1, w1_gs, w2, w2_gs
         self.dual_gs = w1_gs.dim() == 2
-        self.num_local = w1.shape[0]
-        self.inter = w1.shape[1] * 32 // 2
-        self.hidden = w1.shape[2] * 128
-        if tuple(w2.shape[:3]) != (self.num_local, self.hidden // 32, self.inter // 128):
+        self.num_local, two_i, self.hidden = _packed_dims(w1, "w1")
+        self.inter = two_i // 2
+        if _packed_dims(w2, "w2") != (self.num_local, self.hidden, self.inter):
             raise ValueError(f"packed W2 shape {tuple(w2.shape)} does not match W1 {tuple(w1.shape)}")
-        if tuple(w1_gs.shape) not in ((self.num_local,), (self.num_local, 2)) or not w1_gs.is_contiguous():
-            raise ValueError(f"w1_gs shape {tuple(w1_gs.shape)}: expected [L] or [L, 2], contiguous")
+        _dev(w1_gs, torch.float32, "w1_gs")
+        _dev(w2_gs, torch.float32, "w2_gs")
+        if tuple(w1_gs.shape) not in ((self.num_local,), (self.num_local, 2)):
+            raise ValueError(f"w1_gs shape {tuple(w1_gs.shape)}: expected [L] or [L, 2]")
+        if tuple(w2_gs.shape) != (self.num_local,):
+            raise ValueError(f"w2_gs shape {tuple(w2_gs.shape)}: expected [L] = [{self.num_local}]")
         self._c = _Weights(self.num_local, self.hidden, self.inter, w1.data_ptr(), w1_gs.data_ptr(),
                            w2.data_ptr(), w2_gs.data_ptr(), 1 if self.dual_gs else 0)
 

@@ -2,9 +2,11 @@
 in seconds (several tiles per dimension, ragged tails, empty experts).
 
 Bar: bit-exact for quantized codes, scales, global scales, routing arrays,
-the scale fold and the weighted scatter; layer and GEMM outputs within
-1e-2 x max|oracle| (float32 accumulation order differs); cosine >= 0.98
-against the BF16 layer built from the dequantized NVFP4 weights.
+the scale fold, the weighted scatter and the re-quantization of the layer's
+own h; layer and GEMM outputs within 1e-2 x max|oracle| (float32
+accumulation order differs), and BF16 GEMM outputs also within a few BF16
+ulps element by element; cosine >= 0.98 against the BF16 layer built from
+the dequantized NVFP4 weights.
 """
 import numpy as np
 import pytest
@@ -13,9 +15,12 @@ import torch
 import oracle as O
 import workloads as W
 from _cases import pack_weights_np, quant_case
+from _parity_log import record, ulp_error
 
 pytestmark = pytest.mark.gpu
 TOL = 1e-2
+ULP_TOL_BF16 = 2.0   # D = RN_bf16(alpha * sum), BF16 ulps (see test_grouped_gemm)
+ULP_TOL_SILU = 4.0   # h = RN_bf16(silu(RN_bf16(g)) * RN_bf16(u)), BF16 ulps
 
 
 def log(msg):
@@ -62,6 +67,7 @@ def test_quantize_bit_exact(nv, case):
     assert gs.cpu().numpy()[0] == ogs
     assert np.array_equal(sf.cpu().numpy(), osf)
     assert np.array_equal(q.cpu().numpy(), oq)
+    record(f"quantize:{case}", bit_exact_arrays=3)
 
 
 def test_quantize_batched_and_amax_in(nv):
@@ -248,8 +254,16 @@ def test_grouped_gemm(nv, case, tile_m, epi):
         ref = O.bf16_to_f32(O.f32_to_bf16(g))
     if S:
         err = rel_err(got[:S], ref)
-        log(f"  rel err {err:.3e}")
+        ulps = ulp_error(got[:S], ref)
+        log(f"  rel err {err:.3e}  max {ulps:.2f} BF16 ulps")
+        record(f"gemm:{case}:tile{tile_m}:epi{epi}", rel_err=err, ulp_err=ulps)
         assert err <= TOL
+        # D = RN_bf16(alpha * sum): float32 sums in another order differ by far less than
+        # a BF16 ulp of a typical element, so the two roundings differ by at most one ulp
+        # (a second one only for elements near the floor of ulp_error, whose sums cancel);
+        # the SiLU*up epilogue rounds g and u to BF16 first and uses its own exp, so h may
+        # move by a few ulps
+        assert ulps <= (ULP_TOL_BF16 if epi == 0 else ULP_TOL_SILU)
 
 
 # --------------------------------------------------------------------- layer
@@ -272,6 +286,19 @@ def _deq_ref(P, cfg, x, ids, w):
     du = np.stack([f(P["w1_q"][e, I:], P["w1_sf"][e, I:], gs_u[e]) for e in range(L)])
     dd = np.stack([f(P["w2_q"][e], P["w2_sf"][e], P["w2_gs"][e]) for e in range(L)])
     return O.bf16_reference_layer(x, ids, w, cfg.expert_start, dg, du, dd)
+
+
+def check_requant_h(nv, ws, lay, cap, inter, S, h_bits, scal):
+    """Step a6 bit for bit: the layer's h_q, h_sf and gs_h are the oracle's
+    quantization of the GPU's own h (its S valid rows) with amax_h from the
+    L1 epilogue (nvfp4_mega_moe.py history, alpha commit: L2 takes the global
+    scale that quantizing h returns)."""
+    oq, osf, ogs = O.quantize(h_bits, amax=np.float32(scal[1]))
+    assert scal[2] == ogs == O.global_scale(scal[1]), (scal[2], ogs)
+    h_q = nv.ws_view(ws, lay, "h_q", torch.uint8, (cap, inter // 2))[:S].cpu().numpy()
+    h_sf = nv.ws_view(ws, lay, "h_sf", torch.uint8, (cap, inter // 16))[:S].cpu().numpy()
+    assert np.array_equal(h_sf, osf), "h block scales differ from the oracle's quantization of the GPU's h"
+    assert np.array_equal(h_q, oq), "h codes differ from the oracle's quantization of the GPU's h"
 
 
 @pytest.mark.parametrize("name,fold", [("tiny", True), ("mid", True), ("mid_k1", True), ("mid_skew", True),
@@ -308,14 +335,17 @@ def test_layer(nv, name, fold):
     for key in ("slot_token", "token_slot", "slot_expert"):
         assert np.array_equal(nv.ws_view(ws, lay, key, torch.int32, (cap,)).cpu().numpy(), tr.routing[key]), key
     S = tr.routing["S"]
-    h = nv.ws_view(ws, lay, "h", torch.bfloat16, (cap, cfg.inter))[:S].float().cpu().numpy()
+    h_t = nv.ws_view(ws, lay, "h", torch.bfloat16, (cap, cfg.inter))[:S]
+    h = h_t.float().cpu().numpy()
     assert scal[1] == np.abs(h).max()                      # amax of h, taken in the epilogue
+    check_requant_h(nv, ws, lay, cap, cfg.inter, S, bits_of(h_t), scal)
     eh = rel_err(h, O.bf16_to_f32(tr.h))
     got = out.float().cpu().numpy()
     ref = O.bf16_to_f32(tr.out)
     err = rel_err(got, ref)
     cos = O.cosine(got, _deq_ref(P, cfg, x, ids, w))
     log(f"  h rel err {eh:.3e}  out rel err {err:.3e}  cosine {cos:.4f}  S={S}")
+    record(f"layer:{name}:fold{int(fold)}", h_rel_err=eh, rel_err=err, cosine_deq=cos, h_requant_bit_exact=True)
     assert eh <= TOL and err <= TOL
     assert cos >= 0.98
     # run-to-run determinism
@@ -438,4 +468,18 @@ def test_binding_rejects_bad_buffers(nv):
         nv.nvfp4_grouped_gemm(xq[:, :64].contiguous(), xsf, r["slot_token"], gs, w.w1, w.w1_gs, r["offsets"],
                               r["tile_table"], cap, 32, epilogue=nv.EPI_SILU_MUL,
                               amax_out=torch.zeros(1, dtype=torch.float32, device=DEV))
+    # without a row index, slot s reads row s: T rows cannot serve rows_cap = T * k slots
+    with pytest.raises(ValueError, match="a_q"):
+        nv.nvfp4_grouped_gemm(xq, xsf, None, gs, w.w1, w.w1_gs, r["offsets"], r["tile_table"], cap, 32,
+                              epilogue=nv.EPI_SILU_MUL, amax_out=torch.zeros(1, dtype=torch.float32, device=DEV))
+    with pytest.raises(ValueError, match="b_packed"):
+        nv.nvfp4_grouped_gemm(xq, xsf, r["slot_token"], gs, w.w1[..., :2048].contiguous(), w.w1_gs, r["offsets"],
+                              r["tile_table"], cap, 32, epilogue=nv.EPI_SILU_MUL,
+                              amax_out=torch.zeros(1, dtype=torch.float32, device=DEV))
+    with pytest.raises(ValueError, match="w2_gs"):
+        nv.MoEWeights(w.w1, w.w1_gs, w.w2, w.w2_gs.double())
+    with pytest.raises(ValueError, match="w2_gs"):
+        nv.MoEWeights(w.w1, w.w1_gs, w.w2, w.w2_gs[:1].contiguous())
+    with pytest.raises(ValueError, match="w1_gs"):
+        nv.MoEWeights(w.w1, torch.ones((L, 3), dtype=torch.float32, device=DEV), w.w2, w.w2_gs)
     torch.cuda.synchronize()

@@ -4,10 +4,13 @@ intermediate 3072).
 
 * decode shard (64 tokens) and prefill shard (8192 tokens) share one set of
   weights; every expert's NVFP4 weights are compared bit for bit.
-* skewed shard (16384 tokens, Zipf popularity, cold experts, W_up 30x):
-  weights, activation quantization and routing bit for bit; the layer output
-  within 1e-2 x max|oracle|.
-The oracle runs its experts on a thread pool (same arithmetic per expert).
+* skewed shard (16384 tokens, Zipf popularity, cold experts, W_up 30x).
+On every shard: weights, activation quantization, routing and the
+re-quantization of the GPU's own h bit for bit; h and the layer output within
+1e-2 x max|oracle|; cosine >= 0.98 against the BF16 layer built from the
+dequantized NVFP4 weights (the cosine against the original BF16 weights is
+recorded beside it). The oracle runs its experts on a thread pool (same
+arithmetic per expert).
 """
 import os
 import time
@@ -20,6 +23,8 @@ import torch
 import oracle as O
 import workloads as W
 from _cases import pack_weights_np
+from _layer_checks import check_requant_h, check_static_h, dequantized_weights
+from _parity_log import record
 
 pytestmark = [pytest.mark.gpu, pytest.mark.timeout(900)]
 TOL = 1e-2
@@ -126,22 +131,20 @@ def _touched_only(cfg, ids):
 def _cosines(sh, cfg, x, ids, w, got):
     """Cosine of the layer output against the BF16 layer built from the
     dequantized NVFP4 weights (the gate) and against the original BF16
-    weights (logged), over the touched experts."""
-    I = cfg.inter
+    weights (recorded), over the touched experts."""
     ids2, touched = _touched_only(cfg, ids)
-    f = lambda q, sf, gs: O.f32_to_bf16(O.dequantize(q, sf, gs, np.float32))
-    P = sh.P
-    dg = np.stack([f(P["w1_q"][e, :I], P["w1_sf"][e, :I], P["w1_gs"][e]) for e in touched])
-    du = np.stack([f(P["w1_q"][e, I:], P["w1_sf"][e, I:], P["w1_gs"][e]) for e in touched])
-    dd = np.stack([f(P["w2_q"][e], P["w2_sf"][e], P["w2_gs"][e]) for e in touched])
+    t = time.time()
+    with ThreadPoolExecutor(THREADS) as ex:
+        dg, du, dd = dequantized_weights(sh.P, touched, ex.map)
     c_deq = O.cosine(got, O.bf16_reference_layer(x, ids2, w, 0, dg, du, dd))
     del dg, du, dd
     c_bf16 = O.cosine(got, O.bf16_reference_layer(x, ids2, w, 0, sh.wg[touched], sh.wu[touched],
                                                   sh.wd[touched]))
+    log(f"{cfg.name}: BF16 reference layers {time.time() - t:.1f}s")
     return c_deq, c_bf16
 
 
-def _run(nv, sh, name, cosine=False, return_out=False):
+def _run(nv, sh, name, cosine=True, tag=None):
     cfg = W.get_config(name)
     ids, w = W.make_router(cfg)
     x = W.make_activations(cfg)
@@ -165,18 +168,25 @@ def _run(nv, sh, name, cosine=False, return_out=False):
     ref = O.bf16_to_f32(tr.out)
     err = rel_err(got, ref)
     S = tr.routing["S"]
-    h = nv.ws_view(ws, lay, "h", torch.bfloat16, (cap, cfg.inter))[:S].float().cpu().numpy()
+    h_t = nv.ws_view(ws, lay, "h", torch.bfloat16, (cap, cfg.inter))[:S]
+    h = h_t.float().cpu().numpy()
     eh = rel_err(h, O.bf16_to_f32(tr.h))
-    log(f"{name}: h rel err {eh:.3e}, out rel err {err:.3e}")
+    scal = nv.ws_view(ws, lay, "scalars", torch.float32, (4,)).cpu().numpy()
+    assert scal[0] == tr.gs_x and scal[1] == np.abs(h).max()
+    check_requant_h(nv, ws, lay, cap, cfg.inter, S, h_t.view(torch.int16).cpu().numpy().view(np.uint16), scal)
+    log(f"{name}: h rel err {eh:.3e}, out rel err {err:.3e}; h re-quantization bit-exact")
     assert eh <= TOL and err <= TOL
+    fig = dict(S=S, h_rel_err=eh, rel_err=err)
     if cosine:
         c_deq, c_bf16 = _cosines(sh, cfg, x, ids, w, got)
         log(f"{name}: cosine {c_deq:.4f} vs dequantized-weight BF16 layer, {c_bf16:.4f} vs original BF16 weights")
+        fig.update(cosine_deq=c_deq, cosine_bf16_weights=c_bf16)
+    record(f"full:{tag or name}", **fig)
+    sh.fig = fig
+    if cosine:
         assert c_deq >= 0.98
     out2 = nv.nvfp4_moe_forward(sh.gpu, to_bf16(x), to_dev(ids), to_dev(w), cfg.expert_start, ws=ws)
     assert torch.equal(out2.view(torch.int16), out.view(torch.int16))
-    if return_out:
-        return got
 
 
 def test_full_weights_bit_exact(nv, shared):
@@ -184,7 +194,7 @@ def test_full_weights_bit_exact(nv, shared):
 
 
 def test_full_decode(nv, shared):
-    _run(nv, shared, "decode", cosine=True)
+    _run(nv, shared, "decode")
 
 
 def test_full_prefill(nv, shared):
@@ -200,20 +210,26 @@ def _static_equals_dynamic(nv, sh, name):
     x = W.make_activations(cfg)
     d_x, d_ids, d_w = to_bf16(x), to_dev(ids), to_dev(w)
     log(f"{name}: static scales, T={cfg.tokens}, per-half gate/up scales {sh.gpu.dual_gs}")
-    dyn = nv.nvfp4_moe_forward(sh.gpu, d_x, d_ids, d_w, cfg.expert_start)
-    gs = nv.calibrate_static_gs(sh.gpu, d_x, d_ids, d_w, cfg.expert_start)
     T, k = ids.shape
     lay = nv.nvfp4_moe_ws_layout(T, k, cfg.hidden, cfg.inter, cfg.num_local)
+    ws_d = torch.empty(lay["end"], dtype=torch.uint8, device=DEV)
+    dyn = nv.nvfp4_moe_forward(sh.gpu, d_x, d_ids, d_w, cfg.expert_start, ws=ws_d)
+    gs = nv.calibrate_static_gs(sh.gpu, d_x, d_ids, d_w, cfg.expert_start)
     ws = torch.empty(lay["end"], dtype=torch.uint8, device=DEV)
     st = nv.nvfp4_moe_forward_static(sh.gpu, d_x, d_ids, d_w, cfg.expert_start, gs, ws=ws)
     torch.cuda.synchronize()
     assert torch.equal(st.view(torch.int16), dyn.view(torch.int16))
+    cap = T * k
+    S = int(nv.ws_view(ws_d, lay, "offsets", torch.int32, (cfg.num_local + 1,))[-1].item())
+    h_bits = nv.ws_view(ws_d, lay, "h", torch.int16, (cap, cfg.inter))[:S].cpu().numpy().view(np.uint16)
+    check_static_h(nv, ws, lay, cap, cfg.inter, S, h_bits, gs[1].item())
     H = cfg.hidden
     gs_x = O.global_scale(np.abs(O.bf16_to_f64(x)).max())
     assert gs[0].item() == gs_x
     q, sf, _ = O.quantize(x, gs=gs_x)
     assert np.array_equal(nv.ws_view(ws, lay, "x_q", torch.uint8, (T, H // 2)).cpu().numpy(), q)
     assert np.array_equal(nv.ws_view(ws, lay, "x_sf", torch.uint8, (T, H // 16)).cpu().numpy(), sf)
+    record(f"static:{name}:dual{int(sh.gpu.dual_gs)}", equals_dynamic=True, h_codes_bit_exact=True)
 
 
 @pytest.mark.parametrize("name", ["decode", "prefill"])
@@ -241,20 +257,19 @@ def test_full_skewed(nv, skewed):
 def test_full_skewed_unfolded_scales(nv, skewed, skewed_unfolded):
     """Gate and up keep their own global scales (30x apart) instead of the
     fold: weights bit for bit, layer output within tolerance of the oracle in
-    the same mode. Logs the accuracy ablation: cosine of both treatments
-    against the layer built from the original BF16 weights."""
+    the same mode, cosine gate against the layer of its own dequantized
+    weights. Records the accuracy ablation: cosine of both treatments against
+    the layer built from the original BF16 weights (the folded figures come
+    from test_full_skewed when it ran first in this session)."""
     for key in ("w1_q", "w1_sf", "w1_gs"):
         assert np.array_equal(getattr(skewed_unfolded.gpu, key).cpu().numpy(), skewed_unfolded.P[key]), key
     assert np.array_equal(skewed_unfolded.gpu.w1.cpu().numpy(),
                           pack_weights_np(skewed_unfolded.P["w1_q"], skewed_unfolded.P["w1_sf"]))
-    got_dual = _run(nv, skewed_unfolded, "skewed", return_out=True)
-    got_fold = _run(nv, skewed, "skewed", return_out=True)
-    cfg = W.get_config("skewed")
-    ids, w = W.make_router(cfg)
-    x = W.make_activations(cfg)
-    t = time.time()
-    ref = O.bf16_reference_layer(x, ids, w, cfg.expert_start, skewed.wg, skewed.wu, skewed.wd)
-    c_fold, c_dual = O.cosine(got_fold, ref), O.cosine(got_dual, ref)
-    log(f"skewed ablation (BF16 reference {time.time() - t:.1f}s): cosine vs original BF16 weights "
-        f"{c_fold:.5f} with the gate/up fold, {c_dual:.5f} with per-half global scales")
+    _run(nv, skewed_unfolded, "skewed", tag="skewed_unfolded")
+    if not hasattr(skewed, "fig"):
+        _run(nv, skewed, "skewed")
+    c_fold, c_dual = skewed.fig["cosine_bf16_weights"], skewed_unfolded.fig["cosine_bf16_weights"]
+    log(f"skewed ablation: cosine vs original BF16 weights {c_fold:.5f} with the gate/up fold, "
+        f"{c_dual:.5f} with per-half global scales")
+    record("full:skewed_ablation", cosine_bf16_fold=c_fold, cosine_bf16_dual=c_dual)
     assert c_fold > 0.9 and c_dual > 0.9

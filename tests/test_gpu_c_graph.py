@@ -1,17 +1,26 @@
 """The whole layer captured in a HIP graph (through torch.cuda.graph) and
 replayed: every replay, with eager work and synchronizations in between,
-must equal the eager output bit for bit. The layer makes no host
-synchronisation, allocates nothing, and clears its scalars with a kernel
-(no memset node), so it can be captured (nvfp4_cutedsl.py history,
-graph-compatibility commits)."""
+must equal the eager output bit for bit, and the replayed output must match
+the oracle layer within 1e-2 x max|oracle|, also after a new input. The
+layer makes no host synchronisation, allocates nothing, and clears its
+scalars with a kernel (no memset node), so it can be captured
+(nvfp4_cutedsl.py history, graph-compatibility commits)."""
 import numpy as np
 import pytest
 import torch
 
+import oracle as O
 import workloads as W
+from _parity_log import record
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
+TOL = 1e-2
+
+
+def rel_err(got, ref):
+    scale = float(np.abs(ref).max())
+    return float(np.abs(got - ref).max()) / scale if scale > 0 else float(np.abs(got).max())
 
 
 def log(msg):
@@ -62,11 +71,18 @@ def test_graph_replay_matches_eager(nv, name):
         torch.cuda.synchronize()
         log(f"{name}: replay {r}")
         assert torch.equal(out.view(torch.int16), eager.view(torch.int16)), f"replay {r} differs"
+    P = O.prepare_weights(wg, wu, wd)
+    err0 = rel_err(out.float().cpu().numpy(), O.bf16_to_f32(O.moe_forward(x, ids, w, cfg.expert_start, P).out))
     # a new input through the same graph: the replay follows the data
-    d_x.copy_(_bf16(W.make_activations(cfg)[::-1].copy()))
+    x2 = W.make_activations(cfg)[::-1].copy()
+    d_x.copy_(_bf16(x2))
     g.replay()
     torch.cuda.synchronize()
     replayed = out.clone()
     fwd()
     torch.cuda.synchronize()
     assert torch.equal(replayed.view(torch.int16), out.view(torch.int16))
+    err1 = rel_err(replayed.float().cpu().numpy(), O.bf16_to_f32(O.moe_forward(x2, ids, w, cfg.expert_start, P).out))
+    log(f"{name}: replay vs oracle rel err {err0:.3e}, with a new input {err1:.3e}")
+    record(f"graph:{name}", rel_err=max(err0, err1), replays_equal_eager=5)
+    assert err0 <= TOL and err1 <= TOL

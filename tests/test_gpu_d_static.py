@@ -5,9 +5,10 @@ reduction).
 
 Bar: the fixed-scale quantizer is bit-exact against the oracle (saturating
 and small-scale cases included); the L1 epilogue that writes h as NVFP4 is
-bit-exact against the fixed-scale quantizer applied to the BF16 h of the
-plain SiLU*up epilogue, and close to the oracle's codes; the layer with fixed
-scales equals the calibration pass bit for bit, and is within 1e-2 x
+bit-exact against the oracle's fixed-scale quantization of the BF16 h that
+the plain SiLU*up epilogue computes on the same inputs; the layer with fixed
+scales equals the calibration pass bit for bit, its h codes are the oracle's
+quantization of the calibration pass's h, and its output is within 1e-2 x
 max|oracle| of the oracle layer given the same scales.
 """
 import numpy as np
@@ -17,6 +18,8 @@ import torch
 import oracle as O
 import workloads as W
 from _cases import near_midpoint_blocks, quant_case
+from _layer_checks import check_static_h
+from _parity_log import record
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
@@ -84,8 +87,8 @@ def test_quantize_static_batched_and_zero_scale(nv):
 
 @pytest.mark.parametrize("seed", [3, 4])
 def test_quantize_static_near_midpoints(nv, seed):
-    # elements within a few float32 ulps of an E2M1 midpoint: the quantizer's
-    # float32 fast path must hand these blocks to its exact path
+    # elements within a few float32 ulps of an E2M1 midpoint, where a rounding
+    # decided from an inexact quotient would go the wrong way
     bits, gs = near_midpoint_blocks(seed)
     log(f"quantize_static near midpoints seed={seed} blocks={bits.shape[0]}")
     q, sf = nv.nvfp4_quantize_static(to_bf16(bits), to_dev(gs))
@@ -144,18 +147,22 @@ def test_gemm_silu_nvfp4(nv, case, tile_m, dual):
     torch.cuda.synchronize()
     got_q, got_sf = hq.cpu().numpy(), hsf.cpu().numpy()
     assert np.all(got_q[S:] == 0xAB) and np.all(got_sf[S:] == 0xCD), "rows outside the tiles were written"
-    # the epilogue's quantization is the fixed-scale quantizer applied to the same BF16 h
-    q2, sf2 = nv.nvfp4_quantize_static(h[:S].contiguous(), to_dev(np.array([gs_h], np.float32)))
-    torch.cuda.synchronize()
-    assert np.array_equal(got_q[:S], q2.cpu().numpy()) and np.array_equal(got_sf[:S], sf2.cpu().numpy())
-    # and close to the oracle's codes for its own h (h differs in float32 summation order only)
+    # the epilogue's quantization is the oracle's fixed-scale quantization of the BF16 h
+    # that the same GEMM computes (the GPU's h: float32 summation order is not the oracle's)
+    h_bits = h[:S].view(torch.int16).cpu().numpy().view(np.uint16)
+    oq, osf, _ = O.quantize(h_bits, gs=gs_h)
+    assert np.array_equal(got_sf[:S], osf), "epilogue block scales differ from the oracle's"
+    assert np.array_equal(got_q[:S], oq), "epilogue codes differ from the oracle's"
+    # and close to the oracle's codes for the oracle's own h
     if S:
-        oq, osf, _ = O.quantize(h_ref, gs=gs_h)
-        same = float((got_sf[:S] == osf).mean())
-        deq, odeq = O.dequantize(got_q[:S], got_sf[:S], gs_h), O.dequantize(oq, osf, gs_h)
-        cos = O.cosine(deq, odeq)
-        log(f"  scale codes equal {same:.4f}  cosine of dequantized h {cos:.6f}  saturated {(osf == 0x7E).sum()}")
-        assert same >= 0.95 and cos >= 0.995
+        oq2, osf2, _ = O.quantize(h_ref, gs=gs_h)
+        same = float((got_sf[:S] == osf2).mean())
+        cos = O.cosine(O.dequantize(got_q[:S], got_sf[:S], gs_h), O.dequantize(oq2, osf2, gs_h))
+        log(f"  bit-exact on the GPU's h; vs the oracle's own h: scale codes equal {same:.4f}, cosine of "
+            f"dequantized h {cos:.6f}, saturated blocks {(osf2 == 0x7E).sum()}")
+        record(f"gemm_silu_nvfp4:{case}:tile{tile_m}:dual{dual}", codes_bit_exact=True,
+               cosine_vs_oracle_h=cos)
+        assert cos >= 0.995
 
 
 # ------------------------------------------------------------------ layer
@@ -175,12 +182,21 @@ def test_layer_static(nv, name, fold):
     log(f"layer_static {name} fold={fold} T={cfg.tokens} k={cfg.top_k} L={cfg.num_local}")
     weights = nv.prepare_weights(to_bf16(wg), to_bf16(wu), to_bf16(wd), fold=fold)
     d_x, d_ids, d_w = to_bf16(x), to_dev(ids), to_dev(w)
-    # 1. with the scales the dynamic pass measures, the static pass is that pass
-    dyn = nv.nvfp4_moe_forward(weights, d_x, d_ids, d_w, cfg.expert_start)
+    # 1. with the scales the dynamic pass measures, the static pass is that pass, and
+    #    its h codes are the oracle's quantization (fixed gs_h) of the dynamic pass's h
+    T, k = ids.shape
+    cap = T * k
+    lay = nv.nvfp4_moe_ws_layout(T, k, cfg.hidden, cfg.inter, cfg.num_local)
+    ws_d = torch.empty(lay["end"], dtype=torch.uint8, device=DEV)
+    ws_s = torch.empty(lay["end"], dtype=torch.uint8, device=DEV)
+    dyn = nv.nvfp4_moe_forward(weights, d_x, d_ids, d_w, cfg.expert_start, ws=ws_d)
     gs_cal = nv.calibrate_static_gs(weights, d_x, d_ids, d_w, cfg.expert_start)
-    st = nv.nvfp4_moe_forward_static(weights, d_x, d_ids, d_w, cfg.expert_start, gs_cal)
+    st = nv.nvfp4_moe_forward_static(weights, d_x, d_ids, d_w, cfg.expert_start, gs_cal, ws=ws_s)
     torch.cuda.synchronize()
     assert torch.equal(st.view(torch.int16), dyn.view(torch.int16))
+    S = int(nv.ws_view(ws_d, lay, "offsets", torch.int32, (cfg.num_local + 1,))[-1].item())
+    h_bits = nv.ws_view(ws_d, lay, "h", torch.int16, (cap, cfg.inter))[:S].cpu().numpy().view(np.uint16)
+    check_static_h(nv, ws_s, lay, cap, cfg.inter, S, h_bits, gs_cal[1].item())
     # 2. against the oracle, both given the oracle's calibrated scales
     P = O.prepare_weights(wg, wu, wd, fold=fold)
     tr = O.moe_forward(x, ids, w, cfg.expert_start, P)
@@ -188,8 +204,6 @@ def test_layer_static(nv, name, fold):
     gs_o = np.array([tr.gs_x, tr.gs_h], np.float32)
     for scale in (1.0, 1.25):
         xs = W.bf16_bits(O.bf16_to_f32(x) * np.float32(scale))
-        T, k = ids.shape
-        lay = nv.nvfp4_moe_ws_layout(T, k, cfg.hidden, cfg.inter, cfg.num_local)
         ws_buf = torch.full((lay["end"] + 4096,), 0xA5, dtype=torch.uint8, device=DEV)   # canary bytes past the end
         ws = ws_buf[:lay["end"]]
         out = nv.nvfp4_moe_forward_static(weights, to_bf16(xs), d_ids, d_w, cfg.expert_start, to_dev(gs_o), ws=ws)
@@ -201,6 +215,7 @@ def test_layer_static(nv, name, fold):
         assert np.array_equal(nv.ws_view(ws, lay, "x_sf", torch.uint8, (T, H // 16)).cpu().numpy(), ref.x_sf)
         err = rel_err(out.float().cpu().numpy(), O.bf16_to_f32(ref.out))
         log(f"  x{scale}: out rel err {err:.3e}")
+        record(f"layer_static:{name}:fold{int(fold)}:x{scale}", rel_err=err, h_codes_bit_exact=True)
         assert err <= TOL
 
 
@@ -248,3 +263,10 @@ def test_layer_static_graph_replay(nv, name):
         torch.cuda.synchronize()
         log(f"layer_static graph: replay {r}")
         assert torch.equal(out.view(torch.int16), eager.view(torch.int16)), f"replay {r} differs"
+    # the replayed output against the oracle layer given the same fixed scales
+    gs_np = gs.cpu().numpy()
+    ref = O.moe_forward(x, ids, w, cfg.expert_start, O.prepare_weights(wg, wu, wd), static_gs=(gs_np[0], gs_np[1]))
+    err = rel_err(out.float().cpu().numpy(), O.bf16_to_f32(ref.out))
+    log(f"layer_static graph: replay vs oracle rel err {err:.3e}")
+    record(f"graph_static:{name}", rel_err=err, replays_equal_eager=3)
+    assert err <= TOL
