@@ -22,7 +22,8 @@
  *     one call to the next, and reads no environment variables. Its only
  *     process-wide state is launch sizes that depend on the device alone (CU
  *     count times resident workgroups per CU), queried on the first call on
- *     each device and kept per device.
+ *     each device and kept per device, and the device array (with its address
+ *     per device) that nvfp4_quantize_noalloc uses in place of a workspace.
  *   - Calls are asynchronous on `stream` (a hipStream_t; NULL = the default
  *     stream) and never synchronize with the host.
  *   - Arguments are validated on the host before anything is launched; a
@@ -82,6 +83,20 @@ int nvfp4moe_version(void);
 size_t nvfp4_quantize_ws_bytes(int64_t B, int64_t M, int64_t K);
 int nvfp4_quantize(const void* x_bf16, int64_t B, int64_t M, int64_t K, const float* amax_in,
                    uint8_t* q, uint8_t* sf, float* gs_out, void* ws, size_t ws_bytes, void* stream);
+
+/* nvfp4_quantize for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc):
+ * the same arguments, results, kernels and launches without the workspace.
+ * The amax partials live in a device array of the library, 256 KB on each
+ * device it runs on (allocated when the library's code is loaded there, kept
+ * until the process ends); its address is taken on the first call on a device.
+ * The call allocates and frees nothing. Calls on one device share that array,
+ * so calls that overlap on one device (concurrent streams, threads) race;
+ * with amax_in != NULL the array is not used. Requires B <= 128 (more tensors
+ * return NVFP4_ERR_WORKSPACE) and otherwise what nvfp4_quantize requires.
+ */
+int nvfp4_quantize_noalloc(const void* x_bf16, int64_t B, int64_t M, int64_t K, const float* amax_in,
+                           uint8_t* q, uint8_t* sf, float* gs_out, void* stream);
 
 /* Quantize with fixed global scales (nvfp4_cutedsl.py history, page 2,
  * static-scale commit: a warmup pass measures gs once; afterwards activations

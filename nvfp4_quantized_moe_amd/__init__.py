@@ -16,7 +16,7 @@ import torch
 
 __all__ = [
     "lib", "LIB_PATH", "NVFP4Error", "EPI_BF16", "EPI_SILU_MUL", "EPI_SILU_MUL_DUAL", "WS_REGIONS", "nvfp4_quantize",
-    "nvfp4_quantize_ws_bytes", "moe_route_slots", "moe_route_ws_bytes", "nvfp4_tile_table_len",
+    "nvfp4_quantize_ws_bytes", "nvfp4_quantize_noalloc", "moe_route_slots", "moe_route_ws_bytes", "nvfp4_tile_table_len",
     "nvfp4_grouped_gemm", "moe_weighted_scatter", "nvfp4_fold_scales", "nvfp4_packed_bytes",
     "nvfp4_pack_weights", "nvfp4_moe_forward", "nvfp4_quantize_static", "nvfp4_grouped_gemm_silu_nvfp4",
     "nvfp4_moe_forward_static", "calibrate_static_gs",
@@ -52,6 +52,7 @@ _status_string = _sig("nvfp4_status_string", ctypes.c_char_p, ctypes.c_int)
 _version = _sig("nvfp4moe_version", ctypes.c_int)
 _quantize_ws = _sig("nvfp4_quantize_ws_bytes", _sz, _i64, _i64, _i64)
 _quantize = _sig("nvfp4_quantize", ctypes.c_int, _vp, _i64, _i64, _i64, _vp, _vp, _vp, _vp, _vp, _sz, _vp)
+_quantize_noalloc = _sig("nvfp4_quantize_noalloc", ctypes.c_int, _vp, _i64, _i64, _i64, _vp, _vp, _vp, _vp, _vp)
 _quantize_static = _sig("nvfp4_quantize_static", ctypes.c_int, _vp, _i64, _i64, _i64, _vp, _vp, _vp, _vp)
 _route_ws = _sig("moe_route_ws_bytes", _sz, _i32, _i32, _i32)
 _tile_len = _sig("nvfp4_tile_table_len", _i64, _i64, _i32, _i32)
@@ -154,6 +155,22 @@ def nvfp4_quantize(x, amax_in=None, q=None, sf=None, gs=None, ws=None):
     if not batched:
         return q[0], sf[0], gs
     return q, sf, gs
+
+
+def nvfp4_quantize_noalloc(x, q, sf, gs, amax_in=None):
+    """nvfp4_quantize into caller-provided q, sf, gs without a workspace: the
+    library keeps the amax partials in its own device array (at most 128
+    tensors; calls that overlap on one device race). Allocates nothing."""
+    _dev(x, torch.bfloat16, "x")
+    if x.dim() not in (2, 3):
+        raise ValueError(f"x: expected [M, K] or [B, M, K], got shape {tuple(x.shape)}")
+    B, M, K = (x.shape if x.dim() == 3 else (1, *x.shape))
+    _buf(q, torch.uint8, B * M * K // 2, "q")
+    _buf(sf, torch.uint8, B * M * K // 16, "sf")
+    _buf(gs, torch.float32, B, "gs")
+    _buf(amax_in, torch.float32, B, "amax_in")
+    _check(_quantize_noalloc(_ptr(x), B, M, K, _ptr(amax_in), _ptr(q), _ptr(sf), _ptr(gs), _stream()),
+           "nvfp4_quantize_noalloc")
 
 
 def nvfp4_quantize_static(x, gs, q=None, sf=None):

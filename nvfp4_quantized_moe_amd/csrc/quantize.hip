@@ -215,6 +215,45 @@ extern "C" int nvfp4_quantize_static(const void* x_bf16, int64_t B, int64_t M, i
   return nvfp4_launch_quantize_static(x_bf16, B, M, K, gs_in, nullptr, q, sf, (hipStream_t)stream);
 }
 
+// ------------------------------------------- quantize without a workspace
+// Amax partials of nvfp4_quantize_noalloc: kAmaxGrid words per tensor for at
+// most kNoAllocMaxTensors tensors (256 KB), one copy on every device the
+// library runs on, held until the process ends. Every call on a device shares
+// that device's copy; the amax pass writes every partial the quantize kernel
+// of the same call reads, so nothing has to start at zero.
+constexpr int kNoAllocMaxTensors = 128;
+static __device__ __align__(256) uint32_t scratch[kNoAllocMaxTensors * kAmaxGrid];
+
+// Device address of `scratch` on each device, taken once with that device
+// current (in host code the array's name is only a host-side stand-in).
+static std::atomic<uintptr_t> g_scratch_addr[kMaxDevices];
+
+static uint32_t* noalloc_scratch(int dev) {
+  uintptr_t a = g_scratch_addr[dev].load(std::memory_order_acquire);
+  if (a == 0) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr) return nullptr;
+    a = reinterpret_cast<uintptr_t>(p);
+    g_scratch_addr[dev].store(a, std::memory_order_release);
+  }
+  return reinterpret_cast<uint32_t*>(a);
+}
+
+extern "C" int nvfp4_quantize_noalloc(const void* x_bf16, int64_t B, int64_t M, int64_t K, const float* amax_in,
+                                      uint8_t* q, uint8_t* sf, float* gs_out, void* stream) {
+  if (B < 1 || B > 65535 || M < 0 || K <= 0 || K % 32 != 0) return NVFP4_ERR_SHAPE;
+  if (B > kNoAllocMaxTensors) return NVFP4_ERR_WORKSPACE;
+  if (M > 0 && (!x_bf16 || !q || !sf)) return NVFP4_ERR_NULL;
+  if (!gs_out) return NVFP4_ERR_NULL;
+  if (M > 0 && (!nvfp4_aligned16(x_bf16) || !nvfp4_aligned16(q) || !nvfp4_aligned16(sf))) return NVFP4_ERR_ALIGN;
+  const int dev = nvfp4_current_device();
+  if (dev < 0) return NVFP4_ERR_HIP;
+  uint32_t* ws = noalloc_scratch(dev);
+  if (!ws) return NVFP4_ERR_HIP;
+  return nvfp4_launch_quantize(x_bf16, B, M, K, amax_in, nullptr, q, sf, gs_out, ws, nullptr, 0,
+                               (hipStream_t)stream);
+}
+
 extern "C" size_t nvfp4_quantize_ws_bytes(int64_t B, int64_t M, int64_t K) {
   (void)M;
   (void)K;

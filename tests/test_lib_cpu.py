@@ -109,6 +109,11 @@ def test_invalid_arguments_are_rejected_before_launch():
     assert nv._forward(ctypes.byref(huge), buf, 4, buf, buf, 2, 0, buf, buf, 1 << 62, s) == 2
     w = nv._Weights(8, 256, 128, 4096, 4096, 4096, 4096, 2)     # unknown gate/up scale mode
     assert nv._forward(ctypes.byref(w), buf, 4, buf, buf, 2, 0, buf, buf, 1 << 30, s) == 6
+    # quantize without a workspace: more tensors than its array holds, bad K, NULL gs
+    assert nv._quantize_noalloc(buf, 129, 4, 64, null, buf, buf, buf, s) == 4
+    assert nv._quantize_noalloc(buf, 1, 4, 48, null, buf, buf, buf, s) == 2
+    assert nv._quantize_noalloc(buf, 1, 4, 64, null, buf, buf, null, s) == 1
+    assert nv._quantize_noalloc(odd, 1, 4, 64, null, buf, buf, buf, s) == 3
     # fixed-scale entry points: NULL scales, bad shapes, unknown gate/up scale mode
     assert nv._quantize_static(buf, 1, 4, 64, null, buf, buf, s) == 1
     assert nv._quantize_static(buf, 1, 4, 48, buf, buf, buf, s) == 2
