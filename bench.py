@@ -51,22 +51,6 @@ def kernel_source_sha() -> str:
     return hashlib.sha256("\n".join(code).encode()).hexdigest()[:16]
 
 
-def read_traffic(workload: str):
-    """Per-launch HBM bytes of the L1 GEMM from the committed counter summary,
-    or None when absent or taken on a different kernel source."""
-    p = os.path.join(PROFILE_DIR, f"l1_gemm_{workload}_traffic.txt")
-    if not os.path.exists(p):
-        return None
-    kv = {}
-    for line in open(p):
-        if "=" in line and not line.lstrip().startswith("#"):
-            k, v = line.split("=", 1)
-            kv[k.strip()] = v.strip()
-    if kv.get("kernel_source_sha") != kernel_source_sha():
-        return None
-    return float(kv["hbm_bytes_per_launch"])
-
-
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -78,12 +62,14 @@ def main():
     ap.add_argument("--settle-ms", type=float, default=300.0,
                     help="untimed GPU time spent on the workload before the warmup steps, so that "
                          "the clocks leave their start-of-load transient (steady state is timed)")
-    ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-decode", action="store_true",
+                    help="time the headline workload only (no decode, tiny, quantizer, skewed, static-scale "
+                         "and peak objects)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy (elementwise negate) three times, "
                          "so that counter runs can scale FETCH_SIZE / WRITE_SIZE")
     ap.add_argument("--summarize-traffic", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
-                    help="write the per-launch HBM traffic of the L1 GEMM from two rocprofv3 --pmc "
+                    help="write the per-launch HBM traffic of the grouped GEMMs from two rocprofv3 --pmc "
                          "csv runs (FETCH_SIZE, WRITE_SIZE) to profiles/ and exit")
     ap.add_argument("--summarize-trace", metavar="TRACE_DIR",
                     help="write the per-kernel table of a rocprofv3 --kernel-trace --stats csv run to "
@@ -93,9 +79,15 @@ def main():
     ap.add_argument("--quantize-only", action="store_true",
                     help="time only the activation quantizer on the 4096 x 7168 tensor and print its object "
                          "(for a kernel trace of the quantizer alone); not the benchmark line")
+    ap.add_argument("--peaks", action="store_true",
+                    help="measure the achievable HBM streaming-read rate and MFMA rate on this GPU and print "
+                         "them; not the benchmark line")
     ap.add_argument("--summarize-mfma", metavar="PMC_DIR",
-                    help="write the MFMA counters of the L1 GEMM from a rocprofv3 --pmc csv run to "
+                    help="write the MFMA counters of the grouped GEMMs from a rocprofv3 --pmc csv run to "
                          "profiles/ and exit")
+    ap.add_argument("--summarize-valu", metavar="PMC_DIR",
+                    help="write the VALU/SALU/MFMA instruction counts of the grouped GEMMs from a rocprofv3 "
+                         "--pmc csv run to profiles/ and exit")
     args = ap.parse_args()
     if args.summarize_traffic:
         summarize_traffic(args.config, *args.summarize_traffic)
@@ -105,6 +97,9 @@ def main():
         return
     if args.summarize_mfma:
         summarize_mfma(args.config, args.summarize_mfma)
+        return
+    if args.summarize_valu:
+        summarize_valu(args.config, args.summarize_valu)
         return
     if args.config == "quantize" and not args.quantize_only:
         raise SystemExit("bench.py: --config quantize only names the trace of a --quantize-only run")
@@ -123,17 +118,16 @@ def main():
     if args.quantize_only:
         print(json.dumps({"quantize": quantize_c1(nv, W, dev, args.settle_ms)}), flush=True)
         return
+    if args.peaks:
+        print(json.dumps({"achievable_peaks": achievable_peaks(dev)}), flush=True)
+        return
     cfg = W.get_config(args.config)
     t0 = time.time()
     ids, w = W.make_router(cfg)
     x = W.make_activations(cfg)
     wg, wu, wd = W.make_weights(cfg)
     log(f"generated {cfg.name} inputs in {time.time() - t0:.1f}s")
-
-    def bf16(a):
-        return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev)
-
-    weights = nv.prepare_weights(bf16(wg), bf16(wu), bf16(wd))
+    weights = nv.prepare_weights(_bf16(wg, dev), _bf16(wu, dev), _bf16(wd, dev))
     torch.cuda.synchronize()
     if args.copy_calibration:
         src = torch.ones(COPY_CAL_BYTES // 4, dtype=torch.float32, device=dev)
@@ -143,73 +137,14 @@ def main():
         torch.cuda.synchronize()
         del src, dst
 
-    def run_layer(cfg_, ids_, w_, x_, steps, warmup):
-        T, k = ids_.shape
-        d_x, d_ids, d_w = bf16(x_), torch.from_numpy(ids_).to(dev), torch.from_numpy(w_).to(dev)
-        out = torch.empty((T, cfg_.hidden), dtype=torch.bfloat16, device=dev)
-        lay = nv.nvfp4_moe_ws_layout(T, k, cfg_.hidden, cfg_.inter, cfg_.num_local)
-        ws = torch.empty(lay["end"], dtype=torch.uint8, device=dev)
-
-        def step():
-            nv.nvfp4_moe_forward(weights, d_x, d_ids, d_w, cfg_.expert_start, out=out, ws=ws)
-
-        settle(step, args.settle_ms)
-        for _ in range(warmup):
-            step()
-        torch.cuda.synchronize()
-        t = time.perf_counter()
-        for _ in range(steps):
-            step()
-        torch.cuda.synchronize()
-        ms = (time.perf_counter() - t) * 1e3 / steps
-        # the dominant kernel, L1 grouped GEMM, timed alone on the stream it is launched on
-        cap = T * k
-        S = int(nv.ws_view(ws, lay, "offsets", torch.int32, (cfg_.num_local + 1,))[-1].item())
-        counts = nv.ws_view(ws, lay, "counts", torch.int32, (cfg_.num_local,)).cpu().numpy()
-        tile_m = nv.nvfp4_moe_tile_m(T, k, cfg_.num_local)
-        gargs = (nv.ws_view(ws, lay, "x_q", torch.uint8, (T, cfg_.hidden // 2)),
-                 nv.ws_view(ws, lay, "x_sf", torch.uint8, (T, cfg_.hidden // 16)),
-                 nv.ws_view(ws, lay, "slot_token", torch.int32, (cap,)),
-                 nv.ws_view(ws, lay, "scalars", torch.float32, (4,))[0:1],
-                 weights.w1, weights.w1_gs,
-                 nv.ws_view(ws, lay, "offsets", torch.int32, (cfg_.num_local + 1,)),
-                 nv.ws_view(ws, lay, "tiles", torch.int32, (nv.nvfp4_tile_table_len(cap, cfg_.num_local, tile_m),)))
-        h = torch.empty((cap, cfg_.inter), dtype=torch.bfloat16, device=dev)
-        amax = torch.zeros(1, dtype=torch.float32, device=dev)
-        stream = torch.cuda.current_stream()
-        ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        n_l1 = max(steps, 5)
-        settle(lambda: nv.nvfp4_grouped_gemm(*gargs, cap, tile_m, nv.EPI_SILU_MUL, d=h, amax_out=amax),
-               args.settle_ms / 2)
-        ev0.record(stream)
-        for _ in range(n_l1):
-            nv.nvfp4_grouped_gemm(*gargs, cap, tile_m, nv.EPI_SILU_MUL, d=h, amax_out=amax)
-        ev1.record(stream)
-        torch.cuda.synchronize()
-        l1_ms = ev0.elapsed_time(ev1) / n_l1
-        return dict(ms=ms, S=S, touched=int((counts > 0).sum()), l1_ms=l1_ms, tile_m=tile_m, out=out)
-
     log(f"timing {cfg.name}: {args.warmup} warmup + {args.steps} steps")
-    r = run_layer(cfg, ids, w, x, args.steps, args.warmup)
+    r = measure_layer(nv, weights, cfg, ids, w, x, dev, args.steps, args.warmup, args.settle_ms,
+                      flushed=cfg.name != "decode")
     T, k, H, I = cfg.tokens, cfg.top_k, cfg.hidden, cfg.inter
     S = r["S"]
     tok_s = T / (r["ms"] * 1e-3)
-    l1_flop = S * 2.0 * (2 * I) * H                       # per slot: 2 * 2I * H (88.08 MFLOP)
     layer_flop = S * 2.0 * (2 * I * H + H * I)            # per slot: 132.12 MFLOP
-    l1_tflops = l1_flop / (r["l1_ms"] * 1e-3) / 1e12
-    l1_w_bytes = r["touched"] * 2 * I * (H // 2 + H // 16)  # FP4 weights + scales of touched experts
-    traffic = read_traffic(cfg.name)
-    roofline = {
-        "kernel": "grouped_gemm L1 (gate+up, SiLU*up epilogue)",
-        "bound": "mfma", "achieved": round(l1_tflops, 2), "peak": PEAK_FP16_TFLOPS, "unit": "TFLOP/s",
-        "frac": round(l1_tflops / PEAK_FP16_TFLOPS, 4), "traffic": traffic,
-        "avg_launch_ms": round(r["l1_ms"], 4), "flop_per_launch": l1_flop,
-        "frac_of_fp4_peak": round(l1_tflops / PEAK_FP4_TFLOPS, 4),
-    }
-    if cfg.name == "decode":
-        gbs = l1_w_bytes / (r["l1_ms"] * 1e-3) / 1e9
-        roofline.update(bound="hbm", achieved=round(gbs, 1), peak=PEAK_HBM_GBS, unit="GB/s",
-                        frac=round(gbs / PEAK_HBM_GBS, 4), bytes_per_launch=l1_w_bytes)
+    roof_l1, roof_l2 = gemm_rooflines(cfg, r)
     result = {
         "metric": METRIC, "value": round(tok_s, 1), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(r["ms"], 4), "higher_is_better": True, "scaling": "weak",
@@ -219,97 +154,206 @@ def main():
                    "tokens": T, "top_k": k, "local_experts": cfg.num_local, "hidden": H, "inter": I,
                    "slots": S, "touched_experts": r["touched"], "tile_m": r["tile_m"]},
         "layer_tflops": round(layer_flop / (r["ms"] * 1e-3) / 1e12, 2),
-        "roofline": roofline,
+        "roofline": roof_l1,
+        "roofline_l2": roof_l2,
+        "step_ms": r["step"],
+        "stages_ms": r["stages"],
+        "ms_per_step_without_stage_events": round(r["plain_ms"], 4),
+        "timing_note": ("value and ms_per_step: wall clock over the timed steps (synchronized on both sides), "
+                        "each step with HIP events on the layer's stream around its L1 grouped GEMM; roofline: "
+                        "algorithmic work over the mean L1 launch time from those events; step_ms, stages_ms "
+                        "and roofline_l2: a second pass of as many steps with events between all stages "
+                        "(median, p10, p90 per step; medians per stage; mean L2 launch); "
+                        "ms_per_step_without_stage_events: a third pass without events"),
     }
+    if "flushed" in r:
+        result["step_ms_flushed"] = r["flushed"]
     if cfg.name == "prefill" and not args.no_decode:
-        dcfg = W.get_config("decode")
-        dids, dw = W.make_router(dcfg)
-        dx = W.make_activations(dcfg)
-        rd = run_layer(dcfg, dids, dw, dx, max(args.steps, 50), args.warmup)
-        bytes_w = rd["touched"] * (2 * I * (H // 2 + H // 16) + H * (I // 2 + I // 16))
-        gbs = bytes_w / (rd["ms"] * 1e-3) / 1e9
-        l1b = rd["touched"] * 2 * I * (H // 2 + H // 16)
-        l1g = l1b / (rd["l1_ms"] * 1e-3) / 1e9
-        result["decode"] = {
-            "workload": "decode shard: T=64, top-8 of 384, local 96..143, same weights",
-            "tokens_per_s": round(dcfg.tokens / (rd["ms"] * 1e-3), 1), "ms_per_step": round(rd["ms"], 4),
-            "touched_experts": rd["touched"], "slots": rd["S"],
-            "layer_weight_GBs": round(gbs, 1), "layer_hbm_frac": round(gbs / PEAK_HBM_GBS, 4),
-            "l1_gemm_ms": round(rd["l1_ms"], 4), "l1_gemm_GBs": round(l1g, 1),
-            "l1_gemm_hbm_frac": round(l1g / PEAK_HBM_GBS, 4),
-        }
-    if cfg.name == "prefill" and not args.no_decode:
-        result["decode"]["flushed"] = decode_flushed(nv, weights, W.get_config("decode"), dev)
-        result["decode"]["graph"] = decode_graph(nv, weights, W.get_config("decode"), dev, max(args.steps, 50))
+        result["decode"] = decode_shard(nv, weights, W, dev, max(args.steps, 50), args.warmup, args.settle_ms)
+        result["tiny"] = tiny_layer(nv, W, dev, args.settle_ms)
         result["quantize"] = quantize_c1(nv, W, dev, args.settle_ms)
-        result["skewed"] = skewed_shard(nv, W, dev, args.settle_ms, max(args.steps, 10))
+        result["skewed"] = skewed_shard(nv, W, dev, args.settle_ms, max(args.steps, 10), args.warmup)
         result["static_scales"] = static_scales(nv, weights, W, dev, args.settle_ms)
+        result["achievable_peaks"] = achievable_peaks(dev)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(cfg, ids, w, x, wg, wu, wd, T)
     print(json.dumps(result), flush=True)
 
 
-def decode_flushed(nv, weights, dcfg, dev, steps=30):
-    """Decode shard with the last-level cache (256 MB) flushed before every step:
-    each step timed alone with events, after a 512 MB read outside the events."""
+def _bf16(a, dev):
     import torch
-    import workloads as W
-    ids, w = W.make_router(dcfg)
-    x = W.make_activations(dcfg)
-    T, k = ids.shape
-    d_x = torch.from_numpy(x.view(np.int16)).view(torch.bfloat16).to(dev)
-    d_ids, d_w = torch.from_numpy(ids).to(dev), torch.from_numpy(w).to(dev)
-    lay = nv.nvfp4_moe_ws_layout(T, k, dcfg.hidden, dcfg.inter, dcfg.num_local)
-    ws = torch.empty(lay["end"], dtype=torch.uint8, device=dev)
-    out = torch.empty((T, dcfg.hidden), dtype=torch.bfloat16, device=dev)
-    scratch = torch.ones((512 << 20) // 4, dtype=torch.float32, device=dev)
-    sink = torch.empty((), dtype=torch.float32, device=dev)
-    # flush (a 512 MB read, which leaves no dirty lines to write back), then the
-    # step between two events, all enqueued without host waits, so the host's
-    # launch latency is not inside the events
-    evs = []
-    for i in range(steps + 3):
-        torch.sum(scratch, dim=0, out=sink)
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
+
+
+def stats(times_ms):
+    a = np.asarray(times_ms, np.float64)
+    return {"median": round(float(np.median(a)), 4), "p10": round(float(np.percentile(a, 10)), 4),
+            "p90": round(float(np.percentile(a, 90)), 4), "n": int(a.size)}
+
+
+class Flush:
+    """Evicts the 256 MB last-level cache: a 512 MB read (no dirty lines left to
+    write back during the step that follows)."""
+
+    def __init__(self, dev):
+        import torch
+        self.buf = torch.ones((512 << 20) // 4, dtype=torch.float32, device=dev)
+        self.sink = torch.empty((), dtype=torch.float32, device=dev)
+
+    def __call__(self):
+        import torch
+        torch.sum(self.buf, dim=0, out=self.sink)
+
+
+def _events(n):
+    """n timing events, each recorded once so that it exists (the library
+    records them again on its stream)."""
+    import torch
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(n)]
+    for e in evs:
+        e.record()
+    return evs
+
+
+def per_call_times(fn, n, flush=None):
+    """Times of n calls of fn, each between two events on the current stream;
+    with flush, the cache is flushed before every call (outside the events).
+    Everything is enqueued without host waits."""
+    import torch
+    pairs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+    for e0, e1 in pairs:
+        if flush:
+            flush()
         e0.record()
-        nv.nvfp4_moe_forward(weights, d_x, d_ids, d_w, dcfg.expert_start, out=out, ws=ws)
+        fn()
         e1.record()
-        evs.append((e0, e1))
     torch.cuda.synchronize()
-    times = [a.elapsed_time(b) for a, b in evs[3:]]
-    counts = nv.ws_view(ws, lay, "counts", torch.int32, (dcfg.num_local,)).cpu().numpy()
-    touched = int((counts > 0).sum())
-    H, I = dcfg.hidden, dcfg.inter
-    bytes_w = touched * (2 * I * (H // 2 + H // 16) + H * (I // 2 + I // 16))
-    med = float(np.median(times))
-    return {"ms_per_step_median": round(med, 4), "ms_p10": round(float(np.percentile(times, 10)), 4),
-            "ms_p90": round(float(np.percentile(times, 90)), 4),
-            "tokens_per_s": round(T / (med * 1e-3), 1),
-            "layer_weight_GBs": round(bytes_w / (med * 1e-3) / 1e9, 1),
-            "layer_hbm_frac": round(bytes_w / (med * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
+    return [a.elapsed_time(b) for a, b in pairs]
 
 
-def decode_graph(nv, weights, dcfg, dev, steps):
-    """Decode shard with the whole layer captured once in a HIP graph (through
-    torch.cuda.graph) and replayed back to back: the launch latency of the
-    layer's small kernels is what this removes."""
+def measure_layer(nv, weights, cfg, ids, w, x, dev, steps, warmup, settle_ms, flushed=False):
+    """The timed region: `steps` layer steps back to back, each through
+    nvfp4_moe_forward_stage_events with HIP events recorded on the layer's
+    stream only just before and just after the L1 grouped GEMM (a timing
+    event costs a few microseconds); wall clock around the region
+    (synchronized on both sides) gives ms_per_step, the events the L1 launch
+    times. Then a pass of the same number of steps with events between all
+    stages (per-step and per-stage times; the L2 launch times), a pass
+    without events, and optionally steps with the cache flushed before each."""
     import torch
-    import workloads as W
+    T, k = ids.shape
+    d_x, d_ids, d_w = _bf16(x, dev), torch.from_numpy(ids).to(dev), torch.from_numpy(w).to(dev)
+    out = torch.empty((T, cfg.hidden), dtype=torch.bfloat16, device=dev)
+    lay = nv.nvfp4_moe_ws_layout(T, k, cfg.hidden, cfg.inter, cfg.num_local)
+    ws = torch.empty(lay["end"], dtype=torch.uint8, device=dev)
+    plain = lambda: nv.nvfp4_moe_forward(weights, d_x, d_ids, d_w, cfg.expert_start, out=out, ws=ws)
+    staged = lambda ev: nv.nvfp4_moe_forward_stage_events(weights, d_x, d_ids, d_w, cfg.expert_start, ev,
+                                                          out=out, ws=ws)
+    ns = len(nv.STAGES) + 1
+    i_l1 = nv.STAGES.index("a4_a5_l1_gemm")
+    l1_evs = [_events(2) for _ in range(steps)]
+    l1_only = [[None] * ns for _ in range(steps)]
+    for i in range(steps):
+        l1_only[i][i_l1], l1_only[i][i_l1 + 1] = l1_evs[i]
+    all_evs = [_events(ns) for _ in range(steps)]
+    settle(plain, settle_ms)
+    for _ in range(warmup):
+        plain()
+    torch.cuda.synchronize()
+    t = time.perf_counter()
+    for i in range(steps):
+        staged(l1_only[i])
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t) * 1e3 / steps
+    l1 = [a.elapsed_time(b) for a, b in l1_evs]
+    for i in range(steps):
+        staged(all_evs[i])
+    torch.cuda.synchronize()
+    step = [e[0].elapsed_time(e[-1]) for e in all_evs]
+    stage = {name: [e[i].elapsed_time(e[i + 1]) for e in all_evs] for i, name in enumerate(nv.STAGES)}
+    res = dict(ms=ms, step=stats(step),
+               stages={n: round(float(np.median(v)), 4) for n, v in stage.items()},
+               l1_ms=float(np.mean(l1)), l2_ms=float(np.mean(stage["a7_l2_gemm"])))
+    t = time.perf_counter()
+    for _ in range(steps):
+        plain()
+    torch.cuda.synchronize()
+    res["plain_ms"] = (time.perf_counter() - t) * 1e3 / steps
+    if flushed:
+        res["flushed"] = stats(per_call_times(plain, steps, Flush(dev)))
+    counts = nv.ws_view(ws, lay, "counts", torch.int32, (cfg.num_local,)).cpu().numpy()
+    res.update(S=int(counts.sum()), touched=int((counts > 0).sum()),
+               tile_m=nv.nvfp4_moe_tile_m(T, k, cfg.num_local), out=out, d=(d_x, d_ids, d_w), ws=ws, lay=lay)
+    return res
+
+
+def gemm_rooflines(cfg, r):
+    """Roofline objects of the L1 and L2 grouped GEMMs from the mean launch
+    times of the timed region: algorithmic FLOP (slots x 2 x N x K, padding
+    rows not counted) against the dense fp16 MFMA peak; for decode-shaped
+    batches, algorithmic weight bytes (FP4 values + E4M3 scales of the
+    touched experts) against HBM. traffic: HBM bytes per launch from the
+    committed counter summary of the current GEMM source, else null."""
+    H, I, S, nt = cfg.hidden, cfg.inter, r["S"], r["touched"]
+    out = []
+    for gemm, name, ms, n, kk in (("l1", "L1 grouped GEMM (gate+up, SiLU*up epilogue)", r["l1_ms"], 2 * I, H),
+                                  ("l2", "L2 grouped GEMM (down_proj)", r["l2_ms"], H, I)):
+        flop = S * 2.0 * n * kk
+        wbytes = nt * n * (kk // 2 + kk // 16)
+        roof = {"kernel": name, "bound": "mfma", "achieved": round(flop / (ms * 1e-3) / 1e12, 2),
+                "peak": PEAK_FP16_TFLOPS, "unit": "TFLOP/s", "frac": round(flop / (ms * 1e-3) / 1e12 /
+                                                                             PEAK_FP16_TFLOPS, 4),
+                "traffic": read_traffic(cfg.name, gemm), "avg_launch_ms": round(ms, 4), "flop_per_launch": flop,
+                "weight_bytes_per_launch": wbytes}
+        if cfg.name == "decode":
+            gbs = wbytes / (ms * 1e-3) / 1e9
+            roof.update(bound="hbm", achieved=round(gbs, 1), peak=PEAK_HBM_GBS, unit="GB/s",
+                        frac=round(gbs / PEAK_HBM_GBS, 4))
+        out.append(roof)
+    return out
+
+
+def decode_shard(nv, weights, W, dev, steps, warmup, settle_ms):
+    """Decode shard (64 tokens, same weights): the evented timed steps, the L1
+    and L2 rooflines against HBM, steps with a cold last-level cache, and the
+    whole layer replayed from a HIP graph."""
+    dcfg = W.get_config("decode")
     ids, w = W.make_router(dcfg)
     x = W.make_activations(dcfg)
-    T, k = ids.shape
-    d_x = torch.from_numpy(x.view(np.int16)).view(torch.bfloat16).to(dev)
-    d_ids, d_w = torch.from_numpy(ids).to(dev), torch.from_numpy(w).to(dev)
-    lay = nv.nvfp4_moe_ws_layout(T, k, dcfg.hidden, dcfg.inter, dcfg.num_local)
-    ws = torch.empty(lay["end"], dtype=torch.uint8, device=dev)
-    out = torch.empty((T, dcfg.hidden), dtype=torch.bfloat16, device=dev)
-    fwd = lambda: nv.nvfp4_moe_forward(weights, d_x, d_ids, d_w, dcfg.expert_start, out=out, ws=ws)
+    rd = measure_layer(nv, weights, dcfg, ids, w, x, dev, steps, warmup, settle_ms, flushed=True)
+    H, I = dcfg.hidden, dcfg.inter
+    bytes_w = rd["touched"] * (2 * I * (H // 2 + H // 16) + H * (I // 2 + I // 16))
+    gbs = bytes_w / (rd["ms"] * 1e-3) / 1e9
+    l1, l2 = gemm_rooflines(dcfg, rd)
+    fl = rd["flushed"]["median"]
+    res = {
+        "workload": "decode shard: T=64, top-8 of 384, local 96..143, same weights",
+        "tokens_per_s": round(dcfg.tokens / (rd["ms"] * 1e-3), 1), "ms_per_step": round(rd["ms"], 4),
+        "ms_per_step_without_stage_events": round(rd["plain_ms"], 4),
+        "touched_experts": rd["touched"], "slots": rd["S"], "weight_bytes_per_step": bytes_w,
+        "layer_weight_GBs": round(gbs, 1), "layer_hbm_frac": round(gbs / PEAK_HBM_GBS, 4),
+        "step_ms": rd["step"], "stages_ms": rd["stages"], "roofline_l1": l1, "roofline_l2": l2,
+        "flushed": dict(rd["flushed"], layer_hbm_frac=round(bytes_w / (fl * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)),
+    }
+    res["graph"] = layer_graph(nv, weights, dcfg, rd, dev, steps, bytes_w)
+    return res
+
+
+def layer_graph(nv, weights, cfg, r, dev, steps, bytes_w=None):
+    """The whole layer captured once in a HIP graph (torch.cuda.graph) and
+    replayed: back-to-back replays (wall clock and per-replay events) and
+    whether the replay equals the eager output bit for bit."""
+    import torch
+    d_x, d_ids, d_w = r["d"]
+    out, ws = r["out"], r["ws"]
+    fwd = lambda: nv.nvfp4_moe_forward(weights, d_x, d_ids, d_w, cfg.expert_start, out=out, ws=ws)
     s = torch.cuda.Stream()
     s.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(s):
         for _ in range(3):
             fwd()
     torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
     eager = out.clone()
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g):
@@ -325,49 +369,52 @@ def decode_graph(nv, weights, dcfg, dev, steps):
     e1.record()
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / steps
-    counts = nv.ws_view(ws, lay, "counts", torch.int32, (dcfg.num_local,)).cpu().numpy()
-    touched = int((counts > 0).sum())
-    H, I = dcfg.hidden, dcfg.inter
-    bytes_w = touched * (2 * I * (H // 2 + H // 16) + H * (I // 2 + I // 16))
-    return {"ms_per_step": round(ms, 4), "tokens_per_s": round(T / (ms * 1e-3), 1),
-            "layer_weight_GBs": round(bytes_w / (ms * 1e-3) / 1e9, 1),
-            "layer_hbm_frac": round(bytes_w / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
-            "replay_equals_eager": same}
+    res = {"ms_per_step": round(ms, 4), "tokens_per_s": round(cfg.tokens / (ms * 1e-3), 1),
+           "replay_ms": stats(per_call_times(g.replay, steps)), "replay_equals_eager": same}
+    if bytes_w:
+        res["layer_hbm_frac"] = round(bytes_w / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)
+    return res
 
 
-def skewed_shard(nv, W, dev, settle_ms, steps):
+def tiny_layer(nv, W, dev, settle_ms, steps=100):
+    """The tiny layer (32 tokens, 8 experts, H=256, I=128): latency of one
+    eager step and of one graph replay."""
+    cfg = W.get_config("tiny")
+    ids, w = W.make_router(cfg)
+    x = W.make_activations(cfg)
+    wg, wu, wd = W.make_weights(cfg)
+    weights = nv.prepare_weights(_bf16(wg, dev), _bf16(wu, dev), _bf16(wd, dev))
+    r = measure_layer(nv, weights, cfg, ids, w, x, dev, steps, 5, settle_ms / 10)
+    g = layer_graph(nv, weights, cfg, r, dev, steps)
+    return {"workload": "tiny layer: T=32, top-2 of 8 experts (all local), H=256, I=128",
+            "step_latency_us": {k: (round(v * 1e3, 2) if k != "n" else v) for k, v in r["step"].items()},
+            "graph_replay_latency_us": {k: (round(v * 1e3, 2) if k != "n" else v)
+                                        for k, v in g["replay_ms"].items()},
+            "stages_us": {k: round(v * 1e3, 2) for k, v in r["stages"].items()}}
+
+
+def skewed_shard(nv, W, dev, settle_ms, steps, warmup):
     """Skewed-load shard (16384 tokens, Zipf popularity with empty and hot
-    local experts, W_up 30x): layer throughput and grouped-GEMM FLOP rate."""
+    local experts, W_up 30x): throughput, per-step distribution (warm and
+    flushed), per-stage times and the rooflines of both grouped GEMMs."""
     import torch
     cfg = W.get_config("skewed")
     ids, w = W.make_router(cfg)
     x = W.make_activations(cfg)
     wg, wu, wd = W.make_weights(cfg)
-    bf = lambda a: torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev)
-    weights = nv.prepare_weights(bf(wg), bf(wu), bf(wd))
+    weights = nv.prepare_weights(_bf16(wg, dev), _bf16(wu, dev), _bf16(wd, dev))
     del wg, wu, wd
-    T, k = ids.shape
-    d_x, d_ids, d_w = bf(x), torch.from_numpy(ids).to(dev), torch.from_numpy(w).to(dev)
-    lay = nv.nvfp4_moe_ws_layout(T, k, cfg.hidden, cfg.inter, cfg.num_local)
-    ws = torch.empty(lay["end"], dtype=torch.uint8, device=dev)
-    out = torch.empty((T, cfg.hidden), dtype=torch.bfloat16, device=dev)
-    step = lambda: nv.nvfp4_moe_forward(weights, d_x, d_ids, d_w, cfg.expert_start, out=out, ws=ws)
-    settle(step, settle_ms)
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record()
-    for _ in range(steps):
-        step()
-    e1.record()
-    torch.cuda.synchronize()
-    ms = e0.elapsed_time(e1) / steps
-    counts = nv.ws_view(ws, lay, "counts", torch.int32, (cfg.num_local,)).cpu().numpy()
-    S = int(counts.sum())
-    H, I = cfg.hidden, cfg.inter
+    r = measure_layer(nv, weights, cfg, ids, w, x, dev, steps, warmup, settle_ms, flushed=True)
+    counts = nv.ws_view(r["ws"], r["lay"], "counts", torch.int32, (cfg.num_local,)).cpu().numpy()
+    T, k, H, I, S = cfg.tokens, cfg.top_k, cfg.hidden, cfg.inter, r["S"]
+    l1, l2 = gemm_rooflines(cfg, r)
     return {"workload": f"skewed shard: T={T}, top-{k} of {cfg.num_global}, Zipf(1.2) popularity, local "
                         f"{cfg.expert_start}..{cfg.expert_start + cfg.num_local - 1}, H={H}, I={I}",
-            "tokens_per_s": round(T / (ms * 1e-3), 1), "ms_per_step": round(ms, 4), "slots": S,
+            "tokens_per_s": round(T / (r["ms"] * 1e-3), 1), "ms_per_step": round(r["ms"], 4), "slots": S,
             "empty_experts": int((counts == 0).sum()), "max_expert_share": round(float(counts.max()) / S, 4),
-            "layer_tflops": round(S * 2.0 * (2 * I * H + H * I) / (ms * 1e-3) / 1e12, 2)}
+            "layer_tflops": round(S * 2.0 * (2 * I * H + H * I) / (r["ms"] * 1e-3) / 1e12, 2),
+            "step_ms": r["step"], "step_ms_flushed": r["flushed"], "stages_ms": r["stages"],
+            "roofline_l1": l1, "roofline_l2": l2}
 
 
 def static_scales(nv, weights, W, dev, settle_ms, rounds=5):
@@ -381,7 +428,7 @@ def static_scales(nv, weights, W, dev, settle_ms, rounds=5):
         ids, w = W.make_router(cfg)
         x = W.make_activations(cfg)
         T, k = ids.shape
-        d_x = torch.from_numpy(x.view(np.int16)).view(torch.bfloat16).to(dev)
+        d_x = _bf16(x, dev)
         d_ids, d_w = torch.from_numpy(ids).to(dev), torch.from_numpy(w).to(dev)
         lay = nv.nvfp4_moe_ws_layout(T, k, cfg.hidden, cfg.inter, cfg.num_local)
         ws = torch.empty(lay["end"], dtype=torch.uint8, device=dev)
@@ -414,12 +461,13 @@ def static_scales(nv, weights, W, dev, settle_ms, rounds=5):
 
 def quantize_c1(nv, W, dev, settle_ms, reps=50):
     """Activation quantizer alone on the 4096 x 7168 Student-t(3) tensor with
-    +-2000 outliers: HBM bytes of one ideal pass (read x once, write codes,
-    scales and gs) over the measured time."""
+    +-2000 outliers: bytes of one ideal pass (read x once, write codes, scales
+    and gs) over the time of a call, each call timed with events after the
+    last-level cache was flushed (the headline), and back to back."""
     import torch
     qc = W.get_config("quant")
     xq = W.make_quant_input(qc)
-    d = torch.from_numpy(xq.view(np.int16)).view(torch.bfloat16).to(dev)
+    d = _bf16(xq, dev)
     M, K = xq.shape
     q = torch.empty((1, M, K // 2), dtype=torch.uint8, device=dev)
     sf = torch.empty((1, M, K // 16), dtype=torch.uint8, device=dev)
@@ -427,18 +475,60 @@ def quantize_c1(nv, W, dev, settle_ms, reps=50):
     ws = torch.empty(max(nv.nvfp4_quantize_ws_bytes(1, M, K), 256), dtype=torch.uint8, device=dev)
     fn = lambda: nv.nvfp4_quantize(d, q=q, sf=sf, gs=gs, ws=ws)
     settle(fn, settle_ms / 4)
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record()
-    for _ in range(reps):
-        fn()
-    e1.record()
-    torch.cuda.synchronize()
-    us = e0.elapsed_time(e1) * 1e3 / reps
+    flushed = stats(per_call_times(fn, reps, Flush(dev)))
+    warm = stats(per_call_times(fn, reps))
     ideal = M * K * 2 + M * K // 2 + M * K // 16 + 4
+    us = flushed["median"] * 1e3
+    gbs = lambda ms: round(ideal / (ms * 1e-3) / 1e9, 1)
     return {"workload": f"activation quantizer alone, [{M}, {K}] Student-t(3) with 0.1% at +-2000",
-            "us_per_call": round(us, 2), "ideal_bytes": ideal,
-            "GBs": round(ideal / (us * 1e-6) / 1e9, 1), "hbm_frac": round(ideal / (us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4),
-            "gs": float(gs.item())}
+            "us_per_call": round(us, 2), "ideal_bytes": ideal, "GBs": gbs(flushed["median"]),
+            "hbm_frac": round(ideal / (us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4),
+            "flushed_ms": flushed, "back_to_back_ms": warm, "back_to_back_GBs": gbs(warm["median"]),
+            "note": "us_per_call, GBs, hbm_frac: median over calls each preceded by a 512 MB read that evicts "
+                    "the last-level cache", "gs": float(gs.item())}
+
+
+def achievable_peaks(dev, read_bytes=3 << 29, reps=10):
+    """What this GPU sustains in practice: a streaming read of a 1.5 GiB
+    buffer (well past the 256 MB last-level cache) and a loop of independent
+    fp16 MFMAs without memory traffic, each timed with events (median of
+    reps launches)."""
+    import ctypes
+    import torch
+    lib = ctypes.CDLL(os.path.join(ROOT, "nvfp4_quantized_moe_amd", "libnvfp4probe.so"))
+    lib.nvfp4probe_read.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p]
+    lib.nvfp4probe_mfma.argtypes = [ctypes.c_int, ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p]
+    n_cu = torch.cuda.get_device_properties(dev).multi_processor_count
+    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    buf = torch.ones(read_bytes // 4, dtype=torch.float32, device=dev)
+    rgrid = n_cu * 8
+    rout = torch.empty(rgrid, dtype=torch.int32, device=dev)
+
+    def read():
+        if lib.nvfp4probe_read(ctypes.c_void_p(buf.data_ptr()), read_bytes, ctypes.c_void_p(rout.data_ptr()),
+                               rgrid, stream):
+            raise RuntimeError("nvfp4probe_read failed")
+    read()
+    rt = stats(per_call_times(read, reps))
+    del buf
+    iters, mgrid = 20000, n_cu * 2
+    mout = torch.empty(mgrid * 4, dtype=torch.float32, device=dev)
+
+    def mfma():
+        if lib.nvfp4probe_mfma(iters, ctypes.c_void_p(mout.data_ptr()), mgrid, stream):
+            raise RuntimeError("nvfp4probe_mfma failed")
+    mfma()
+    mt = stats(per_call_times(mfma, reps))
+    flop = mgrid * 4.0 * iters * 4 * 32768
+    gbs = read_bytes / (rt["median"] * 1e-3) / 1e9
+    tfs = flop / (mt["median"] * 1e-3) / 1e12
+    return {"hbm_read_GBs": round(gbs, 1), "hbm_read_frac_of_peak": round(gbs / PEAK_HBM_GBS, 4),
+            "hbm_read_bytes": read_bytes, "hbm_read_ms": rt,
+            "mfma_fp16_TFLOPs": round(tfs, 1), "mfma_frac_of_peak": round(tfs / PEAK_FP16_TFLOPS, 4),
+            "mfma_flop": flop, "mfma_ms": mt,
+            "note": f"read: {rgrid} workgroups of 256 threads, eight 16-byte loads in flight per thread; MFMA: "
+                    f"{mgrid} workgroups of 4 waves (2 per SIMD), 4 independent v_mfma_f32_32x32x16_f16 chains "
+                    f"per wave, no memory traffic in the loop"}
 
 
 def settle(fn, ms):
@@ -472,42 +562,101 @@ def _counter_rows(d, counter):
     return rows
 
 
-def summarize_traffic(workload, fetch_dir, write_dir):
-    """Per-launch HBM bytes of the L1 GEMM (the grouped GEMM instance with the
-    SiLU*up epilogue), each counter scaled by what it reads for the plain
-    1 GiB copy of --copy-calibration."""
-    out = {}
-    for tag, d, counter in (("fetch", fetch_dir, "FETCH_SIZE"), ("write", write_dir, "WRITE_SIZE")):
-        rows = _counter_rows(d, counter)
-        cal = [v for n, v in rows if "neg" in n.lower()]
-        l1 = [v for n, v in rows if "grouped_gemm_kernel" in n and n.replace(" ", "").split(">")[0].endswith(",1")]
-        if not cal or not l1:
-            raise SystemExit(f"{counter}: calibration dispatches {len(cal)}, L1 GEMM dispatches {len(l1)}")
-        factor = COPY_CAL_BYTES / (float(np.median(cal)) * 1024.0)
-        out[tag] = dict(kib=float(np.mean(l1)), factor=factor, n=len(l1),
-                        bytes=float(np.mean(l1)) * 1024.0 * factor)
-    path = os.path.join(PROFILE_DIR, f"l1_gemm_{workload}_traffic.txt")
-    with open(path, "w") as f:
-        f.write(f"# HBM traffic of the L1 grouped GEMM (gate+up, SiLU*up epilogue), {workload} shard\n")
-        f.write("# counters from two rocprofv3 runs on the MI355X box, from the repository root:\n")
-        for c, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
-            f.write(f"#   timeout -s KILL 180 rocprofv3 --pmc {c} -f csv -d {d} -o run -- python -u bench.py "
-                    f"--config {workload} --steps 2 --warmup 1 --no-decode --no-cpu-baseline --settle-ms 0 "
-                    f"--copy-calibration\n")
-        f.write(f"# summarized with: python bench.py --config {workload} --summarize-traffic {fetch_dir} {write_dir}\n")
-        f.write("# each counter (KiB per dispatch) is scaled by bytes / counter of a plain 1 GiB copy\n")
-        f.write(f"kernel_source_sha = {kernel_source_sha()}\n")
-        for tag in ("fetch", "write"):
-            o = out[tag]
-            f.write(f"{tag}_kib_per_launch = {o['kib']:.1f}\n{tag}_copy_factor = {o['factor']:.4f}\n"
-                    f"{tag}_dispatches = {o['n']}\n{tag}_bytes_per_launch = {o['bytes']:.0f}\n")
-        f.write(f"hbm_bytes_per_launch = {out['fetch']['bytes'] + out['write']['bytes']:.0f}\n")
-    print(open(path).read())
-
-
 def _short_kernel_name(n):
     n = n.split("(")[0].replace("void ", "").replace("nvfp4::", "")
     return n if len(n) < 90 else n[:87] + "..."
+
+
+def _gemm_epi(name):
+    """Epilogue template argument of a grouped GEMM kernel name (1, 2: L1 with
+    SiLU*up; 3: L1 writing NVFP4 h; 0: L2), else None."""
+    if "grouped_gemm_kernel<" not in name:
+        return None
+    args = name.replace(" ", "").split("grouped_gemm_kernel<", 1)[1].split(">")[0].split(",")
+    return int(args[-1]) if args and args[-1].isdigit() else None
+
+
+def _kernel_label(name):
+    epi = _gemm_epi(name)
+    if epi is not None:
+        return {0: "l2_gemm", 1: "l1_gemm", 2: "l1_gemm", 3: "l1_gemm_nvfp4"}.get(epi, "gemm")
+    return _short_kernel_name(name)
+
+
+def _per_kernel(rows):
+    """Mean counter value per dispatch, by kernel label: {label: (mean, dispatches)}."""
+    by = {}
+    for n, v in rows:
+        by.setdefault(_kernel_label(n), []).append(v)
+    return {k: (float(np.mean(v)), len(v)) for k, v in by.items()}
+
+
+def _profile_header(f, what, workload, cmds, summarize):
+    f.write(f"# {what}, {workload} shard\n")
+    f.write("# command(s), from the repository root on the MI355X box:\n")
+    for c in cmds:
+        f.write(f"#   {c}\n")
+    f.write(f"# summarized with: python bench.py --config {workload} {summarize}\n")
+    f.write(f"kernel_source_sha = {kernel_source_sha()}\n")
+
+
+def _bench_cmd(workload, extra=""):
+    return (f"python -u bench.py --config {workload} --steps 2 --warmup 1 --no-decode --no-cpu-baseline "
+            f"--settle-ms 0{extra}")
+
+
+def read_traffic(workload: str, gemm: str = "l1"):
+    """Per-launch HBM bytes of the L1 or L2 grouped GEMM from the committed
+    counter summary, or None when absent or taken on a different kernel
+    source."""
+    p = os.path.join(PROFILE_DIR, f"gemm_{workload}_traffic.txt")
+    if not os.path.exists(p):
+        return None
+    kv = {}
+    for line in open(p):
+        if "=" in line and not line.lstrip().startswith("#"):
+            k, v = line.split("=", 1)
+            kv[k.strip()] = v.split("#")[0].strip()
+    if kv.get("kernel_source_sha") != kernel_source_sha() or f"{gemm}_hbm_bytes_per_launch" not in kv:
+        return None
+    return float(kv[f"{gemm}_hbm_bytes_per_launch"])
+
+
+def summarize_traffic(workload, fetch_dir, write_dir):
+    """Per-launch HBM bytes of every kernel of the run, each counter (KiB per
+    dispatch) scaled by what it reads for the plain 1 GiB copy of
+    --copy-calibration; the grouped GEMMs' figures also as key = value lines."""
+    per, fac = {}, {}
+    for tag, d, counter in (("fetch", fetch_dir, "FETCH_SIZE"), ("write", write_dir, "WRITE_SIZE")):
+        rows = _counter_rows(d, counter)
+        cal = [v for n, v in rows if "neg" in n.lower()]
+        if not cal:
+            raise SystemExit(f"{counter}: no calibration copy dispatches (run with --copy-calibration)")
+        fac[tag] = COPY_CAL_BYTES / (float(np.median(cal)) * 1024.0)
+        per[tag] = _per_kernel([(n, v) for n, v in rows if "neg" not in n.lower()])
+    path = os.path.join(PROFILE_DIR, f"gemm_{workload}_traffic.txt")
+    with open(path, "w") as f:
+        _profile_header(f, "HBM traffic per kernel launch (FETCH_SIZE, WRITE_SIZE, copy-calibrated)", workload,
+                        [f"timeout -s KILL 180 rocprofv3 --pmc {c} -f csv -d {d} -o run -- "
+                         + _bench_cmd(workload, " --copy-calibration")
+                         for c, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir))],
+                        f"--summarize-traffic {fetch_dir} {write_dir}")
+        f.write(f"# each counter (KiB per dispatch) is scaled by bytes / counter of a plain 1 GiB copy: "
+                f"fetch x{fac['fetch']:.4f}, write x{fac['write']:.4f}\n")
+        f.write("# kernel | dispatches | fetch MB/launch | write MB/launch\n")
+        for k in sorted(per["fetch"]):
+            fm, n = per["fetch"][k]
+            wm = per["write"].get(k, (0.0, 0))[0]
+            f.write(f"#   {k} | {n} | {fm * 1024 * fac['fetch'] / 1e6:.2f} | {wm * 1024 * fac['write'] / 1e6:.2f}\n")
+        f.write(f"fetch_copy_factor = {fac['fetch']:.4f}\nwrite_copy_factor = {fac['write']:.4f}\n")
+        for g in ("l1_gemm", "l2_gemm"):
+            if g in per["fetch"]:
+                fb = per["fetch"][g][0] * 1024 * fac["fetch"]
+                wb = per["write"].get(g, (0.0, 0))[0] * 1024 * fac["write"]
+                key = g.split("_")[0]
+                f.write(f"{key}_fetch_bytes_per_launch = {fb:.0f}\n{key}_write_bytes_per_launch = {wb:.0f}\n"
+                        f"{key}_hbm_bytes_per_launch = {fb + wb:.0f}\n")
+    print(open(path).read())
 
 
 def summarize_trace(workload, d, all_workloads=False):
@@ -577,32 +726,99 @@ def summarize_trace(workload, d, all_workloads=False):
     print(open(path).read())
 
 
+MFMA_COUNTERS = ["SQ_INSTS_MFMA", "SQ_VALU_MFMA_BUSY_CYCLES", "SQ_VALU_MFMA_COEXEC_CYCLES", "SQ_BUSY_CYCLES",
+                 "SQ_ACTIVE_INST_VALU", "SQ_ACTIVE_INST_LDS", "SQ_WAVES", "GRBM_GUI_ACTIVE"]
+VALU_COUNTERS = ["SQ_INSTS_VALU", "SQ_INSTS_SALU", "SQ_INSTS_MFMA", "SQ_INSTS_LDS", "SQ_INSTS_VMEM",
+                 "SQ_WAVE_CYCLES", "SQ_WAIT_INST_ANY", "SQ_WAVES"]
+STALL_COUNTERS = ["SQ_WAIT_ANY", "SQ_WAIT_INST_LDS", "SQ_LDS_BANK_CONFLICT", "SQ_LDS_IDX_ACTIVE", "SQ_ACTIVE_INST_ANY",
+                  "SQ_ACTIVE_INST_MISC", "SQ_ACTIVE_INST_VMEM", "SQ_WAVE_CYCLES"]
+
+
+def _counter_table(dirs, counters):
+    """{kernel label: {counter: mean per dispatch, 'n': dispatches}} over one
+    or more rocprofv3 csv runs (each counter from the runs that hold it)."""
+    tab = {}
+    for d in dirs:
+        for c in counters:
+            try:
+                rows = _counter_rows(d, c)
+            except SystemExit:
+                continue
+            for k, (m, n) in _per_kernel(rows).items():
+                tab.setdefault(k, {"n": n})[c] = m
+    return tab
+
+
 def summarize_mfma(workload, d):
-    """MFMA work of the L1 GEMM from one rocprofv3 --pmc run: executed MFMA
-    instructions (32x32x16 fp16: 32768 FLOP each) against the algorithmic
-    FLOP, and the MFMA-busy share of the SIMD cycles."""
-    ins = _counter_rows(d, "SQ_INSTS_MFMA")
-    busy = _counter_rows(d, "SQ_VALU_MFMA_BUSY_CYCLES")
-    gui = _counter_rows(d, "GRBM_GUI_ACTIVE")
-    sqb = _counter_rows(d, "SQ_BUSY_CYCLES")
-    sel = lambda rows: [v for n, v in rows if "grouped_gemm_kernel" in n and
-                        n.replace(" ", "").split(">")[0].endswith(",1")]
-    i, b, g, q = (float(np.mean(sel(r))) for r in (ins, busy, gui, sqb))
-    path = os.path.join(PROFILE_DIR, f"l1_gemm_{workload}_mfma.txt")
+    """MFMA work of the grouped GEMMs from one rocprofv3 --pmc run: executed
+    MFMA instructions (32x32x16 fp16: 32768 FLOP each) and the MFMA-busy
+    cycles against the kernel's active cycles on all SIMDs."""
+    tab = _counter_table([d], MFMA_COUNTERS)
+    path = os.path.join(PROFILE_DIR, f"gemm_{workload}_mfma.txt")
     with open(path, "w") as o:
-        o.write(f"# MFMA counters of the L1 grouped GEMM (gate+up, SiLU*up epilogue), {workload} shard\n")
-        o.write("# command, from the repository root on the MI355X box:\n")
-        o.write(f"#   timeout -s KILL 180 rocprofv3 --pmc SQ_INSTS_MFMA SQ_VALU_MFMA_BUSY_CYCLES SQ_BUSY_CYCLES "
-                f"SQ_WAVES GRBM_GUI_ACTIVE -f csv -d {d} -o run -- python -u bench.py --config {workload} "
-                f"--steps 2 --warmup 1 --no-decode --no-cpu-baseline --settle-ms 0\n")
-        o.write(f"# summarized with: python bench.py --config {workload} --summarize-mfma {d}\n")
-        o.write(f"kernel_source_sha = {kernel_source_sha()}\n")
-        o.write(f"dispatches = {len(sel(ins))}\n")
-        o.write(f"mfma_instructions_per_launch = {i:.0f}\n")
-        o.write(f"executed_mfma_flop_per_launch = {i * 32768:.0f}\n")
-        o.write(f"mfma_busy_cycles_per_launch = {b:.0f}   # summed over SIMDs; 32 per 32x32x16 fp16 MFMA\n")
-        o.write(f"grbm_gui_active_per_launch = {g:.0f}\n")
-        o.write(f"sq_busy_cycles_per_launch = {q:.0f}\n")
+        _profile_header(o, "MFMA counters of the grouped GEMMs", workload,
+                        [f"timeout -s KILL 180 rocprofv3 --pmc {' '.join(MFMA_COUNTERS)} -f csv -d {d} -o run -- "
+                         + _bench_cmd(workload)], f"--summarize-mfma {d}")
+        o.write("# mfma_busy_share = SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE x 1024 SIMDs): the share of the\n"
+                "# kernel's active cycles in which a SIMD's matrix core works (both counters per launch; a\n"
+                "# 32x32x16 fp16 MFMA keeps the matrix core busy for 32 of these cycles)\n")
+        for g in ("l1_gemm", "l2_gemm", "l1_gemm_nvfp4"):
+            if g not in tab:
+                continue
+            t = tab[g]
+            key = g.replace("_gemm", "")
+            o.write(f"{key}_dispatches = {t['n']}\n")
+            o.write(f"{key}_mfma_instructions_per_launch = {t['SQ_INSTS_MFMA']:.0f}\n")
+            o.write(f"{key}_executed_mfma_flop_per_launch = {t['SQ_INSTS_MFMA'] * 32768:.0f}\n")
+            o.write(f"{key}_mfma_busy_cycles_per_launch = {t['SQ_VALU_MFMA_BUSY_CYCLES']:.0f}\n")
+            o.write(f"{key}_grbm_gui_active_per_launch = {t['GRBM_GUI_ACTIVE']:.0f}\n")
+            o.write(f"{key}_mfma_busy_share = "
+                    f"{t['SQ_VALU_MFMA_BUSY_CYCLES'] / (t['GRBM_GUI_ACTIVE'] * 1024):.4f}\n")
+            o.write(f"{key}_valu_mfma_coexec_cycles_per_launch = {t['SQ_VALU_MFMA_COEXEC_CYCLES']:.0f}\n")
+            o.write(f"{key}_active_inst_valu_per_launch = {t['SQ_ACTIVE_INST_VALU']:.0f}\n")
+            o.write(f"{key}_active_inst_lds_per_launch = {t['SQ_ACTIVE_INST_LDS']:.0f}\n")
+    print(open(path).read())
+
+
+def summarize_valu(workload, dirs):
+    """Instruction mix and stalls of every kernel from two rocprofv3 --pmc runs
+    (comma-separated directories: the VALU_COUNTERS run, then the
+    STALL_COUNTERS run; per wave instruction counts summed over the launch):
+    VALU (including MFMA), SALU, MFMA, LDS and vector-memory instructions, the
+    share of wave cycles spent waiting for an instruction to be issued; for the
+    grouped GEMMs also the non-MFMA VALU and the SALU instructions per MFMA,
+    LDS bank conflicts and waits."""
+    dl = dirs.split(",")
+    tab = _counter_table(dl, VALU_COUNTERS + STALL_COUNTERS)
+    path = os.path.join(PROFILE_DIR, f"gemm_{workload}_valu.txt")
+    with open(path, "w") as o:
+        _profile_header(o, "Instruction mix and stalls per kernel launch", workload,
+                        [f"timeout -s KILL 180 rocprofv3 --pmc {' '.join(cs)} -f csv -d {d} -o run -- "
+                         + _bench_cmd(workload) for cs, d in zip((VALU_COUNTERS, STALL_COUNTERS), dl)],
+                        f"--summarize-valu {dirs}")
+        o.write("# kernel | dispatches | VALU | SALU | MFMA | LDS | VMEM | wait-inst share of wave cycles\n")
+        for k in sorted(tab):
+            t = tab[k]
+            wait = t.get("SQ_WAIT_INST_ANY", 0.0) / max(t.get("SQ_WAVE_CYCLES", 1.0), 1.0)
+            o.write(f"#   {k} | {t['n']} | {t.get('SQ_INSTS_VALU', 0):.0f} | {t.get('SQ_INSTS_SALU', 0):.0f} | "
+                    f"{t.get('SQ_INSTS_MFMA', 0):.0f} | {t.get('SQ_INSTS_LDS', 0):.0f} | "
+                    f"{t.get('SQ_INSTS_VMEM', 0):.0f} | {wait:.3f}\n")
+        for g in ("l1_gemm", "l2_gemm", "l1_gemm_nvfp4"):
+            if g not in tab or not tab[g].get("SQ_INSTS_MFMA"):
+                continue
+            t = tab[g]
+            m = t["SQ_INSTS_MFMA"]
+            key = g.replace("_gemm", "")
+            o.write(f"{key}_valu_non_mfma_per_mfma = {(t['SQ_INSTS_VALU'] - m) / m:.3f}\n")
+            o.write(f"{key}_salu_per_mfma = {t['SQ_INSTS_SALU'] / m:.3f}\n")
+            o.write(f"{key}_lds_per_mfma = {t['SQ_INSTS_LDS'] / m:.3f}\n")
+            o.write(f"{key}_wait_inst_share = {t['SQ_WAIT_INST_ANY'] / t['SQ_WAVE_CYCLES']:.4f}\n")
+            if "SQ_WAIT_ANY" in t:
+                o.write(f"{key}_wait_any_share = {t['SQ_WAIT_ANY'] / t['SQ_WAVE_CYCLES']:.4f}\n")
+                o.write(f"{key}_wait_inst_lds_share = {t['SQ_WAIT_INST_LDS'] / t['SQ_WAVE_CYCLES']:.4f}\n")
+                o.write(f"{key}_lds_bank_conflict_per_launch = {t['SQ_LDS_BANK_CONFLICT']:.0f}\n")
+                o.write(f"{key}_lds_idx_active_per_launch = {t['SQ_LDS_IDX_ACTIVE']:.0f}\n")
+                o.write(f"{key}_active_inst_vmem_per_launch = {t['SQ_ACTIVE_INST_VMEM']:.0f}\n")
     print(open(path).read())
 
 

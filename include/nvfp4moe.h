@@ -284,6 +284,32 @@ int nvfp4_moe_forward(const nvfp4_moe_weights* w, const void* x_bf16, int32_t T,
                       const int32_t* topk_ids, const float* topk_w, int32_t k, int32_t expert_start,
                       void* out_bf16, void* ws, size_t ws_bytes, void* stream);
 
+/* nvfp4_moe_forward with per-stage timing: the same launches, with HIP events
+ * recorded on `stream` between them, so that the caller can time each step of
+ * the real layer. events: host array of NVFP4_NSTAGES + 1 hipEvent_t the caller
+ * created (timing enabled); events[0] is recorded before the first launch and
+ * events[i + 1] after the launches of stage i:
+ *   NVFP4_STAGE_AMAX_ROUTE  a1, amax of x, sharing its launch with a3: the whole
+ *                           route when T*k <= 1024, else the per-chunk histograms
+ *   NVFP4_STAGE_QUANT_X     a2, block quantization of x
+ *   NVFP4_STAGE_ROUTE       the rest of a3 (scan, slot scatter, tile table) when
+ *                           T*k > 1024; no launch (events back to back) otherwise
+ *   NVFP4_STAGE_L1          a4 + a5, L1 grouped GEMM with the SiLU*up epilogue
+ *   NVFP4_STAGE_QUANT_H     a6, re-quantization of h
+ *   NVFP4_STAGE_L2          a7, L2 grouped GEMM
+ *   NVFP4_STAGE_SCATTER     a8, weighted scatter
+ * A NULL entry skips that record; a NULL events array returns NVFP4_ERR_NULL,
+ * a failed event record NVFP4_ERR_HIP. Arguments and results as
+ * nvfp4_moe_forward.
+ */
+enum {
+  NVFP4_STAGE_AMAX_ROUTE = 0, NVFP4_STAGE_QUANT_X, NVFP4_STAGE_ROUTE, NVFP4_STAGE_L1, NVFP4_STAGE_QUANT_H,
+  NVFP4_STAGE_L2, NVFP4_STAGE_SCATTER, NVFP4_NSTAGES
+};
+int nvfp4_moe_forward_stage_events(const nvfp4_moe_weights* w, const void* x_bf16, int32_t T,
+                                   const int32_t* topk_ids, const float* topk_w, int32_t k, int32_t expert_start,
+                                   void* out_bf16, void* ws, size_t ws_bytes, void* const* events, void* stream);
+
 /* The layer with fixed global scales (nvfp4_cutedsl.py history, page 2,
  * static-scale commit: warmup measures gs for the L1 input and for the L1
  * output; inference quantizes with them, no max reduction, no host sync).

@@ -19,7 +19,7 @@ __all__ = [
     "nvfp4_quantize_ws_bytes", "nvfp4_quantize_noalloc", "moe_route_slots", "moe_route_ws_bytes", "nvfp4_tile_table_len",
     "nvfp4_grouped_gemm", "moe_weighted_scatter", "nvfp4_fold_scales", "nvfp4_packed_bytes",
     "nvfp4_pack_weights", "nvfp4_moe_forward", "nvfp4_quantize_static", "nvfp4_grouped_gemm_silu_nvfp4",
-    "nvfp4_moe_forward_static", "calibrate_static_gs",
+    "nvfp4_moe_forward_static", "calibrate_static_gs", "nvfp4_moe_forward_stage_events", "STAGES",
     "nvfp4_moe_ws_bytes", "nvfp4_moe_ws_layout", "nvfp4_moe_tile_m", "MoEWeights", "prepare_weights",
     "ws_view",
 ]
@@ -72,6 +72,8 @@ _moe_ws = _sig("nvfp4_moe_ws_bytes", _sz, _i32, _i32, _i32, _i32, _i32)
 _moe_tile_m = _sig("nvfp4_moe_tile_m", _i32, _i32, _i32, _i32)
 _forward = _sig("nvfp4_moe_forward", ctypes.c_int, ctypes.POINTER(_Weights), _vp, _i32, _vp, _vp,
                 _i32, _i32, _vp, _vp, _sz, _vp)
+_forward_stages = _sig("nvfp4_moe_forward_stage_events", ctypes.c_int, ctypes.POINTER(_Weights), _vp, _i32, _vp,
+                       _vp, _i32, _i32, _vp, _vp, _sz, ctypes.POINTER(_vp), _vp)
 _forward_static = _sig("nvfp4_moe_forward_static", ctypes.c_int, ctypes.POINTER(_Weights), _vp, _i32, _vp, _vp,
                        _i32, _i32, _vp, _vp, _vp, _sz, _vp)
 
@@ -423,8 +425,7 @@ def _check_layer_inputs(weights, x, topk_w, T, k):
         _dev(getattr(weights, name), getattr(weights, name).dtype, f"weights.{name}")
 
 
-def nvfp4_moe_forward(weights: MoEWeights, x, topk_ids, topk_w, expert_start, out=None, ws=None):
-    """One rank's partial output BF16 [T, H] of the expert FFN."""
+def _layer_buffers(weights, x, topk_ids, topk_w, out, ws):
     _dev(x, torch.bfloat16, "x")
     _dev(topk_ids, torch.int32, "topk_ids")
     _dev(topk_w, torch.float32, "topk_w")
@@ -435,27 +436,49 @@ def nvfp4_moe_forward(weights: MoEWeights, x, topk_ids, topk_w, expert_start, ou
     out = torch.empty((T, H), dtype=torch.bfloat16, device=dev) if out is None else _buf(out, torch.bfloat16, T * H, "out")
     need = nvfp4_moe_ws_bytes(T, k, H, weights.inter, weights.num_local)
     ws = _alloc_ws(need, dev) if ws is None else _buf(ws, torch.uint8, 0, "ws")
+    return T, k, out, ws
+
+
+def nvfp4_moe_forward(weights: MoEWeights, x, topk_ids, topk_w, expert_start, out=None, ws=None):
+    """One rank's partial output BF16 [T, H] of the expert FFN."""
+    T, k, out, ws = _layer_buffers(weights, x, topk_ids, topk_w, out, ws)
     _check(_forward(ctypes.byref(weights._c), _ptr(x), T, _ptr(topk_ids), _ptr(topk_w), k, expert_start,
                     _ptr(out), _ptr(ws), ws.numel(), _stream()), "nvfp4_moe_forward")
+    return out
+
+
+# stages between the events of nvfp4_moe_forward_stage_events (NVFP4_STAGE_* order)
+STAGES = ["a1_amax_route", "a2_quantize_x", "a3_route", "a4_a5_l1_gemm", "a6_quantize_h", "a7_l2_gemm",
+          "a8_scatter"]
+
+
+def nvfp4_moe_forward_stage_events(weights: MoEWeights, x, topk_ids, topk_w, expert_start, events, out=None,
+                                   ws=None):
+    """nvfp4_moe_forward with events recorded between its launches: events is
+    a list of len(STAGES) + 1 torch.cuda.Event (timing enabled, each recorded
+    once beforehand so that it exists) or None (no record there); events[i]
+    to events[i + 1] spans stage STAGES[i] of this call."""
+    if len(events) != len(STAGES) + 1:
+        raise ValueError(f"events: expected {len(STAGES) + 1} entries, got {len(events)}")
+    handles = (_vp * len(events))()
+    for i, e in enumerate(events):
+        if e is not None:
+            if not e.cuda_event:
+                raise ValueError(f"events[{i}]: not created yet (record it once first)")
+            handles[i] = e.cuda_event
+    T, k, out, ws = _layer_buffers(weights, x, topk_ids, topk_w, out, ws)
+    _check(_forward_stages(ctypes.byref(weights._c), _ptr(x), T, _ptr(topk_ids), _ptr(topk_w), k, expert_start,
+                           _ptr(out), _ptr(ws), ws.numel(), handles, _stream()), "nvfp4_moe_forward_stage_events")
     return out
 
 
 def nvfp4_moe_forward_static(weights: MoEWeights, x, topk_ids, topk_w, expert_start, gs, out=None, ws=None):
     """The layer with fixed global scales gs = float32 [2] (gs_x, gs_h) on the
     device, e.g. from calibrate_static_gs; no amax passes, h quantized in L1."""
-    _dev(x, torch.bfloat16, "x")
-    _dev(topk_ids, torch.int32, "topk_ids")
-    _dev(topk_w, torch.float32, "topk_w")
     _dev(gs, torch.float32, "gs")
     if gs.numel() != 2:
         raise ValueError(f"gs: expected 2 values (gs_x, gs_h), got {gs.numel()}")
-    T, k = topk_ids.shape
-    H = weights.hidden
-    _check_layer_inputs(weights, x, topk_w, T, k)
-    dev = x.device
-    out = torch.empty((T, H), dtype=torch.bfloat16, device=dev) if out is None else _buf(out, torch.bfloat16, T * H, "out")
-    need = nvfp4_moe_ws_bytes(T, k, H, weights.inter, weights.num_local)
-    ws = _alloc_ws(need, dev) if ws is None else _buf(ws, torch.uint8, 0, "ws")
+    T, k, out, ws = _layer_buffers(weights, x, topk_ids, topk_w, out, ws)
     _check(_forward_static(ctypes.byref(weights._c), _ptr(x), T, _ptr(topk_ids), _ptr(topk_w), k, expert_start,
                            _ptr(gs), _ptr(out), _ptr(ws), ws.numel(), _stream()), "nvfp4_moe_forward_static")
     return out

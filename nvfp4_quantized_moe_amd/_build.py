@@ -18,14 +18,20 @@ FLAGS = [
 ]
 
 
+PROBE_LIB = os.path.join(PKG, "libnvfp4probe.so")
+
+
 def sources():
     return sorted(glob.glob(os.path.join(PKG, "csrc", "*.hip")))
 
 
-def build(verbose: bool = False) -> str:
-    """Compile every HIP source into one shared library next to this file."""
-    tmp = LIB + ".tmp"
-    cmd = [HIPCC, *FLAGS, "-I", os.path.join(ROOT, "include"), *sources(), "-o", tmp]
+def probe_sources():
+    return sorted(glob.glob(os.path.join(PKG, "csrc", "probe", "*.hip")))
+
+
+def _compile(srcs, out, verbose):
+    tmp = out + ".tmp"
+    cmd = [HIPCC, *FLAGS, "-I", os.path.join(ROOT, "include"), *srcs, "-o", tmp]
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         raise RuntimeError("hipcc failed:\n" + res.stdout + res.stderr)
@@ -33,7 +39,14 @@ def build(verbose: bool = False) -> str:
         msg = "\n".join(l for l in res.stderr.splitlines() if "packed-fp32-ops" not in l)
         if msg.strip():
             print(msg)
-    os.replace(tmp, LIB)
+    os.replace(tmp, out)
+
+
+def build(verbose: bool = False) -> str:
+    """Compile every HIP source of the layer into one shared library next to
+    this file, and the benchmark's roofline probes into a second one."""
+    _compile(sources(), LIB, verbose)
+    _compile(probe_sources(), PROBE_LIB, verbose)
     return LIB
 
 

@@ -95,13 +95,19 @@ static int check_forward_args(const nvfp4_moe_weights* w, const void* x_bf16, in
   return NVFP4_OK;
 }
 
-extern "C" int nvfp4_moe_forward(const nvfp4_moe_weights* w, const void* x_bf16, int32_t T, const int32_t* topk_ids,
-                                 const float* topk_w, int32_t k, int32_t expert_start, void* out_bf16, void* ws,
-                                 size_t ws_bytes, void* stream_) {
+// The dynamic layer; with ev != NULL, event ev[i + 1] (when not NULL) is
+// recorded on the stream after the launches of stage i (NVFP4_STAGE_*), and
+// ev[0] before the first launch.
+static int moe_forward(const nvfp4_moe_weights* w, const void* x_bf16, int32_t T, const int32_t* topk_ids,
+                       const float* topk_w, int32_t k, int32_t expert_start, void* out_bf16, void* ws,
+                       size_t ws_bytes, hipStream_t stream, hipEvent_t* ev) {
   int st = check_forward_args(w, x_bf16, T, topk_ids, topk_w, k, out_bf16, ws, ws_bytes);
   if (st) return st;
+  auto mark = [&](int i) -> int {
+    if (ev && ev[i] && hipEventRecord(ev[i], stream) != hipSuccess) return NVFP4_ERR_HIP;
+    return NVFP4_OK;
+  };
   const int32_t L = w->num_local, H = w->hidden, I = w->inter;
-  hipStream_t stream = (hipStream_t)stream_;
   const int32_t tile_m = nvfp4_moe_tile_m(T, k, L);
   size_t o[NVFP4_WS_NREGIONS];
   nvfp4_moe_ws_layout(T, k, H, I, L, tile_m, o);
@@ -125,6 +131,7 @@ extern "C" int nvfp4_moe_forward(const nvfp4_moe_weights* w, const void* x_bf16,
   void* qws = R(NVFP4_WS_QUANT_SCRATCH);
   const int32_t cap = T * k;
 
+  if ((st = mark(0))) return st;
   if (cap <= 1024) {
     // decode-sized batches: a1 (amax partials of x, which also zero the scalars
     // gs_x, amax_h, gs_h, reserved) and a3 (route) share one launch; then a2
@@ -134,8 +141,10 @@ extern "C" int nvfp4_moe_forward(const nvfp4_moe_weights* w, const void* x_bf16,
                                       expert_start, L, tile_m, counts, offsets, slot_token, slot_expert,
                                       slot_weight, token_slot, tiles, stream)))
       return st;
+    if ((st = mark(1 + NVFP4_STAGE_AMAX_ROUTE))) return st;
     if ((st = nvfp4_launch_quantize_from_partials(x_bf16, T, H, qws, gx, x_q, x_sf, &scalars[0], stream)))
       return st;
+    if ((st = mark(1 + NVFP4_STAGE_QUANT_X)) || (st = mark(1 + NVFP4_STAGE_ROUTE))) return st;
   } else {
     // a1 (amax partials of x, which also zero the scalars gs_x, amax_h, gs_h,
     // reserved) and a3's per-chunk histograms share one launch; then a2, then
@@ -144,13 +153,16 @@ extern "C" int nvfp4_moe_forward(const nvfp4_moe_weights* w, const void* x_bf16,
                                       reinterpret_cast<uint32_t*>(scalars), 4, topk_ids, T, k, expert_start, L,
                                       route_ws, stream)))
       return st;
+    if ((st = mark(1 + NVFP4_STAGE_AMAX_ROUTE))) return st;
     if ((st = nvfp4_launch_quantize_from_partials(x_bf16, T, H, qws, nvfp4_amax_grid((int64_t)T * H), x_q, x_sf,
                                                   &scalars[0], stream)))
       return st;
+    if ((st = mark(1 + NVFP4_STAGE_QUANT_X))) return st;
     if ((st = nvfp4_launch_route_from_counts(topk_ids, topk_w, T, k, expert_start, L, tile_m, counts, offsets,
                                              slot_token, slot_expert, slot_weight, token_slot, tiles, route_ws,
                                              stream)))
       return st;
+    if ((st = mark(1 + NVFP4_STAGE_ROUTE))) return st;
   }
   if (cap > 0) {
     // a4/a5: L1 with the fused SiLU*up epilogue and amax of h
@@ -160,18 +172,40 @@ extern "C" int nvfp4_moe_forward(const nvfp4_moe_weights* w, const void* x_bf16,
                                         &scalars[1], stream)))
       return st;
   }
+  if ((st = mark(1 + NVFP4_STAGE_L1))) return st;
   // a6: re-quantize the S valid rows of h with gs_h = amax_h / 2688
   if ((st = nvfp4_launch_quantize(h, 1, cap, I, &scalars[1], &offsets[L], h_q, h_sf, &scalars[2], qws, nullptr,
                                   0, stream)))
     return st;
+  if ((st = mark(1 + NVFP4_STAGE_QUANT_H))) return st;
   if (cap > 0) {
     // a7: L2 in slot order
     if ((st = nvfp4_launch_grouped_gemm(h_q, h_sf, nullptr, &scalars[2], w->w2, w->w2_gs, offsets,
                                         tiles, L, cap, H, I, tile_m, NVFP4_EPI_BF16, y, nullptr, stream)))
       return st;
   }
+  if ((st = mark(1 + NVFP4_STAGE_L2))) return st;
   // a8: weighted scatter back to token rows
-  return nvfp4_launch_scatter(y, token_slot, topk_w, T, k, H, out_bf16, stream);
+  if ((st = nvfp4_launch_scatter(y, token_slot, topk_w, T, k, H, out_bf16, stream))) return st;
+  return mark(1 + NVFP4_STAGE_SCATTER);
+}
+
+extern "C" int nvfp4_moe_forward(const nvfp4_moe_weights* w, const void* x_bf16, int32_t T, const int32_t* topk_ids,
+                                 const float* topk_w, int32_t k, int32_t expert_start, void* out_bf16, void* ws,
+                                 size_t ws_bytes, void* stream) {
+  return moe_forward(w, x_bf16, T, topk_ids, topk_w, k, expert_start, out_bf16, ws, ws_bytes, (hipStream_t)stream,
+                     nullptr);
+}
+
+extern "C" int nvfp4_moe_forward_stage_events(const nvfp4_moe_weights* w, const void* x_bf16, int32_t T,
+                                              const int32_t* topk_ids, const float* topk_w, int32_t k,
+                                              int32_t expert_start, void* out_bf16, void* ws, size_t ws_bytes,
+                                              void* const* events, void* stream) {
+  if (!events) return NVFP4_ERR_NULL;
+  hipEvent_t ev[NVFP4_NSTAGES + 1];
+  for (int i = 0; i <= NVFP4_NSTAGES; ++i) ev[i] = reinterpret_cast<hipEvent_t>(events[i]);
+  return moe_forward(w, x_bf16, T, topk_ids, topk_w, k, expert_start, out_bf16, ws, ws_bytes, (hipStream_t)stream,
+                     ev);
 }
 
 // The layer with fixed global scales gs_in = (gs_x, gs_h), measured once
