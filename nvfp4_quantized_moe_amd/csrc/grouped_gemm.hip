@@ -58,7 +58,8 @@ struct GemmCfg {
   static constexpr int THREADS = 64 * WAVES;
   static constexpr int A_TASKS = BM * 4;           // (row, 32-element chunk) per stage
   static constexpr int A_PER_T = (A_TASKS + THREADS - 1) / THREADS;
-  static constexpr int LDS = 2 * BM * kAPitch;
+  static constexpr int LDS = 2 * BM * kAPitch;   // two A buffers (a spare 1 KB follows them)
+  static constexpr int LDS_SPARE = 1024;
 };
 
 // Buffer resources (gfx9 descriptor): loads at offsets >= num_records return
@@ -165,7 +166,7 @@ __global__ __launch_bounds__(64 * WAVES) void grouped_gemm_kernel(
   struct Src {
     __amdgpu_buffer_rsrc_t rbw;
     uint32_t a_off[C::A_PER_T], as_off[C::A_PER_T];
-    int row0[SUB_N];
+    uint32_t b_off[SUB_N];  // byte offset of weight subtile j's stage-0 chunk, or out of range
   };
   // row-tile order: the row tiles of one column tile are adjacent, so the
   // row tiles of one expert share its weight tile in L2 at the same time;
@@ -182,7 +183,7 @@ __global__ __launch_bounds__(64 * WAVES) void grouped_gemm_kernel(
       src.as_off[i] = kOutOfRange;
     }
 #pragma unroll
-    for (int j = 0; j < SUB_N; ++j) src.row0[j] = -1;
+    for (int j = 0; j < SUB_N; ++j) src.b_off[j] = kOutOfRange;
     if (item >= items) return;
     int mt, nt;
     tile_of(item, mt, nt);
@@ -221,7 +222,9 @@ __global__ __launch_bounds__(64 * WAVES) void grouped_gemm_kernel(
         const int col0 = nt * C::BN + ch * 32;
         row0 = col0 < N ? col0 : -1;
       }
-      src.row0[j] = row0;
+      // the stage-0 chunk offset is kept, so that a stage's loads need one add
+      // and no multiply (which the compiler would branch around in the loop)
+      src.b_off[j] = row0 >= 0 ? (uint32_t)(row0 >> 5) * (uint32_t)nstages * kPackChunk : kOutOfRange;
     }
   };
   const uint32_t b_lane = 16u * (uint32_t)lane;
@@ -256,7 +259,9 @@ __global__ __launch_bounds__(64 * WAVES) void grouped_gemm_kernel(
   // Loads of loop stage t into ring slot slot_: stage t of the current item
   // for t < nstages, stage t - S of the next item for t >= S, zeros between
   // (padding stages). The choice is wave-uniform and made with selects.
-  auto load_stage = [&](const Src& cur, const Src& nxt, int t, int slot_) {
+  // Activations are loaded one stage earlier than weights (their LDS copy is
+  // written during the stage before the one that reads it).
+  auto load_a = [&](const Src& cur, const Src& nxt, int t, int slot_) {
     const bool in_cur = t < nstages, in_nxt = t >= S;
     const int st = in_cur ? t : t - S;
     const bool in = in_cur || (in_nxt && st < nstages);
@@ -266,29 +271,44 @@ __global__ __launch_bounds__(64 * WAVES) void grouped_gemm_kernel(
       ra[slot_][i] = buf_load16(ra_q, in_cur ? cur.a_off[i] : nxt.a_off[i], so);
       rsa[slot_][i] = buf_load2(ra_s, in_cur ? cur.as_off[i] : nxt.as_off[i], sso);
     }
+  };
+  auto load_b = [&](const Src& cur, const Src& nxt, int t, int slot_) {
+    const bool in_cur = t < nstages, in_nxt = t >= S;
+    const int st = in_cur ? t : t - S;
+    const bool in = in_cur || (in_nxt && st < nstages);
     const __amdgpu_buffer_rsrc_t rbw = in_cur ? cur.rbw : nxt.rbw;
 #pragma unroll
     for (int j = 0; j < SUB_N; ++j) {
       // wave-uniform: a scalar offset. A subtile past N has an out-of-range base
       // (>= 2^31), which stays out of range after adding st * kPackChunk (< 2^31).
-      const int row0 = in_cur ? cur.row0[j] : nxt.row0[j];
-      const uint32_t chunk = in && row0 >= 0 ? ((uint32_t)(row0 >> 5) * (uint32_t)nstages + (uint32_t)st) * kPackChunk
-                                             : kOutOfRange;
+      const uint32_t base = in_cur ? cur.b_off[j] : nxt.b_off[j];
+      const uint32_t chunk = in ? base + (uint32_t)st * kPackChunk : kOutOfRange;
       rb[slot_][j][0] = buf_load16(rbw, b_lane, chunk);
       rb[slot_][j][1] = buf_load16(rbw, b_lane + 1024u, chunk);
       rsb[slot_][j] = buf_load4(rbw, bs_lane, chunk);
     }
   };
   float16_t acc[SUB_M][SUB_N];
-  // MFMAs of one stage from ring slot u and LDS buffer buf
-  auto mma_stage = [&](int buf, int u) {
+  // MFMAs of one stage from ring slot u and LDS buffer buf; meanwhile the
+  // activations of the next stage (ring slot su) are decoded into LDS buffer
+  // sbuf, one 8-value piece per MFMA step, so that the stage ends with no
+  // decode work left before its barrier
+  // Prefill-height tiles (64 rows and more) load activations a stage earlier
+  // and decode them into LDS during the previous stage's MFMAs; decode-height
+  // tiles (32 rows, weight-streaming) keep the decode after the MFMAs, which
+  // holds fewer registers (more resident workgroups per CU).
+  constexpr bool kEarlyA = C::BM >= 64;
+  auto mma_stage = [&](int buf, int u, int sbuf, int su) {
     const uint8_t* abuf = lds + buf * (C::BM * kAPitch) + lr * kAPitch + 128 * lg;
+    uint8_t* sdst = lds + sbuf * (C::BM * kAPitch);
     // software pipeline over the 8 MFMA steps of the stage: the operands of
     // step t + 1 are read and decoded while the MFMAs of step t execute
     half8_t av[2][SUB_M], bv[2][SUB_N];
-    Scales4 sb[SUB_N];
+    Scales4 sb[SUB_N], sa[C::A_PER_T];
 #pragma unroll
     for (int j = 0; j < SUB_N; ++j) sb[j] = scales4(rsb[u][j]);
+#pragma unroll
+    for (int i = 0; i < C::A_PER_T; ++i) sa[i] = scales4(rsa[su][i]);
 #pragma unroll
     for (int i = 0; i < SUB_M; ++i) av[0][i] = *reinterpret_cast<const half8_t*>(abuf + 32 * i * kAPitch);
 #pragma unroll
@@ -304,39 +324,61 @@ __global__ __launch_bounds__(64 * WAVES) void grouped_gemm_kernel(
         for (int j = 0; j < SUB_N; ++j)
           bv[nxt][j] = decode8(pick_u32(rb[u][j][(t + 1) >> 2], (t + 1) & 3), scale_pair(sb[j], (t + 1) >> 1));
       }
+      // piece q of staging task i of the next stage's activations (A_PER_T <= 2)
+      const int si = (t >> 2) < C::A_PER_T ? (t >> 2) : 0, q = t & 3;
+      // threads past the tile's tasks decode the zeros their out-of-range loads
+      // returned into a spare 1 KB of LDS: with no branch around the decode,
+      // the compiler keeps every activation load where it is issued instead of
+      // sinking it next to its only use
+      if (kEarlyA && (t >> 2) < C::A_PER_T) {
+        const int task = tid + si * C::THREADS;
+        uint8_t* dst = task < C::A_TASKS ? sdst + (task >> 2) * kAPitch + (task & 3) * 64 + 16 * q
+                                         : lds + C::LDS + 16 * lane;
+        *reinterpret_cast<half8_t*>(dst) = decode8(pick_u32(ra[su][si], q), scale_pair(sa[si], q >> 1));
+      }
 #pragma unroll
       for (int i = 0; i < SUB_M; ++i)
 #pragma unroll
         for (int j = 0; j < SUB_N; ++j)
           acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(av[cur][i], bv[cur][j], acc[i][j], 0, 0, 0);
       // issue order: the next step's LDS reads first, then one MFMA followed by
-      // a share of the next step's VALU decode, repeated
+      // a share of the step's VALU work (next step's weight decode, this
+      // step's activation piece), repeated; the LDS write last
+      constexpr int kValu = 10 * SUB_N + (kEarlyA ? 9 : 0);
       __builtin_amdgcn_sched_group_barrier(0x100, SUB_M, 0);
 #pragma unroll
       for (int m = 0; m < SUB_M * SUB_N; ++m) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x002, (10 * SUB_N + SUB_M * SUB_N - 1) / (SUB_M * SUB_N), 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, (kValu + SUB_M * SUB_N - 1) / (SUB_M * SUB_N), 0);
       }
+      if (kEarlyA) __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);
     }
   };
 
   // Each item runs S stages (K's stage count rounded up to a multiple of P; the
-  // extra stages multiply zeros). The loads run P - 1 stages ahead across item
-  // boundaries: the last P - 1 stages of an item load the first P - 1 stages of
-  // the workgroup's next item (load_stage selects the source per stage), and the
-  // item's last stage decodes the next item's stage 0 into LDS, so the next
-  // item starts without waiting for memory. Stage s of an item uses LDS buffer
-  // (s + par) & 1, where par flips with every item when S is odd.
+  // extra stages multiply zeros). The loads run ahead across item boundaries
+  // (activations P stages, weights P - 1): the last stages of an item load the
+  // first stages of the workgroup's next item (load_a/load_b select the source
+  // per stage), and the item's last stage decodes the next item's stage 0 into
+  // LDS, so the next item starts without waiting for memory. Stage s of an
+  // item uses LDS buffer (s + par) & 1, where par flips with every item when S
+  // is odd.
   int par = 0;
   Src cur;
   make_src(slot, cur);
+  // prologue: activations of stages 0 .. P-1 and weights of stages 0 .. P-2
+  // (stage t in ring slot t % P); stage 0's activations decoded into LDS
 #pragma unroll
-  for (int p = 0; p < P - 1; ++p) load_stage(cur, cur, p, p);
+  for (int p = 0; p < P; ++p) {
+    if (kEarlyA || p < P - 1) load_a(cur, cur, p, p);
+    if (p < P - 1) load_b(cur, cur, p, p);
+  }
   store_a(0, 0);
   // NVFP4 output: the threshold table of the fixed global scale of h
-  uint16_t* h_tile = reinterpret_cast<uint16_t*>(lds + C::LDS);  // [BM][BN/2] BF16 h of one item
-  const uint4* h_lut = reinterpret_cast<const uint4*>(lds + C::LDS + C::BM * C::BN);
-  if (EPI == kEpiSiluNvfp4) build_threshold_lut(out_gs[0], reinterpret_cast<uint32_t*>(lds + C::LDS + C::BM * C::BN),
+  uint8_t* const epi_lds = lds + C::LDS + C::LDS_SPARE;
+  uint16_t* h_tile = reinterpret_cast<uint16_t*>(epi_lds);  // [BM][BN/2] BF16 h of one item
+  const uint4* h_lut = reinterpret_cast<const uint4*>(epi_lds + C::BM * C::BN);
+  if (EPI == kEpiSiluNvfp4) build_threshold_lut(out_gs[0], reinterpret_cast<uint32_t*>(epi_lds + C::BM * C::BN),
                                                 tid, C::THREADS);
   __syncthreads();
 
@@ -354,9 +396,23 @@ __global__ __launch_bounds__(64 * WAVES) void grouped_gemm_kernel(
 #pragma unroll
       for (int u = 0; u < P; ++u) {
         const int s = s0 + u;
-        load_stage(cur, nxt, s + P - 1, (u + P - 1) % P);
-        mma_stage((s + par) & 1, u);
-        store_a((s + 1 + par) & 1, (u + 1) % P);
+        // early activations: stage s + P into slot u (stage s's were decoded
+        // during stage s - 1), weights of stage s + P - 1; then stage s's MFMAs,
+        // during which stage s + 1's activations go from slot (u + 1) % P into
+        // LDS. Otherwise both P - 1 stages ahead and the decode after the MFMAs.
+        if (kEarlyA) {
+          load_a(cur, nxt, s + P, u);
+          load_b(cur, nxt, s + P - 1, (u + P - 1) % P);
+          // the stage's global loads stay ahead of all of its MFMA work, so
+          // that their latency runs under the whole stage
+          __builtin_amdgcn_sched_barrier(0);
+          mma_stage((s + par) & 1, u, (s + 1 + par) & 1, (u + 1) % P);
+        } else {
+          load_a(cur, nxt, s + P - 1, (u + P - 1) % P);
+          load_b(cur, nxt, s + P - 1, (u + P - 1) % P);
+          mma_stage((s + par) & 1, u, 0, 0);
+          store_a((s + 1 + par) & 1, (u + 1) % P);
+        }
         __syncthreads();
       }
     }
@@ -442,7 +498,7 @@ static int launch_cfg(const uint8_t* a_q, const uint8_t* a_sf, const int32_t* a_
   const int n_out = EPI != NVFP4_EPI_BF16 ? N / 2 : N;
   const int bn_out = EPI != NVFP4_EPI_BF16 ? C::BN / 2 : C::BN;
   // NVFP4 output adds the BF16 h tile of one item and the threshold table
-  constexpr int lds_bytes = C::LDS + (EPI == kEpiSiluNvfp4 ? C::BM * C::BN + kLutBytes : 0);
+  constexpr int lds_bytes = C::LDS + C::LDS_SPARE + (EPI == kEpiSiluNvfp4 ? C::BM * C::BN + kLutBytes : 0);
   const int n_ntiles = (n_out + bn_out - 1) / bn_out;
   const int max_tiles = rows_cap / C::BM + num_local;
   const int64_t max_items = (int64_t)max_tiles * n_ntiles;
