@@ -33,6 +33,8 @@ PEAK_FP4_TFLOPS = 10100.0     # MI355X dense fp4 MFMA (not usable for block-16 E
 PEAK_HBM_GBS = 8000.0
 PROFILE_DIR = os.path.join(ROOT, "profiles")
 COPY_CAL_BYTES = 1 << 30      # bytes read (and written) by the calibration copy
+N_XCD = 8                     # GRBM_GUI_ACTIVE counts the GPU-busy cycles of every XCD
+TRACE_STEPS = 5               # --steps of the kernel-trace commands the trace summaries name
 
 
 def log(msg):
@@ -256,31 +258,38 @@ def measure_layer(nv, weights, cfg, ids, w, x, dev, steps, warmup, settle_ms, fl
     for i in range(steps):
         l1_only[i][i_l1], l1_only[i][i_l1 + 1] = l1_evs[i]
     all_evs = [_events(ns) for _ in range(steps)]
+    flush = Flush(dev) if flushed else None
     settle(plain, settle_ms)
     for _ in range(warmup):
         plain()
     torch.cuda.synchronize()
+    # The passes follow one another with nothing but a synchronization
+    # between them (the event times are read at the end): an idle gap of a
+    # few tens of milliseconds lets the clocks drop, and the first steps
+    # after it run up to 40% slower.
     t = time.perf_counter()
     for i in range(steps):
         staged(l1_only[i])
     torch.cuda.synchronize()
     ms = (time.perf_counter() - t) * 1e3 / steps
-    l1 = [a.elapsed_time(b) for a, b in l1_evs]
     for i in range(steps):
         staged(all_evs[i])
     torch.cuda.synchronize()
-    step = [e[0].elapsed_time(e[-1]) for e in all_evs]
-    stage = {name: [e[i].elapsed_time(e[i + 1]) for e in all_evs] for i, name in enumerate(nv.STAGES)}
-    res = dict(ms=ms, step=stats(step),
-               stages={n: round(float(np.median(v)), 4) for n, v in stage.items()},
-               l1_ms=float(np.mean(l1)), l2_ms=float(np.mean(stage["a7_l2_gemm"])))
     t = time.perf_counter()
     for _ in range(steps):
         plain()
     torch.cuda.synchronize()
-    res["plain_ms"] = (time.perf_counter() - t) * 1e3 / steps
+    plain_ms = (time.perf_counter() - t) * 1e3 / steps
+    fl = per_call_times(plain, steps, flush) if flushed else None
+    l1 = [a.elapsed_time(b) for a, b in l1_evs]
+    step = [e[0].elapsed_time(e[-1]) for e in all_evs]
+    stage = {name: [e[i].elapsed_time(e[i + 1]) for e in all_evs] for i, name in enumerate(nv.STAGES)}
+    res = dict(ms=ms, step=stats(step),
+               stages={n: round(float(np.median(v)), 4) for n, v in stage.items()},
+               l1_ms=float(np.mean(l1)), l2_ms=float(np.mean(stage["a7_l2_gemm"])), plain_ms=plain_ms)
     if flushed:
-        res["flushed"] = stats(per_call_times(plain, steps, Flush(dev)))
+        res["flushed"] = stats(fl)
+        del flush
     counts = nv.ws_view(ws, lay, "counts", torch.int32, (cfg.num_local,)).cpu().numpy()
     res.update(S=int(counts.sum()), touched=int((counts > 0).sum()),
                tile_m=nv.nvfp4_moe_tile_m(T, k, cfg.num_local), out=out, d=(d_x, d_ids, d_w), ws=ws, lay=lay)
@@ -501,7 +510,7 @@ def achievable_peaks(dev, read_bytes=3 << 29, reps=10):
     n_cu = torch.cuda.get_device_properties(dev).multi_processor_count
     stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
     buf = torch.ones(read_bytes // 4, dtype=torch.float32, device=dev)
-    rgrid = n_cu * 8
+    rgrid = n_cu * 32
     rout = torch.empty(rgrid, dtype=torch.int32, device=dev)
 
     def read():
@@ -526,7 +535,7 @@ def achievable_peaks(dev, read_bytes=3 << 29, reps=10):
             "hbm_read_bytes": read_bytes, "hbm_read_ms": rt,
             "mfma_fp16_TFLOPs": round(tfs, 1), "mfma_frac_of_peak": round(tfs / PEAK_FP16_TFLOPS, 4),
             "mfma_flop": flop, "mfma_ms": mt,
-            "note": f"read: {rgrid} workgroups of 256 threads, eight 16-byte loads in flight per thread; MFMA: "
+            "note": f"read: {rgrid} workgroups of 256 threads, eight 16-byte non-temporal loads in flight per thread; MFMA: "
                     f"{mgrid} workgroups of 4 waves (2 per SIMD), 4 independent v_mfma_f32_32x32x16_f16 chains "
                     f"per wave, no memory traffic in the loop"}
 
@@ -591,8 +600,8 @@ def _per_kernel(rows):
     return {k: (float(np.mean(v)), len(v)) for k, v in by.items()}
 
 
-def _profile_header(f, what, workload, cmds, summarize):
-    f.write(f"# {what}, {workload} shard\n")
+def _profile_header(f, what, workload, cmds, summarize, title=None):
+    f.write(f"# {what}, {title or workload + ' shard'}\n")
     f.write("# command(s), from the repository root on the MI355X box:\n")
     for c in cmds:
         f.write(f"#   {c}\n")
@@ -605,6 +614,16 @@ def _bench_cmd(workload, extra=""):
             f"--settle-ms 0{extra}")
 
 
+def _kv(path):
+    """key = value lines of a profile summary (comments skipped)."""
+    kv = {}
+    for line in open(path):
+        if "=" in line and not line.lstrip().startswith("#"):
+            k, v = line.split("=", 1)
+            kv[k.strip()] = v.split("#")[0].strip()
+    return kv
+
+
 def read_traffic(workload: str, gemm: str = "l1"):
     """Per-launch HBM bytes of the L1 or L2 grouped GEMM from the committed
     counter summary, or None when absent or taken on a different kernel
@@ -612,11 +631,7 @@ def read_traffic(workload: str, gemm: str = "l1"):
     p = os.path.join(PROFILE_DIR, f"gemm_{workload}_traffic.txt")
     if not os.path.exists(p):
         return None
-    kv = {}
-    for line in open(p):
-        if "=" in line and not line.lstrip().startswith("#"):
-            k, v = line.split("=", 1)
-            kv[k.strip()] = v.split("#")[0].strip()
+    kv = _kv(p)
     if kv.get("kernel_source_sha") != kernel_source_sha() or f"{gemm}_hbm_bytes_per_launch" not in kv:
         return None
     return float(kv[f"{gemm}_hbm_bytes_per_launch"])
@@ -625,23 +640,35 @@ def read_traffic(workload: str, gemm: str = "l1"):
 def summarize_traffic(workload, fetch_dir, write_dir):
     """Per-launch HBM bytes of every kernel of the run, each counter (KiB per
     dispatch) scaled by what it reads for the plain 1 GiB copy of
-    --copy-calibration; the grouped GEMMs' figures also as key = value lines."""
+    --copy-calibration; the grouped GEMMs' figures also as key = value lines.
+    workload quantize: the two runs are of --quantize-only, which has no
+    calibration copy; the factors of the committed prefill summary (same
+    counters, same GPU model) scale them."""
     per, fac = {}, {}
+    quant = workload == "quantize"
     for tag, d, counter in (("fetch", fetch_dir, "FETCH_SIZE"), ("write", write_dir, "WRITE_SIZE")):
         rows = _counter_rows(d, counter)
         cal = [v for n, v in rows if "neg" in n.lower()]
-        if not cal:
+        if cal:
+            fac[tag] = COPY_CAL_BYTES / (float(np.median(cal)) * 1024.0)
+        elif quant:
+            fac[tag] = float(_kv(os.path.join(PROFILE_DIR, "gemm_prefill_traffic.txt"))[f"{tag}_copy_factor"])
+        else:
             raise SystemExit(f"{counter}: no calibration copy dispatches (run with --copy-calibration)")
-        fac[tag] = COPY_CAL_BYTES / (float(np.median(cal)) * 1024.0)
         per[tag] = _per_kernel([(n, v) for n, v in rows if "neg" not in n.lower()])
-    path = os.path.join(PROFILE_DIR, f"gemm_{workload}_traffic.txt")
+    name = "quantize_activation_traffic.txt" if quant else f"gemm_{workload}_traffic.txt"
+    path = os.path.join(PROFILE_DIR, name)
+    cmd = "python -u bench.py --quantize-only" if quant else _bench_cmd(workload, " --copy-calibration")
     with open(path, "w") as f:
-        _profile_header(f, "HBM traffic per kernel launch (FETCH_SIZE, WRITE_SIZE, copy-calibrated)", workload,
-                        [f"timeout -s KILL 180 rocprofv3 --pmc {c} -f csv -d {d} -o run -- "
-                         + _bench_cmd(workload, " --copy-calibration")
+        _profile_header(f, "HBM traffic per kernel launch (FETCH_SIZE, WRITE_SIZE, copy-calibrated)",
+                        workload,
+                        [f"timeout -s KILL 180 rocprofv3 --pmc {c} -f csv -d {d} -o run -- " + cmd
                          for c, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir))],
-                        f"--summarize-traffic {fetch_dir} {write_dir}")
-        f.write(f"# each counter (KiB per dispatch) is scaled by bytes / counter of a plain 1 GiB copy: "
+                        f"--summarize-traffic {fetch_dir} {write_dir}",
+                        title="activation quantizer alone (4096 x 7168 BF16, amax pass then quantize)" if quant
+                        else None)
+        src = "the factors of gemm_prefill_traffic.txt" if quant else "a plain 1 GiB copy"
+        f.write(f"# each counter (KiB per dispatch) is scaled by bytes / counter of {src}: "
                 f"fetch x{fac['fetch']:.4f}, write x{fac['write']:.4f}\n")
         f.write("# kernel | dispatches | fetch MB/launch | write MB/launch\n")
         for k in sorted(per["fetch"]):
@@ -649,13 +676,18 @@ def summarize_traffic(workload, fetch_dir, write_dir):
             wm = per["write"].get(k, (0.0, 0))[0]
             f.write(f"#   {k} | {n} | {fm * 1024 * fac['fetch'] / 1e6:.2f} | {wm * 1024 * fac['write'] / 1e6:.2f}\n")
         f.write(f"fetch_copy_factor = {fac['fetch']:.4f}\nwrite_copy_factor = {fac['write']:.4f}\n")
-        for g in ("l1_gemm", "l2_gemm"):
+        keys = ((("amax_kernel", "amax"), ("quantize_kernel<false>", "quantize")) if quant else
+                (("l1_gemm", "l1"), ("l2_gemm", "l2")))
+        for g, key in keys:
             if g in per["fetch"]:
                 fb = per["fetch"][g][0] * 1024 * fac["fetch"]
                 wb = per["write"].get(g, (0.0, 0))[0] * 1024 * fac["write"]
-                key = g.split("_")[0]
                 f.write(f"{key}_fetch_bytes_per_launch = {fb:.0f}\n{key}_write_bytes_per_launch = {wb:.0f}\n"
                         f"{key}_hbm_bytes_per_launch = {fb + wb:.0f}\n")
+        if quant:
+            M, K = 4096, 7168
+            f.write(f"# algorithmic: x read once {M * K * 2} B; codes {M * K // 2} B + scales {M * K // 16} B "
+                    f"+ gs 4 B written\n")
     print(open(path).read())
 
 
@@ -698,7 +730,7 @@ def summarize_trace(workload, d, all_workloads=False):
             o.write(f"# Kernel trace of the benchmark, {workload} shard alone\n\n")
         o.write("Command, from the repository root on the MI355X box:\n\n```\n")
         o.write(f"rocprofv3 --kernel-trace --stats -f csv -d {d} -o run -- python -u bench.py --config {workload} "
-                f"--steps 5 --warmup 1 --no-cpu-baseline --settle-ms 100{'' if all_workloads else ' --no-decode'}\n")
+                f"--steps {TRACE_STEPS} --warmup 1 --no-cpu-baseline --settle-ms 100{'' if all_workloads else ' --no-decode'}\n")
         o.write(f"python bench.py --config {workload} --summarize-trace {d}{' --trace-all' if all_workloads else ''}"
                 "\n```\n\n")
         o.write("Grouped GEMM template arguments: <SUB_M, SUB_N, WAVES, stages in flight, epilogue> "
@@ -710,19 +742,25 @@ def summarize_trace(workload, d, all_workloads=False):
                     f"{float(r['AverageNs']) / 1e3:.1f} | {float(r['MinNs']) / 1e3:.1f} | "
                     f"{float(r['MaxNs']) / 1e3:.1f} | {float(r['Percentage']):.1f}% |\n")
         if not all_workloads:
-            # the benchmark's last GPU work is the L1 GEMM timed alone with events (5 launches in the command
-            # above): the same launches, read from the per-dispatch trace
+            # measure_layer runs its passes back to back after the settle period and the warmup: the L1
+            # launches evented for roofline.avg_launch_ms, the all-stage pass, the plain pass and (not for
+            # decode) the flushed pass, TRACE_STEPS steps each; they are the last L1 dispatches of the trace
             t = glob.glob(os.path.join(d, "**", "*kernel_trace.csv"), recursive=True)
             if t:
                 l1 = sorted((int(r["Start_Timestamp"]), int(r["End_Timestamp"]))
                             for r in csv.DictReader(open(t[0]))
-                            if "grouped_gemm_kernel<" in r["Kernel_Name"]
-                            and _short_kernel_name(r["Kernel_Name"]).rstrip(">").endswith(", 1"))
-                last = [(e - b) / 1e3 for b, e in l1[-5:]]
-                if last:
-                    o.write(f"\nL1 GEMM, the last {len(last)} dispatches (the launches the benchmark times with HIP "
-                            f"events for `roofline.avg_launch_ms`): {np.mean(last):.1f} us on average "
-                            f"(min {min(last):.1f}, max {max(last):.1f}).\n")
+                            if _gemm_epi(r["Kernel_Name"]) in (1, 2))
+                passes = ["evented L1 (roofline.avg_launch_ms)", "all stages evented", "no events",
+                          "cache flushed before each step"][:3 if workload == "decode" else 4]
+                n = TRACE_STEPS
+                if len(l1) >= n * len(passes):
+                    o.write("\nL1 GEMM launches of the timed passes, from the per-dispatch trace:\n\n"
+                            "| pass | launches | avg us | min us | max us |\n|---|---|---|---|---|\n")
+                    tail = l1[len(l1) - n * len(passes):]
+                    for i, pname in enumerate(passes):
+                        dur = [(e - b) / 1e3 for b, e in tail[i * n:(i + 1) * n]]
+                        o.write(f"| {pname} | {len(dur)} | {np.mean(dur):.1f} | {min(dur):.1f} | "
+                                f"{max(dur):.1f} |\n")
     print(open(path).read())
 
 
@@ -759,9 +797,10 @@ def summarize_mfma(workload, d):
         _profile_header(o, "MFMA counters of the grouped GEMMs", workload,
                         [f"timeout -s KILL 180 rocprofv3 --pmc {' '.join(MFMA_COUNTERS)} -f csv -d {d} -o run -- "
                          + _bench_cmd(workload)], f"--summarize-mfma {d}")
-        o.write("# mfma_busy_share = SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE x 1024 SIMDs): the share of the\n"
-                "# kernel's active cycles in which a SIMD's matrix core works (both counters per launch; a\n"
-                "# 32x32x16 fp16 MFMA keeps the matrix core busy for 32 of these cycles)\n")
+        o.write("# mfma_busy_share = SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE / 8 XCDs x 1024 SIMDs): the\n"
+                "# share of the kernel's active cycles in which a SIMD's matrix core works (both counters per\n"
+                "# launch, GRBM_GUI_ACTIVE summed over the 8 XCDs; a 32x32x16 fp16 MFMA keeps the matrix core\n"
+                "# busy for 32 of these cycles: mfma_busy_cycles = 32 x mfma_instructions)\n")
         for g in ("l1_gemm", "l2_gemm", "l1_gemm_nvfp4"):
             if g not in tab:
                 continue
@@ -773,7 +812,7 @@ def summarize_mfma(workload, d):
             o.write(f"{key}_mfma_busy_cycles_per_launch = {t['SQ_VALU_MFMA_BUSY_CYCLES']:.0f}\n")
             o.write(f"{key}_grbm_gui_active_per_launch = {t['GRBM_GUI_ACTIVE']:.0f}\n")
             o.write(f"{key}_mfma_busy_share = "
-                    f"{t['SQ_VALU_MFMA_BUSY_CYCLES'] / (t['GRBM_GUI_ACTIVE'] * 1024):.4f}\n")
+                    f"{t['SQ_VALU_MFMA_BUSY_CYCLES'] / (t['GRBM_GUI_ACTIVE'] / N_XCD * 1024):.4f}\n")
             o.write(f"{key}_valu_mfma_coexec_cycles_per_launch = {t['SQ_VALU_MFMA_COEXEC_CYCLES']:.0f}\n")
             o.write(f"{key}_active_inst_valu_per_launch = {t['SQ_ACTIVE_INST_VALU']:.0f}\n")
             o.write(f"{key}_active_inst_lds_per_launch = {t['SQ_ACTIVE_INST_LDS']:.0f}\n")

@@ -84,6 +84,14 @@ __device__ __forceinline__ uint32_t buf_load4(__amdgpu_buffer_rsrc_t r, uint32_t
 __device__ __forceinline__ uint32_t buf_load2(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
   return __builtin_amdgcn_raw_buffer_load_b16(r, (int)voff, (int)soff, 0);
 }
+// The same loads with the non-temporal cache policy (for data read once).
+constexpr int kCachePolicyNT = 2;
+__device__ __forceinline__ uint4 buf_load16_nt(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+  return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, (int)soff, kCachePolicyNT));
+}
+__device__ __forceinline__ uint32_t buf_load4_nt(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+  return __builtin_amdgcn_raw_buffer_load_b32(r, (int)voff, (int)soff, kCachePolicyNT);
+}
 
 __device__ __forceinline__ uint32_t pick_u32(const uint4& v, int i) {
   return i == 0 ? v.x : i == 1 ? v.y : i == 2 ? v.z : v.w;
@@ -283,9 +291,18 @@ __global__ __launch_bounds__(64 * WAVES) void grouped_gemm_kernel(
       // (>= 2^31), which stays out of range after adding st * kPackChunk (< 2^31).
       const uint32_t base = in_cur ? cur.b_off[j] : nxt.b_off[j];
       const uint32_t chunk = in ? base + (uint32_t)st * kPackChunk : kOutOfRange;
-      rb[slot_][j][0] = buf_load16(rbw, b_lane, chunk);
-      rb[slot_][j][1] = buf_load16(rbw, b_lane + 1024u, chunk);
-      rsb[slot_][j] = buf_load4(rbw, bs_lane, chunk);
+      // decode-height tiles stream every weight byte once (one row tile per
+      // expert): non-temporal loads, measured 6-11% faster there; taller tiles
+      // re-read an expert's weights for its next row tile and keep them cached
+      if (SUB_M == 1) {
+        rb[slot_][j][0] = buf_load16_nt(rbw, b_lane, chunk);
+        rb[slot_][j][1] = buf_load16_nt(rbw, b_lane + 1024u, chunk);
+        rsb[slot_][j] = buf_load4_nt(rbw, bs_lane, chunk);
+      } else {
+        rb[slot_][j][0] = buf_load16(rbw, b_lane, chunk);
+        rb[slot_][j][1] = buf_load16(rbw, b_lane + 1024u, chunk);
+        rsb[slot_][j] = buf_load4(rbw, bs_lane, chunk);
+      }
     }
   };
   float16_t acc[SUB_M][SUB_N];

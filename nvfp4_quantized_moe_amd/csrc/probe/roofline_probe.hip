@@ -10,24 +10,30 @@ namespace {
 typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
 typedef float float16_t __attribute__((ext_vector_type(16)));
 
-// Every thread reads 16-byte vectors grid-stride, eight loads in flight, and
-// folds them with XOR; one word per workgroup is stored so that nothing is
-// dropped. n16 = number of 16-byte vectors.
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+
+// Every thread reads 16-byte vectors grid-stride with non-temporal loads,
+// eight in flight, and folds them with XOR; one word per workgroup is stored
+// so that nothing is dropped. n16 = number of 16-byte vectors. (Of the shapes
+// tried on MI355X -- 4 to 32 workgroups per CU, 4 to 16 loads in flight,
+// plain or non-temporal, grid-stride or one contiguous chunk per workgroup --
+// this one reads fastest.)
 __global__ __launch_bounds__(256) void read_kernel(const uint4* __restrict__ p, int64_t n16,
                                                    uint32_t* __restrict__ out) {
+  const u32x4_t* q = reinterpret_cast<const u32x4_t*>(p);
   const int64_t stride = (int64_t)gridDim.x * blockDim.x;
   uint32_t acc = 0;
   int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   for (; i + 7 * stride < n16; i += 8 * stride) {
-    uint4 v[8];
+    u32x4_t v[8];
 #pragma unroll
-    for (int u = 0; u < 8; ++u) v[u] = p[i + u * stride];
+    for (int u = 0; u < 8; ++u) v[u] = __builtin_nontemporal_load(q + i + u * stride);
 #pragma unroll
-    for (int u = 0; u < 8; ++u) acc ^= v[u].x ^ v[u].y ^ v[u].z ^ v[u].w;
+    for (int u = 0; u < 8; ++u) acc ^= v[u][0] ^ v[u][1] ^ v[u][2] ^ v[u][3];
   }
   for (; i < n16; i += stride) {
-    const uint4 v = p[i];
-    acc ^= v.x ^ v.y ^ v.z ^ v.w;
+    const u32x4_t v = __builtin_nontemporal_load(q + i);
+    acc ^= v[0] ^ v[1] ^ v[2] ^ v[3];
   }
   __shared__ uint32_t red[4];
   for (int o = 32; o > 0; o >>= 1) acc ^= (uint32_t)__shfl_xor((int)acc, o, 64);
