@@ -26,6 +26,9 @@
  *     per device) that nvfp4_quantize_noalloc uses in place of a workspace.
  *   - Calls are asynchronous on `stream` (a hipStream_t; NULL = the default
  *     stream) and never synchronize with the host.
+ *   - Every entry point that launches work returns an int: NVFP4_OK (0) or
+ *     one of the nvfp4_status codes below (declared int so that the ABI does
+ *     not depend on the size of an enum).
  *   - Arguments are validated on the host before anything is launched; a
  *     rejected call returns a nonzero status and launches nothing. A launch
  *     failure returns NVFP4_ERR_HIP (the error is taken with hipGetLastError,
@@ -77,7 +80,9 @@ int nvfp4moe_version(void);
  * gs = 0, sf = 0 and magnitude 0.
  *   q  : uint8 [B, M, K/2]    sf : uint8 [B, M, K/16]    gs_out : float [B]
  *   amax_in : float [B] or NULL (device; the h path passes the L1 epilogue's amax)
- *   ws : scratch of at least nvfp4_quantize_ws_bytes(B, M, K) bytes
+ *   ws : scratch of at least nvfp4_quantize_ws_bytes(B, M, K) bytes: the
+ *        per-workgroup amax partials, a fixed number per tensor, so the size
+ *        depends on B alone (M and K are accepted for a stable signature)
  * Requires B >= 1, M >= 0, K > 0, K % 32 == 0.
  */
 size_t nvfp4_quantize_ws_bytes(int64_t B, int64_t M, int64_t K);
