@@ -296,9 +296,12 @@ int nvfp4_moe_forward(const nvfp4_moe_weights* w, const void* x_bf16, int32_t T,
  * events[i + 1] after the launches of stage i:
  *   NVFP4_STAGE_AMAX_ROUTE  a1, amax of x, sharing its launch with a3: the whole
  *                           route when T*k <= 1024, else the per-chunk histograms
- *   NVFP4_STAGE_QUANT_X     a2, block quantization of x
- *   NVFP4_STAGE_ROUTE       the rest of a3 (scan, slot scatter, tile table) when
- *                           T*k > 1024; no launch (events back to back) otherwise
+ *   NVFP4_STAGE_QUANT_X     a2, block quantization of x; when T*k > 1024 its launch
+ *                           also runs the rest of a3 (scan, slot scatter, tile table)
+ *   NVFP4_STAGE_ROUTE       no launch of its own (events back to back), except for
+ *                           very large routes (more than 65536 histogram entries:
+ *                           ceil(T*k / 1024) x num_local), which take separate scan
+ *                           and scatter launches here
  *   NVFP4_STAGE_L1          a4 + a5, L1 grouped GEMM with the SiLU*up epilogue
  *   NVFP4_STAGE_QUANT_H     a6, re-quantization of h
  *   NVFP4_STAGE_L2          a7, L2 grouped GEMM

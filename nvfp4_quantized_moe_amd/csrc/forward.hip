@@ -154,14 +154,25 @@ static int moe_forward(const nvfp4_moe_weights* w, const void* x_bf16, int32_t T
                                       route_ws, stream)))
       return st;
     if ((st = mark(1 + NVFP4_STAGE_AMAX_ROUTE))) return st;
-    if ((st = nvfp4_launch_quantize_from_partials(x_bf16, T, H, qws, nvfp4_amax_grid((int64_t)T * H), x_q, x_sf,
-                                                  &scalars[0], stream)))
+    // a2 with the rest of a3 (scan and scatter) in its launch, or, past the
+    // fused route's size limit, a2 and then a3's two launches
+    const int gx = nvfp4_amax_grid((int64_t)T * H);
+    st = nvfp4_launch_quantize_route(x_bf16, T, H, qws, gx, x_q, x_sf, &scalars[0], topk_ids, topk_w, T, k,
+                                     expert_start, L, tile_m, route_ws, counts, offsets, slot_token, slot_expert,
+                                     slot_weight, token_slot, tiles, stream);
+    if (st == NVFP4_ERR_ARG) {
+      if ((st = nvfp4_launch_quantize_from_partials(x_bf16, T, H, qws, gx, x_q, x_sf, &scalars[0], stream)))
+        return st;
+      if ((st = mark(1 + NVFP4_STAGE_QUANT_X))) return st;
+      if ((st = nvfp4_launch_route_from_counts(topk_ids, topk_w, T, k, expert_start, L, tile_m, counts, offsets,
+                                               slot_token, slot_expert, slot_weight, token_slot, tiles, route_ws,
+                                               stream)))
+        return st;
+    } else if (st) {
       return st;
-    if ((st = mark(1 + NVFP4_STAGE_QUANT_X))) return st;
-    if ((st = nvfp4_launch_route_from_counts(topk_ids, topk_w, T, k, expert_start, L, tile_m, counts, offsets,
-                                             slot_token, slot_expert, slot_weight, token_slot, tiles, route_ws,
-                                             stream)))
+    } else if ((st = mark(1 + NVFP4_STAGE_QUANT_X))) {
       return st;
+    }
     if ((st = mark(1 + NVFP4_STAGE_ROUTE))) return st;
   }
   if (cap > 0) {

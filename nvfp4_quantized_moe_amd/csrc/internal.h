@@ -54,6 +54,19 @@ int nvfp4_launch_scatter(const void* y_bf16, const int32_t* token_slot, const fl
                          int32_t H, void* out_bf16, hipStream_t stream);
 int nvfp4_launch_fill_u32(uint32_t* p, int n, uint32_t v, hipStream_t stream);
 
+// Prefill-sized batches: quantize x from its amax partials (in ws) and run
+// the route's scan and scatter from the per-chunk histograms (in route_ws,
+// from nvfp4_launch_amax_count) in one launch. NVFP4_ERR_ARG when more than
+// kFusedRouteMaxCounts histogram entries (nchunks x num_local): then use
+// nvfp4_launch_quantize_from_partials and nvfp4_launch_route_from_counts.
+constexpr int64_t kFusedRouteMaxCounts = 1 << 16;
+int nvfp4_launch_quantize_route(const void* x_bf16, int64_t M, int64_t K, const void* ws, int n_partial,
+                                uint8_t* q, uint8_t* sf, float* gs_out, const int32_t* topk_ids,
+                                const float* topk_w, int32_t T, int32_t k, int32_t expert_start, int32_t num_local,
+                                int32_t tile_m, const void* route_ws, int32_t* counts, int32_t* offsets,
+                                int32_t* slot_token, int32_t* slot_expert, float* slot_weight, int32_t* token_slot,
+                                int32_t* tile_table, hipStream_t stream);
+
 // Decode-sized batches (T*k <= 1024): one launch for the amax partials of x
 // (nvfp4_amax_route_grid(T*H) of them, in partial) and the whole route.
 int nvfp4_amax_route_grid(int64_t per);

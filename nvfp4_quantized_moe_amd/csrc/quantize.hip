@@ -21,6 +21,7 @@
 #include "internal.h"
 #include "amax.h"
 #include "quant_block.h"
+#include "route_body.h"
 
 namespace nvfp4 {
 
@@ -68,18 +69,18 @@ __device__ __forceinline__ float block_gs_and_lut(const float* __restrict__ gs_i
   return gs;
 }
 
+// Workgroup bid of nbid quantizing tensor b: gs and threshold table, then a
+// grid-stride loop over the 16-element blocks, one block per thread.
 template <bool kRowsDev>
-__global__ __launch_bounds__(256) void quantize_kernel(const uint16_t* __restrict__ x, int64_t M, int64_t K,
-                                                       const int32_t* __restrict__ rows_dev,
-                                                       const float* __restrict__ gs_in,
-                                                       const float* __restrict__ amax_in,
-                                                       const uint32_t* __restrict__ partial, int n_partial,
-                                                       float* __restrict__ gs_out, uint8_t* __restrict__ q,
-                                                       uint8_t* __restrict__ sf) {
-  const int b = blockIdx.y;
+__device__ __forceinline__ void quantize_body(const uint16_t* __restrict__ x, int64_t M, int64_t K,
+                                              const int32_t* __restrict__ rows_dev, const float* __restrict__ gs_in,
+                                              const float* __restrict__ amax_in,
+                                              const uint32_t* __restrict__ partial, int n_partial,
+                                              float* __restrict__ gs_out, uint8_t* __restrict__ q,
+                                              uint8_t* __restrict__ sf, int b, int bid, int nbid) {
   __shared__ uint4 lut[kLutWords / 4];
   const float gs = block_gs_and_lut(gs_in, amax_in, partial, n_partial, b, reinterpret_cast<uint32_t*>(lut));
-  if (gs_out && blockIdx.x == 0 && threadIdx.x == 0) gs_out[b] = gs;
+  if (gs_out && bid == 0 && threadIdx.x == 0) gs_out[b] = gs;
   const double six_gs = 6.0 * (double)gs;  // exact
   int64_t rows = M;
   if (kRowsDev) rows = min(rows, (int64_t)rows_dev[0]);
@@ -95,9 +96,52 @@ __global__ __launch_bounds__(256) void quantize_kernel(const uint16_t* __restric
     sfb[blk] = (uint8_t)code;
   };
   const uint4* src = reinterpret_cast<const uint4*>(xb);
-  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
-  int64_t blk = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t stride = (int64_t)nbid * blockDim.x;
+  int64_t blk = (int64_t)bid * blockDim.x + threadIdx.x;
   for (; blk < nblk; blk += stride) one(blk, src[2 * blk], src[2 * blk + 1]);
+}
+
+template <bool kRowsDev>
+__global__ __launch_bounds__(256) void quantize_kernel(const uint16_t* __restrict__ x, int64_t M, int64_t K,
+                                                       const int32_t* __restrict__ rows_dev,
+                                                       const float* __restrict__ gs_in,
+                                                       const float* __restrict__ amax_in,
+                                                       const uint32_t* __restrict__ partial, int n_partial,
+                                                       float* __restrict__ gs_out, uint8_t* __restrict__ q,
+                                                       uint8_t* __restrict__ sf) {
+  quantize_body<kRowsDev>(x, M, K, rows_dev, gs_in, amax_in, partial, n_partial, gs_out, q, sf, blockIdx.y,
+                          blockIdx.x, gridDim.x);
+}
+
+// The layer's quantization of x for prefill-sized batches with the route's
+// scan and scatter in the same launch (both need only the per-chunk
+// histograms of the previous launch, and the quantization needs neither):
+// workgroups [0, nchunks) scatter one chunk each, computing their chunk's
+// first slot per expert from the histograms; workgroup nchunks writes counts,
+// offsets and the tile table; the others quantize x. Two launches of a few
+// microseconds each (scan, scatter) no longer run between quantize x and the
+// L1 GEMM.
+__global__ __launch_bounds__(256) void quantize_route_kernel(
+    const uint16_t* __restrict__ x, int64_t M, int64_t K, const uint32_t* __restrict__ partial, int n_partial,
+    float* __restrict__ gs_out, uint8_t* __restrict__ q, uint8_t* __restrict__ sf, const int32_t* __restrict__ ids,
+    const float* __restrict__ w, int32_t n, int32_t k, int32_t start, int32_t L, int tile_m, int nbits,
+    const int32_t* __restrict__ chunk_counts, int nchunks, int32_t* __restrict__ counts,
+    int32_t* __restrict__ offsets, int32_t* __restrict__ slot_token, int32_t* __restrict__ slot_expert,
+    float* __restrict__ slot_weight, int32_t* __restrict__ token_slot, int32_t* __restrict__ tile_table) {
+  const int bid = (int)blockIdx.x;
+  if (bid < nchunks) {
+    extern __shared__ int32_t route_lds[];  // running [L], totals [L]
+    const int S = route_chunk_bases(chunk_counts, nchunks, L, bid, route_lds, route_lds + L);
+    route_scatter_chunk(ids, w, n, k, start, L, nbits, S, bid, route_lds, slot_token, slot_expert, slot_weight,
+                        token_slot);
+    return;
+  }
+  if (bid == nchunks) {
+    route_tiles_wg(chunk_counts, nchunks, L, tile_m, counts, offsets, tile_table);
+    return;
+  }
+  quantize_body<false>(x, M, K, nullptr, nullptr, nullptr, partial, n_partial, gs_out, q, sf, 0, bid - nchunks - 1,
+                       (int)gridDim.x - nchunks - 1);
 }
 
 }  // namespace nvfp4
@@ -186,6 +230,32 @@ int nvfp4_launch_quantize_from_partials(const void* x_bf16, int64_t M, int64_t K
   dim3 grid((unsigned)quant_grid(M * (K / 16)), 1u);
   hipLaunchKernelGGL(quantize_kernel<false>, grid, dim3(256), 0, stream, x, M, K, nullptr, nullptr, nullptr,
                      partial, n_partial, gs_out, q, sf);
+  NVFP4_CHECK_LAUNCH();
+  return NVFP4_OK;
+}
+
+// Quantize x (amax partials in ws) and, in the same launch, the route's scan
+// and scatter from the per-chunk histograms in route_ws (layer, T*k > 1024).
+// Returns NVFP4_ERR_ARG when the histograms are too many for the per-workgroup
+// base computation (the caller then launches the route kernels).
+int nvfp4_launch_quantize_route(const void* x_bf16, int64_t M, int64_t K, const void* ws, int n_partial,
+                                uint8_t* q, uint8_t* sf, float* gs_out, const int32_t* topk_ids,
+                                const float* topk_w, int32_t T, int32_t k, int32_t expert_start, int32_t num_local,
+                                int32_t tile_m, const void* route_ws, int32_t* counts, int32_t* offsets,
+                                int32_t* slot_token, int32_t* slot_expert, float* slot_weight, int32_t* token_slot,
+                                int32_t* tile_table, hipStream_t stream) {
+  const int n = T * k;
+  const int nchunks = (int)(((int64_t)n + kRouteChunk - 1) / kRouteChunk);
+  const int L = num_local;
+  if (nchunks < 1 || (int64_t)nchunks * L > kFusedRouteMaxCounts) return NVFP4_ERR_ARG;
+  const int nq = quant_grid(M * (K / 16));
+  const int nr = nchunks + 1;
+  const int grid = nr + (nq - nr > 1 ? nq - nr : 1);
+  hipLaunchKernelGGL(quantize_route_kernel, dim3((unsigned)grid), dim3(256), (size_t)3 * L * 4, stream,
+                     reinterpret_cast<const uint16_t*>(x_bf16), M, K, reinterpret_cast<const uint32_t*>(ws),
+                     n_partial, gs_out, q, sf, topk_ids, topk_w, n, k, expert_start, L, tile_m, route_nbits(L),
+                     reinterpret_cast<const int32_t*>(route_ws), nchunks, counts, offsets, slot_token, slot_expert,
+                     slot_weight, token_slot, tile_table);
   NVFP4_CHECK_LAUNCH();
   return NVFP4_OK;
 }

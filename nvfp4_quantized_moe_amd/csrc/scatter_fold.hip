@@ -17,6 +17,8 @@
 
 namespace nvfp4 {
 
+constexpr int kScatterBatch = 8;  // slot rows loaded together per 8-element chunk
+
 __global__ __launch_bounds__(256) void scatter_kernel(const uint16_t* __restrict__ y,
                                                       const int32_t* __restrict__ token_slot,
                                                       const float* __restrict__ topk_w, int T, int k, int H,
@@ -34,18 +36,28 @@ __global__ __launch_bounds__(256) void scatter_kernel(const uint16_t* __restrict
   const int nchunk = H / 8;
   for (int c = blockIdx.y * blockDim.x + threadIdx.x; c < nchunk; c += gridDim.y * blockDim.x) {
     float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-    for (int j = 0; j < k; ++j) {
-      const int s = s_slot[j];
-      if (s < 0) continue;
-      const float w = s_w[j];
-      uint4 v = *reinterpret_cast<const uint4*>(y + (size_t)s * H + c * 8);
-      uint32_t u[4] = {v.x, v.y, v.z, v.w};
+    // up to 8 slots' loads in flight at once, then their adds in j order
+    for (int j0 = 0; j0 < k; j0 += kScatterBatch) {
+      uint4 v[kScatterBatch];
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const float p0 = w * bf16_to_f32(u[q] & 0xFFFFu);
-        const float p1 = w * bf16_to_f32(u[q] >> 16);
-        acc[2 * q] = acc[2 * q] + p0;
-        acc[2 * q + 1] = acc[2 * q + 1] + p1;
+      for (int jj = 0; jj < kScatterBatch; ++jj) {
+        const int j = j0 + jj;
+        const int s = j < k ? s_slot[j] : -1;
+        v[jj] = s >= 0 ? *reinterpret_cast<const uint4*>(y + (size_t)s * H + c * 8) : make_uint4(0, 0, 0, 0);
+      }
+#pragma unroll
+      for (int jj = 0; jj < kScatterBatch; ++jj) {
+        const int j = j0 + jj;
+        if (j >= k || s_slot[j] < 0) continue;
+        const float w = s_w[j];
+        const uint32_t u[4] = {v[jj].x, v[jj].y, v[jj].z, v[jj].w};
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const float p0 = w * bf16_to_f32(u[q] & 0xFFFFu);
+          const float p1 = w * bf16_to_f32(u[q] >> 16);
+          acc[2 * q] = acc[2 * q] + p0;
+          acc[2 * q + 1] = acc[2 * q + 1] + p1;
+        }
       }
     }
     uint4 o;
