@@ -257,13 +257,24 @@ extern "C" int nvfp4_moe_forward_static(const nvfp4_moe_weights* w, const void* 
   uint16_t* y = reinterpret_cast<uint16_t*>(R(NVFP4_WS_Y));
   const int32_t cap = T * k;
 
-  // a2 with gs_x: one pass over x
-  if (T > 0 && (st = nvfp4_launch_quantize_static(x_bf16, 1, T, H, &gs_in[0], nullptr, x_q, x_sf, stream)))
-    return st;
-  // a3: route
-  if ((st = nvfp4_launch_route(topk_ids, topk_w, T, k, expert_start, L, tile_m, counts, offsets, slot_token,
-                               slot_expert, slot_weight, token_slot, tiles, route_ws, stream)))
-    return st;
+  if (cap > 1024) {
+    // a2 with gs_x (one pass over x) and a3's per-chunk histograms in one
+    // launch, then the rest of a3
+    if ((st = nvfp4_launch_quantize_static_count(x_bf16, T, H, &gs_in[0], x_q, x_sf, topk_ids, T, k, expert_start, L,
+                                                 route_ws, stream)))
+      return st;
+    if ((st = nvfp4_launch_route_from_counts(topk_ids, topk_w, T, k, expert_start, L, tile_m, counts, offsets,
+                                             slot_token, slot_expert, slot_weight, token_slot, tiles, route_ws,
+                                             stream)))
+      return st;
+  } else {
+    // a2 with gs_x: one pass over x; a3: route
+    if (T > 0 && (st = nvfp4_launch_quantize_static(x_bf16, 1, T, H, &gs_in[0], nullptr, x_q, x_sf, stream)))
+      return st;
+    if ((st = nvfp4_launch_route(topk_ids, topk_w, T, k, expert_start, L, tile_m, counts, offsets, slot_token,
+                                 slot_expert, slot_weight, token_slot, tiles, route_ws, stream)))
+      return st;
+  }
   if (cap > 0) {
     if (tile_m >= 64) {
       // a4/a5/a6: L1, SiLU*up and NVFP4 h with gs_h in one kernel

@@ -67,6 +67,12 @@ int nvfp4_launch_quantize_route(const void* x_bf16, int64_t M, int64_t K, const 
                                 int32_t* slot_token, int32_t* slot_expert, float* slot_weight, int32_t* token_slot,
                                 int32_t* tile_table, hipStream_t stream);
 
+// Static layer, prefill-sized batches: quantize x with gs_in[0] and count the
+// route's per-chunk histograms (into route_ws) in one launch.
+int nvfp4_launch_quantize_static_count(const void* x_bf16, int64_t M, int64_t K, const float* gs_in, uint8_t* q,
+                                       uint8_t* sf, const int32_t* topk_ids, int32_t T, int32_t k,
+                                       int32_t expert_start, int32_t num_local, void* route_ws, hipStream_t stream);
+
 // Decode-sized batches (T*k <= 1024): one launch for the amax partials of x
 // (nvfp4_amax_route_grid(T*H) of them, in partial) and the whole route.
 int nvfp4_amax_route_grid(int64_t per);

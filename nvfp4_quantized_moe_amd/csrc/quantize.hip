@@ -113,6 +113,23 @@ __global__ __launch_bounds__(256) void quantize_kernel(const uint16_t* __restric
                           blockIdx.x, gridDim.x);
 }
 
+// The static layer's quantization of x with a fixed global scale for
+// prefill-sized batches, with the route's per-chunk histograms in the same
+// launch: workgroups [0, nchunks) count one chunk each (dispatched first, so
+// that they run beside the quantization), the others quantize x with gs_in[0].
+__global__ __launch_bounds__(256) void quantize_static_count_kernel(
+    const uint16_t* __restrict__ x, int64_t M, int64_t K, const float* __restrict__ gs_in, uint8_t* __restrict__ q,
+    uint8_t* __restrict__ sf, const int32_t* __restrict__ ids, int32_t n, int32_t start, int32_t L,
+    int32_t* __restrict__ chunk_counts, int nchunks) {
+  const int bid = (int)blockIdx.x;
+  if (bid < nchunks) {
+    route_count_body(ids, n, start, L, chunk_counts, bid);
+    return;
+  }
+  quantize_body<false>(x, M, K, nullptr, gs_in, nullptr, nullptr, 0, nullptr, q, sf, 0, bid - nchunks,
+                       (int)gridDim.x - nchunks);
+}
+
 // The layer's quantization of x for prefill-sized batches with the route's
 // scan and scatter in the same launch (both need only the per-chunk
 // histograms of the previous launch, and the quantization needs neither):
@@ -256,6 +273,23 @@ int nvfp4_launch_quantize_route(const void* x_bf16, int64_t M, int64_t K, const 
                      n_partial, gs_out, q, sf, topk_ids, topk_w, n, k, expert_start, L, tile_m, route_nbits(L),
                      reinterpret_cast<const int32_t*>(route_ws), nchunks, counts, offsets, slot_token, slot_expert,
                      slot_weight, token_slot, tile_table);
+  NVFP4_CHECK_LAUNCH();
+  return NVFP4_OK;
+}
+
+// Quantize x [M, K] with the fixed global scale gs_in[0] and, in the same
+// launch, the route's per-chunk histograms into route_ws (static layer,
+// T*k > 1024; nvfp4_launch_route_from_counts finishes the route).
+int nvfp4_launch_quantize_static_count(const void* x_bf16, int64_t M, int64_t K, const float* gs_in, uint8_t* q,
+                                       uint8_t* sf, const int32_t* topk_ids, int32_t T, int32_t k,
+                                       int32_t expert_start, int32_t num_local, void* route_ws, hipStream_t stream) {
+  const int n = T * k;
+  const int nchunks = (int)(((int64_t)n + kRouteChunk - 1) / kRouteChunk);
+  const int nq = quant_grid(M * (K / 16));
+  const int grid = nchunks + (nq - nchunks > 1 ? nq - nchunks : 1);
+  hipLaunchKernelGGL(quantize_static_count_kernel, dim3((unsigned)grid), dim3(256), (size_t)num_local * 4, stream,
+                     reinterpret_cast<const uint16_t*>(x_bf16), M, K, gs_in, q, sf, topk_ids, n, expert_start,
+                     num_local, reinterpret_cast<int32_t*>(route_ws), nchunks);
   NVFP4_CHECK_LAUNCH();
   return NVFP4_OK;
 }
