@@ -18,6 +18,7 @@
 namespace nvfp4 {
 
 constexpr int kScatterBatch = 8;  // slot rows loaded together per 8-element chunk
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
 __global__ __launch_bounds__(256) void scatter_kernel(const uint16_t* __restrict__ y,
                                                       const int32_t* __restrict__ token_slot,
@@ -65,7 +66,11 @@ __global__ __launch_bounds__(256) void scatter_kernel(const uint16_t* __restrict
     o.y = f32_to_bf16(acc[2]) | (f32_to_bf16(acc[3]) << 16);
     o.z = f32_to_bf16(acc[4]) | (f32_to_bf16(acc[5]) << 16);
     o.w = f32_to_bf16(acc[6]) | (f32_to_bf16(acc[7]) << 16);
-    *reinterpret_cast<uint4*>(out + (size_t)t * H + c * 8) = o;
+    // non-temporal: the output is not read again in the layer, and its lines
+    // would otherwise be written back from the caches during the next
+    // launches (the next layer step's amax pass ran 7 us longer for it)
+    const u32x4_t ov = {o.x, o.y, o.z, o.w};
+    __builtin_nontemporal_store(ov, reinterpret_cast<u32x4_t*>(out + (size_t)t * H + c * 8));
   }
 }
 
