@@ -58,8 +58,9 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--config", default="prefill", choices=["prefill", "decode", "skewed", "quantize"],
-                    help="headline workload (quantize: only with --summarize-trace of a --quantize-only run)")
+    ap.add_argument("--config", default="prefill", choices=["prefill", "decode", "skewed", "quantize", "peaks"],
+                    help="headline workload (quantize, peaks: only with --summarize-trace of a --quantize-only or "
+                         "--peaks run)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--settle-ms", type=float, default=300.0,
                     help="untimed GPU time spent on the workload before the warmup steps, so that "
@@ -103,8 +104,8 @@ def main():
     if args.summarize_valu:
         summarize_valu(args.config, args.summarize_valu)
         return
-    if args.config == "quantize" and not args.quantize_only:
-        raise SystemExit("bench.py: --config quantize only names the trace of a --quantize-only run")
+    if args.config in ("quantize", "peaks") and not (args.quantize_only or args.peaks):
+        raise SystemExit(f"bench.py: --config {args.config} only names the trace of a --quantize-only or --peaks run")
     if args.gpus != 1:
         print(f"bench.py: the layer runs one rank's share of the experts on one GPU; --gpus {args.gpus} is not "
               f"supported (expert-parallel sharding across GPUs and its all-reduce are not implemented)",
@@ -509,7 +510,11 @@ def quantize_c1(nv, W, dev, settle_ms, reps=50):
                     "the last-level cache", "gs": float(gs.item())}
 
 
-def achievable_peaks(dev, read_bytes=3 << 29, reps=10):
+PEAK_READ_BYTES = 3 << 29                  # bytes the read probe streams
+PEAK_MFMA_FLOP = 512 * 4.0 * 20000 * 4 * 32768   # FLOP of one MFMA probe launch on 256 CUs
+
+
+def achievable_peaks(dev, read_bytes=PEAK_READ_BYTES, reps=10):
     """What this GPU sustains in practice: a streaming read of a 1.5 GiB
     buffer (well past the 256 MB last-level cache) and a loop of independent
     fp16 MFMAs without memory traffic, each timed with events (median of
@@ -584,7 +589,7 @@ def _counter_rows(d, counter):
 
 
 def _short_kernel_name(n):
-    n = n.split("(")[0].replace("void ", "").replace("nvfp4::", "")
+    n = n.replace("(anonymous namespace)::", "").split("(")[0].replace("void ", "").replace("nvfp4::", "")
     return n if len(n) < 90 else n[:87] + "..."
 
 
@@ -714,6 +719,28 @@ def summarize_trace(workload, d, all_workloads=False):
     if not f:
         raise SystemExit(f"no kernel_stats.csv under {d}")
     rows = list(csv.DictReader(open(f[0])))
+    if workload == "peaks":
+        path = os.path.join(PROFILE_DIR, "achievable_peaks_kernel_trace.md")
+        with open(path, "w") as o:
+            o.write("# Kernel trace of the achievable-peak probes (bench.py --peaks): a streaming read of a 1.5 GiB "
+                    "buffer and a loop of independent fp16 MFMAs\n\n")
+            o.write("Command, from the repository root on the MI355X box:\n\n```\n")
+            o.write(f"rocprofv3 --kernel-trace --stats -f csv -d {d} -o run -- python -u bench.py --peaks\n")
+            o.write(f"python bench.py --config peaks --summarize-trace {d}\n```\n\n")
+            o.write("Each probe runs once untimed, then 10 times between events (the JSON medians).\n\n")
+            o.write("| kernel | calls | avg us | min us | max us | rate at the minimum |\n|---|---|---|---|---|---|\n")
+            for r in rows:
+                n = _short_kernel_name(r["Name"])
+                mn = float(r["MinNs"]) / 1e3
+                rate = ""
+                if "read" in n:
+                    rate = f"{PEAK_READ_BYTES / (mn * 1e-6) / 1e12:.2f} TB/s"
+                elif "mfma" in n:
+                    rate = f"{PEAK_MFMA_FLOP / (mn * 1e-6) / 1e12:.0f} TFLOP/s"
+                o.write(f"| `{n}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.1f} | {mn:.1f} | "
+                        f"{float(r['MaxNs']) / 1e3:.1f} | {rate} |\n")
+        print(open(path).read())
+        return
     if workload == "quantize":
         name = "quantize_activation_kernel_trace.md"
     else:
