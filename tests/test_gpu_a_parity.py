@@ -114,12 +114,17 @@ def _router_case(name):
     if name == "big_L":
         ids = rng.integers(0, 3000, (600, 6)).astype(np.int32)
         return ids, rng.random((600, 6)).astype(np.float32), 500, 2100
+    if name == "many_counts":
+        # 36 chunks x 2000 local experts = 72000 histogram entries: past the one-launch scan/scatter's
+        # limit (65536), so the separate scan and scatter kernels run
+        ids = rng.integers(0, 2400, (4500, 8)).astype(np.int32)
+        return ids, rng.random((4500, 8)).astype(np.float32), 300, 2000
     raise KeyError(name)
 
 
 @pytest.mark.parametrize("case", ["tiny", "mid", "mid_k1", "mid_skew", "decode", "prefill", "skewed",
                                   "random_out_of_range", "empty", "none_local", "big_L", "edge_1024",
-                                  "edge_1025"])
+                                  "edge_1025", "many_counts"])
 @pytest.mark.parametrize("tile_m", [32, 96, 128])
 def test_route_bit_exact(nv, case, tile_m):
     ids, w, start, L = _router_case(case)
