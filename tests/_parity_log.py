@@ -3,9 +3,8 @@
 Every GPU parity test records what it measured against the oracle (largest
 error relative to max|oracle|, BF16 ulps, cosine, or the number of
 bit-exact arrays it compared). At the end of the session conftest prints a
-compact summary, so that the tail of a pytest run carries the numbers, and
-writes them all as JSON to $NVFP4_PARITY_JSON, or to gpurun_out/ at the
-repository root when that folder exists.
+compact summary, so that the tail of a pytest run carries the numbers, and,
+when $NVFP4_PARITY_JSON names a file, writes them all there as JSON.
 """
 from __future__ import annotations
 
@@ -78,15 +77,10 @@ def summary_lines():
     return lines
 
 
-def write_json(root: str):
-    if not RECORDS:
-        return None
+def write_json():
     path = os.environ.get("NVFP4_PARITY_JSON")
-    if not path:
-        out = os.path.join(root, "gpurun_out")
-        if not os.path.isdir(out):
-            return None
-        path = os.path.join(out, "gpu_parity.json")
+    if not RECORDS or not path:
+        return None
     with open(path, "w") as f:
         json.dump(RECORDS, f, indent=1)
     return path

@@ -23,8 +23,8 @@ def pytest_terminal_summary(terminalreporter, exitstatus, config):
     lines = _parity_log.summary_lines()
     if not lines:
         return
-    path = _parity_log.write_json(ROOT)
+    path = _parity_log.write_json()
     for line in lines:
         terminalreporter.write_line(line)
     if path:
-        terminalreporter.write_line(f"  all figures: {os.path.relpath(path, ROOT)}")
+        terminalreporter.write_line(f"  all figures: {path}")
