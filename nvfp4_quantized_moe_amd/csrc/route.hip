@@ -9,14 +9,19 @@
 // The sort here is stable in the flat index t*k + j (histogram, prefix sum,
 // stable scatter), so the result is unique and deterministic.
 //
-// Three kernels over chunks of kRouteChunk flat entries:
+// Steps over chunks of kRouteChunk flat entries:
 //   count    per-chunk histogram in LDS
-//   scan     one workgroup: counts, offsets, per-chunk bases, GEMM tile table
+//   scan     counts, offsets, per-chunk bases, GEMM tile table
 //   scatter  per chunk, in flat order: rank among equal keys from ballots on
 //            the key bits, waves taking turns on an LDS running base per
 //            expert; also writes the -1 / 0 padding of slots >= S.
-// Batches of at most 1024 flat entries (decode) take all three steps in one
-// workgroup and one launch (route_small_kernel), with the same result.
+// Scan and scatter share one launch (route_scan_scatter_kernel): every
+// scatter workgroup sums the histograms for its own chunk's bases, and one
+// more workgroup writes counts, offsets and the tile table. Past 65536
+// histogram entries a one-workgroup scan kernel computes the bases first
+// (route_scan_kernel, then route_scatter_kernel). Batches of at most 1024 flat
+// entries (decode) take all steps in one workgroup and one launch
+// (route_small_kernel). All paths give the same result.
 #include "common.h"
 #include "internal.h"
 #include "amax.h"
