@@ -162,6 +162,7 @@ def main():
         "roofline_l2": roof_l2,
         "step_ms": r["step"],
         "stages_ms": r["stages"],
+        "stage_bandwidth": stage_bandwidth(cfg, r),
         "ms_per_step_without_stage_events": round(r["plain_ms"], 4),
         "timing_note": ("value and ms_per_step: wall clock over the timed steps (synchronized on both sides), "
                         "each step with HIP events on the layer's stream around its L1 grouped GEMM; roofline: "
@@ -309,6 +310,26 @@ def measure_layer(nv, weights, cfg, ids, w, x, dev, steps, warmup, settle_ms, fl
     return res
 
 
+def stage_bandwidth(cfg, r):
+    """The memory-bound stages against HBM peak: algorithmic bytes of each
+    (read x for the amax; read x, write codes and scales for quantize x; the
+    same for h's S valid rows; read the k local slots' rows of Y and write the
+    output for the scatter) over the stage's median time from the
+    stage-evented pass (which includes a few microseconds of event overhead)."""
+    T, H, I, S = cfg.tokens, cfg.hidden, cfg.inter, r["S"]
+    st = r["stages"]
+    rows = {"a1_amax_route": T * H * 2,
+            "a2_quantize_x": T * H * 2 + T * H // 2 + T * H // 16,
+            "a6_quantize_h": S * I * 2 + S * I // 2 + S * I // 16,
+            "a8_scatter": S * H * 2 + T * H * 2}
+    out = {}
+    for name, b in rows.items():
+        ms = st[name]
+        gbs = b / (ms * 1e-3) / 1e9 if ms > 0 else 0.0
+        out[name] = {"bytes": b, "ms": ms, "GBs": round(gbs, 1), "hbm_frac": round(gbs / PEAK_HBM_GBS, 4)}
+    return out
+
+
 def gemm_rooflines(cfg, r):
     """Roofline objects of the L1 and L2 grouped GEMMs from the mean launch
     times of the timed region: algorithmic FLOP (slots x 2 x N x K, padding
@@ -380,7 +401,8 @@ def decode_shard(nv, weights, W, dev, steps, warmup, settle_ms, bf16_w=None):
         "ms_per_step_without_stage_events": round(rd["plain_ms"], 4),
         "touched_experts": rd["touched"], "slots": rd["S"], "weight_bytes_per_step": bytes_w,
         "layer_weight_GBs": round(gbs, 1), "layer_hbm_frac": round(gbs / PEAK_HBM_GBS, 4),
-        "step_ms": rd["step"], "stages_ms": rd["stages"], "roofline_l1": l1, "roofline_l2": l2,
+        "step_ms": rd["step"], "stages_ms": rd["stages"], "stage_bandwidth": stage_bandwidth(dcfg, rd),
+        "roofline_l1": l1, "roofline_l2": l2,
         "flushed": dict(rd["flushed"], layer_hbm_frac=round(bytes_w / (fl * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)),
     }
     if bf16_w is not None:
@@ -476,7 +498,7 @@ def skewed_shard(nv, W, dev, settle_ms, steps, warmup):
             "empty_experts": int((counts == 0).sum()), "max_expert_share": round(float(counts.max()) / S, 4),
             "layer_tflops": round(S * 2.0 * (2 * I * H + H * I) / (r["ms"] * 1e-3) / 1e12, 2),
             "step_ms": r["step"], "step_ms_flushed": r["flushed"], "stages_ms": r["stages"],
-            "roofline_l1": l1, "roofline_l2": l2}
+            "stage_bandwidth": stage_bandwidth(cfg, r), "roofline_l1": l1, "roofline_l2": l2}
 
 
 def static_scales(nv, weights, W, dev, settle_ms, rounds=5):
