@@ -300,7 +300,7 @@ def _deq_ref(P, cfg, x, ids, w):
 
 @pytest.mark.parametrize("name,fold", [("tiny", True), ("mid", True), ("mid_k1", True), ("mid_skew", True),
                                        ("mid_route3", True), ("tiny", False), ("mid_skew", False),
-                                       ("wide_route", True)])
+                                       ("wide_route", True), ("long_k1", True)])
 def test_layer(nv, name, fold):
     cfg, ids, w, x, wg, wu, wd = _layer_inputs(name)
     log(f"layer {name} fold={fold} T={cfg.tokens} k={cfg.top_k} L={cfg.num_local} H={cfg.hidden} I={cfg.inter}")

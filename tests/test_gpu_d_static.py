@@ -176,7 +176,7 @@ def _layer(name):
 
 
 @pytest.mark.parametrize("name,fold", [("tiny", True), ("mid", True), ("mid_skew", True), ("mid_skew", False),
-                                       ("mid_route3", True), ("wide_route", True)])
+                                       ("mid_route3", True), ("wide_route", True), ("long_k1", True)])
 def test_layer_static(nv, name, fold):
     cfg, ids, w, x, wg, wu, wd = _layer(name)
     log(f"layer_static {name} fold={fold} T={cfg.tokens} k={cfg.top_k} L={cfg.num_local}")

@@ -93,6 +93,10 @@ CONFIGS = {
     # more than 1024 slot entries (the chunked route) with decode-height (32-row) tiles
     "mid_route3": LayerConfig("mid_route3", 13, tokens=200, top_k=8, num_global=384, num_local=48,
                               expert_start=96, hidden=256, inter=128),
+    # top-1 with more than 1024 slot entries: the chunked route inside the quantize launch and prefill-height
+    # (96-row) GEMM tiles at a small size
+    "long_k1": LayerConfig("long_k1", 15, tokens=3000, top_k=1, num_global=12, num_local=12,
+                           expert_start=0, hidden=256, inter=128),
     # many local experts: 36 route chunks x 2048 experts = 73728 histogram entries, past the limit of the
     # route's scan/scatter inside the quantize launch (the layer then launches them separately)
     "wide_route": LayerConfig("wide_route", 14, tokens=4608, top_k=8, num_global=2560, num_local=2048,
