@@ -35,7 +35,7 @@ __device__ __forceinline__ float e4m3_to_f32(uint32_t code) {
 
 // Nearest E4M3 code to a non-negative double, ties to the even code,
 // saturating at 448 (0x7E). Subnormal codes are multiples of 2^-9.
-__device__ __forceinline__ uint32_t e4m3_encode_rne_sat(double v) {
+__host__ __device__ __forceinline__ uint32_t e4m3_encode_rne_sat(double v) {
   if (!(v < 448.0)) return 0x7Eu;                      // also catches +inf
   if (v < 0.015625) {                                   // below 2^-6: step 2^-9
     return (uint32_t)__builtin_rint(v * 512.0);        // 8 -> 0x08 = 2^-6, still exact

@@ -479,8 +479,7 @@ __global__ __launch_bounds__(64 * WAVES) void grouped_gemm_kernel(
       // h of the item is in LDS: each thread quantizes whole 16-column blocks
       // (exact roundings, the quantizer's own code) and writes them as NVFP4
       __syncthreads();
-      const float gs_o = out_gs[0];
-      const double six_gs_o = 6.0 * (double)gs_o;
+      const QuantScale qs_o = quant_scale(out_gs[0]);
       uint8_t* d_q = reinterpret_cast<uint8_t*>(d);
       for (int blk = tid; blk < C::BM * (C::BN / 32); blk += C::THREADS) {
         const int lrow = blk / (C::BN / 32), lb = blk % (C::BN / 32);
@@ -490,7 +489,7 @@ __global__ __launch_bounds__(64 * WAVES) void grouped_gemm_kernel(
         const uint4 v0 = src[0], v1 = src[1];
         const uint32_t w[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
         uint2 packed;
-        const uint32_t code = quantize_block16(w, gs_o, six_gs_o, h_lut, &packed);
+        const uint32_t code = quantize_block16(w, qs_o, h_lut, &packed);
         *reinterpret_cast<uint2*>(d_q + (size_t)row * (n_out / 2) + col0 / 2) = packed;
         d_sf[(size_t)row * (n_out / 16) + col0 / 16] = (uint8_t)code;
       }

@@ -7,8 +7,7 @@
 //                         sign kept in bit 3 of the nibble
 // tests history, packing-along-K commit: two nibbles per byte along K.
 //
-// The exact per-block rounding (threshold table in LDS, scale from a float64
-// quotient) is in quant_block.h.
+// The exact per-block rounding (threshold table in LDS) is in quant_block.h.
 //
 // Kernels: amax (wave reductions, one partial maximum per workgroup on the
 // float bits, order-free) and quantize (each workgroup reduces the partials,
@@ -31,6 +30,7 @@ __global__ void fill_u32_kernel(uint32_t* p, int n, uint32_t v) {
 }
 
 constexpr int kQuantPerCu = 8;      // quantize workgroups per CU (at most the resident count)
+constexpr int kQuantBlocks = 4;     // 16-element blocks per thread and round
 
 __global__ __launch_bounds__(kAmaxThreads) void amax_kernel(const uint16_t* __restrict__ x, int64_t per_batch,
                                                    const int32_t* __restrict__ rows_dev, int64_t K,
@@ -70,7 +70,7 @@ __device__ __forceinline__ float block_gs_and_lut(const float* __restrict__ gs_i
 }
 
 // Workgroup bid of nbid quantizing tensor b: gs and threshold table, then a
-// grid-stride loop over the 16-element blocks, one block per thread.
+// grid-stride loop over the 16-element blocks.
 template <bool kRowsDev>
 __device__ __forceinline__ void quantize_body(const uint16_t* __restrict__ x, int64_t M, int64_t K,
                                               const int32_t* __restrict__ rows_dev, const float* __restrict__ gs_in,
@@ -81,7 +81,7 @@ __device__ __forceinline__ void quantize_body(const uint16_t* __restrict__ x, in
   __shared__ uint4 lut[kLutWords / 4];
   const float gs = block_gs_and_lut(gs_in, amax_in, partial, n_partial, b, reinterpret_cast<uint32_t*>(lut));
   if (gs_out && bid == 0 && threadIdx.x == 0) gs_out[b] = gs;
-  const double six_gs = 6.0 * (double)gs;  // exact
+  const QuantScale qs = quant_scale(gs);
   int64_t rows = M;
   if (kRowsDev) rows = min(rows, (int64_t)rows_dev[0]);
   const int64_t nblk = rows * (K / 16);
@@ -91,14 +91,28 @@ __device__ __forceinline__ void quantize_body(const uint16_t* __restrict__ x, in
   auto one = [&](int64_t blk, const uint4& v0, const uint4& v1) {
     const uint32_t w[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
     uint2 packed;
-    const uint32_t code = quantize_block16(w, gs, six_gs, lut, &packed);
+    const uint32_t code = quantize_block16(w, qs, lut, &packed);
     *reinterpret_cast<uint2*>(qb + blk * 8) = packed;
     sfb[blk] = (uint8_t)code;
   };
   const uint4* src = reinterpret_cast<const uint4*>(xb);
   const int64_t stride = (int64_t)nbid * blockDim.x;
   int64_t blk = (int64_t)bid * blockDim.x + threadIdx.x;
-  for (; blk < nblk; blk += stride) one(blk, src[2 * blk], src[2 * blk + 1]);
+  // kQuantBlocks blocks per thread and round, all loads issued before the
+  // first block is quantized (blocks past the end re-read the last block and
+  // store nothing)
+  for (; blk < nblk; blk += kQuantBlocks * stride) {
+    uint4 v[kQuantBlocks][2];
+#pragma unroll
+    for (int u = 0; u < kQuantBlocks; ++u) {
+      const int64_t bu = min(blk + u * stride, nblk - 1);
+      v[u][0] = src[2 * bu];
+      v[u][1] = src[2 * bu + 1];
+    }
+#pragma unroll
+    for (int u = 0; u < kQuantBlocks; ++u)
+      if (blk + u * stride < nblk) one(blk + u * stride, v[u][0], v[u][1]);
+  }
 }
 
 template <bool kRowsDev>
