@@ -35,10 +35,12 @@
 
 namespace nvfp4 {
 
-// 128 scale codes x 8 words: words 0..6 of entry `code` hold the E2M1
-// midpoint offset pairs of that scale code; word 7 of entry c holds the two
-// E4M3 midpoint offsets that settle a scale-code estimate c (c <= 126).
-constexpr int kLutWords = 128 * 8;
+// Threshold table in LDS: words [0, 512) hold 16-bit E2M1 midpoint offsets,
+// four words (seven offsets and a spare) per scale code; word kScaleWords + c
+// (c <= 126) holds the two E4M3 midpoint offsets that settle a scale-code
+// estimate c. 16-bit entries keep the per-block reads to 20 bytes.
+constexpr int kScaleWords = 512;
+constexpr int kLutWords = kScaleWords + 128;
 constexpr int kLutBytes = kLutWords * 4;
 
 // Offset of threshold U in one 16-bit half (0 for U >= 0x7FFF: nothing passes).
@@ -99,28 +101,33 @@ __host__ __device__ __forceinline__ uint32_t scale_midpoint_offset(int c, float 
   return threshold_offset(midpoint_threshold(m, gs, (c & 1) != 0));
 }
 
-// Threshold table for global scale gs. Entry `code`, word j < 7: the offset
-// pair of E2M1 midpoint j of that scale code (all zero, so that nothing
-// passes, for code 0 and for gs <= 0 or NaN). Word 7 of entry c: the offset
-// of the scale midpoint below c in the low half (one that always passes for
-// c = 0) and of the one above c in the high half (none for c >= 126). Threads
-// tid = 0 .. nthreads-1 fill it together; the caller synchronises.
+// E2M1 midpoint j (0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5) of scale code `code`
+// as a 16-bit offset (0, so that nothing passes, for code 0 and for gs <= 0
+// or NaN); an exact tie rounds up at the odd j (0.75, 1.75, 3.5: the upper
+// E2M1 code is even). The midpoint times the scale value has 3 x 4
+// significant bits, exact in float32.
+__host__ __device__ __forceinline__ uint32_t e2m1_midpoint_offset(int code, int j, float gs) {
+  if (!(code > 0 && code <= 0x7E && gs > 0.0f)) return 0u;
+  const float mid = j < 4 ? 0.25f + 0.5f * j : (j == 6 ? 5.0f : j - 1.5f);
+  return threshold_offset(midpoint_threshold(mid * e4m3_value((uint32_t)code), gs, (j & 1) != 0));
+}
+
+// Word i of the threshold table for global scale gs: for i < kScaleWords,
+// offsets of midpoints 2(i%4) (low half) and 2(i%4)+1 (high half) of scale
+// code i/4 (the high half of the fourth word is unused); word kScaleWords + c:
+// the offset of the scale midpoint below c in the low half (one that always
+// passes for c = 0) and of the one above c in the high half (none for
+// c >= 126). Threads tid = 0 .. nthreads-1 fill it together; the caller
+// synchronises.
 __host__ __device__ __forceinline__ uint32_t threshold_lut_word(float gs, int i) {
-  const int code = i >> 3, j = i & 7;
-  if (j == 7) {
-    const uint32_t lo = code == 0 ? kAlwaysPasses : scale_midpoint_offset(code - 1, gs);
-    const uint32_t hi = code >= 126 ? 0u : scale_midpoint_offset(code, gs);
+  if (i >= kScaleWords) {
+    const int c = i - kScaleWords;
+    const uint32_t lo = c == 0 ? kAlwaysPasses : scale_midpoint_offset(c - 1, gs);
+    const uint32_t hi = c >= 126 ? 0u : scale_midpoint_offset(c, gs);
     return lo | (hi << 16);
   }
-  uint32_t u = 0xFFFFu;
-  if (code > 0 && code <= 0x7E && gs > 0.0f) {
-    // E2M1 midpoint j (0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5); an exact tie
-    // rounds up at the odd j (0.75, 1.75, 3.5: the upper code is even)
-    const float mid = j < 4 ? 0.25f + 0.5f * j : (j == 6 ? 5.0f : j - 1.5f);
-    // midpoint times the scale value: 3 x 4 significant bits, exact in float32
-    u = midpoint_threshold(mid * e4m3_value((uint32_t)code), gs, (j & 1) != 0);
-  }
-  return threshold_offset_pair(u);
+  const int code = i >> 2, j = 2 * (i & 3);
+  return e2m1_midpoint_offset(code, j, gs) | (j + 1 < 7 ? e2m1_midpoint_offset(code, j + 1, gs) << 16 : 0u);
 }
 __device__ __forceinline__ void build_threshold_lut(float gs, uint32_t* lut, int tid, int nthreads) {
   for (int i = tid; i < kLutWords; i += nthreads) lut[i] = threshold_lut_word(gs, i);
@@ -159,9 +166,9 @@ __host__ __device__ __forceinline__ uint32_t e4m3_code_near(float q) {
   return c < 0x7Eu ? c : 0x7Eu;
 }
 
-// Exact nearest E4M3 code to bmax / (6 gs) (bmax: BF16 bits of the block
-// maximum, <= 0x7F80): the estimate c, then c - 1 plus the two midpoint tests
-// of table word 7 of entry c.
+// Exact nearest E4M3 code to bmax / (6 gs) (bmax: BF16 bits of a finite
+// block maximum, < 0x7F80): the estimate c, then c - 1 plus the two midpoint
+// tests of table word kScaleWords + c.
 __host__ __device__ __forceinline__ uint32_t block_scale_code(uint32_t bmax, const QuantScale& qs,
                                                              const uint32_t* lut) {
   const float b = __builtin_bit_cast(float, bmax << 16);
@@ -170,7 +177,7 @@ __host__ __device__ __forceinline__ uint32_t block_scale_code(uint32_t bmax, con
     c = e4m3_code_near(__builtin_ldexpf(b * qs.rcp, qs.nexp));
   else
     c = e4m3_encode_rne_sat((double)b / qs.six_gs);
-  const uint32_t s = (bmax | (bmax << 16)) + lut[8 * c + 7];
+  const uint32_t s = (bmax | (bmax << 16)) + lut[kScaleWords + c];
   return c - 1u + ((s >> 15) & 1u) + (s >> 31);
 }
 
@@ -262,14 +269,27 @@ __host__ __device__ __forceinline__ uint32_t block_max_bits(const uint32_t w[8])
   return m[0][0] > m[0][1] ? m[0][0] : m[0][1];
 }
 
+// The seven E2M1 offset pairs of scale code `code` from its four table words
+// (each 16-bit offset copied into both halves by a byte permute).
+__host__ __device__ __forceinline__ void e2m1_offsets(const uint4& t, uint32_t cc[7]) {
+  constexpr uint32_t kLo = 0x01000100u, kHi = 0x03020302u;
+  cc[0] = byte_perm(t.x, t.x, kLo);
+  cc[1] = byte_perm(t.x, t.x, kHi);
+  cc[2] = byte_perm(t.y, t.y, kLo);
+  cc[3] = byte_perm(t.y, t.y, kHi);
+  cc[4] = byte_perm(t.z, t.z, kLo);
+  cc[5] = byte_perm(t.z, t.z, kHi);
+  cc[6] = byte_perm(t.w, t.w, kLo);
+}
+
 // One block: w[j] holds elements 2j (low half) and 2j+1 (high half) as BF16.
 // Writes the 16 nibbles (element 2j in the low nibble of byte j) to *out and
 // returns the scale code. qs = quant_scale(gs); lut is the table of gs.
 __device__ __forceinline__ uint32_t quantize_block16(const uint32_t w[8], const QuantScale& qs, const uint4* lut,
                                                      uint2* out) {
   const uint32_t code = block_scale_code(block_max_bits(w), qs, reinterpret_cast<const uint32_t*>(lut));
-  const uint4 t0 = lut[2 * code], t1 = lut[2 * code + 1];
-  const uint32_t cc[7] = {t0.x, t0.y, t0.z, t0.w, t1.x, t1.y, t1.z};
+  uint32_t cc[7];
+  e2m1_offsets(lut[code], cc);
   *out = make_uint2(pack_quads(nibble_quad(w[0], w[1], cc), nibble_quad(w[2], w[3], cc)),
                     pack_quads(nibble_quad(w[4], w[5], cc), nibble_quad(w[6], w[7], cc)));
   return code;

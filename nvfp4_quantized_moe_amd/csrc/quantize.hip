@@ -30,7 +30,7 @@ __global__ void fill_u32_kernel(uint32_t* p, int n, uint32_t v) {
 }
 
 constexpr int kQuantPerCu = 8;      // quantize workgroups per CU (at most the resident count)
-constexpr int kQuantBlocks = 4;     // 16-element blocks per thread and round
+constexpr int kQuantBlocks = 2;     // 16-element blocks per thread and round
 
 __global__ __launch_bounds__(kAmaxThreads) void amax_kernel(const uint16_t* __restrict__ x, int64_t per_batch,
                                                    const int32_t* __restrict__ rows_dev, int64_t K,

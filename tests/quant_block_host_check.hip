@@ -146,6 +146,28 @@ int main(int argc, char** argv) {
         if ((a != b || e1 != e2) && ++bad <= 5) printf("round-down mismatch: %a * %a\n", m, g);
       }
   }
+  // the E2M1 part of the table: every scale code's four words expand to the
+  // seven offset pairs of its midpoints
+  {
+    const float mids[7] = {0.25f, 0.75f, 1.25f, 1.75f, 2.5f, 3.5f, 5.0f};
+    const float gss[] = {0.0f, 1.0f, 2000.0f / 2688.0f, 0x1p-60f, 1e-40f, 3.0e38f / 2688.0f, 0.3f, 7.1e-3f};
+    for (float g : gss) {
+      uint32_t lut[kLutWords];
+      for (int i = 0; i < kLutWords; ++i) lut[i] = threshold_lut_word(g, i);
+      for (int code = 0; code < 128; ++code) {
+        uint32_t cc[7];
+        const uint4 t = make_uint4(lut[4 * code], lut[4 * code + 1], lut[4 * code + 2], lut[4 * code + 3]);
+        e2m1_offsets(t, cc);
+        for (int j = 0; j < 7; ++j) {
+          uint32_t want = 0;
+          if (code > 0 && code <= 0x7E && g > 0.0f)
+            want = threshold_offset_pair(midpoint_threshold((float)(mids[j] * e4m3_ref(code)), g, (j & 1) != 0));
+          ++n;
+          if (cc[j] != want && ++bad <= 5) printf("table mismatch: gs %a code %d midpoint %d\n", g, code, j);
+        }
+      }
+    }
+  }
   printf("pairs %ld mismatches %ld\n", n, bad);
   return bad != 0;
 }
