@@ -133,6 +133,13 @@ __device__ __forceinline__ half8_t decode8(uint32_t w, half2_t s2) {
 
 __device__ __forceinline__ float silu_f32(float g) { return g * __builtin_amdgcn_rcpf(1.0f + __expf(-g)); }
 
+// h = BF16(SiLU(g) * u) with g = BF16(acc_gate * alpha) and u = BF16(acc_up * alpha_up), as BF16 bits
+__device__ __forceinline__ uint32_t silu_mul_bf16(float acc_gate, float acc_up, float alpha, float alpha_up) {
+  const float g = bf16_to_f32(f32_to_bf16(acc_gate * alpha));
+  const float u = bf16_to_f32(f32_to_bf16(acc_up * alpha_up));
+  return f32_to_bf16(silu_f32(g) * u);
+}
+
 // Work item = (row tile from the tile table, column tile). The row tile's
 // activations are decoded once per stage into LDS as fp16 and shared by the
 // waves; each wave streams its own 32*SUB_N weight rows from global memory
@@ -315,6 +322,8 @@ __global__ __launch_bounds__(64 * WAVES) void grouped_gemm_kernel(
   // tiles (32 rows, weight-streaming) keep the decode after the MFMAs, which
   // holds fewer registers (more resident workgroups per CU).
   constexpr bool kEarlyA = C::BM >= 64;
+  // BF16 output of prefill-height tiles: two rows per 4-byte store (below)
+  constexpr bool kPairStores = C::BM >= 64;
   auto mma_stage = [&](int buf, int u, int sbuf, int su) {
     const uint8_t* abuf = lds + buf * (C::BM * kAPitch) + lr * kAPitch + 128 * lg;
     uint8_t* sdst = lds + sbuf * (C::BM * kAPitch);
@@ -443,34 +452,76 @@ __global__ __launch_bounds__(64 * WAVES) void grouped_gemm_kernel(
     const float alpha = a_gs[0] * b_gs[dual_gs ? 2 * e : e];
     const float alpha_up = dual_gs ? a_gs[0] * b_gs[2 * e + 1] : alpha;
     // epilogue: lane holds column lr and rows 8*(v/4) + 4*lg + (v%4) of each 32x32 tile
+    if (EPI == kEpiSiluNvfp4 || !kPairStores) {
+      // one value per store (NVFP4 output: into the LDS tile); decode-height
+      // tiles keep this form, whose registers fit 4 resident workgroups per CU
 #pragma unroll
-    for (int i = 0; i < SUB_M; ++i) {
+      for (int i = 0; i < SUB_M; ++i) {
 #pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int row = r0 + i * 32 + 8 * (v >> 2) + 4 * lg + (v & 3);
-        if (row >= r_end) continue;
-        if (kSilu) {
+        for (int v = 0; v < 16; ++v) {
+          const int row = r0 + i * 32 + 8 * (v >> 2) + 4 * lg + (v & 3);
+          if (row >= r_end) continue;
+          if (kSilu) {
 #pragma unroll
-          for (int j = 0; j < SUB_N; j += 2) {
-            const int ch = wave * SUB_N + j;  // even chunk: gate, next chunk: up
-            const int lc = (ch >> 1) * 32 + lr, col = nt * (C::BN / 2) + lc;
-            if (col >= n_out) continue;
-            const float g = bf16_to_f32(f32_to_bf16(acc[i][j][v] * alpha));
-            const float u = bf16_to_f32(f32_to_bf16(acc[i][j + 1][v] * alpha_up));
-            const uint32_t h = f32_to_bf16(silu_f32(g) * u);
-            if (EPI == kEpiSiluNvfp4) {
-              h_tile[(row - r0) * (C::BN / 2) + lc] = (uint16_t)h;
-            } else {
-              d[(size_t)row * n_out + col] = (uint16_t)h;
-              amax_local = fmaxf(amax_local, fabsf(bf16_to_f32(h)));
+            for (int j = 0; j < SUB_N; j += 2) {
+              const int ch = wave * SUB_N + j;  // even chunk: gate, next chunk: up
+              const int lc = (ch >> 1) * 32 + lr, col = nt * (C::BN / 2) + lc;
+              if (col >= n_out) continue;
+              const uint32_t h = silu_mul_bf16(acc[i][j][v], acc[i][j + 1][v], alpha, alpha_up);
+              if (EPI == kEpiSiluNvfp4) {
+                h_tile[(row - r0) * (C::BN / 2) + lc] = (uint16_t)h;
+              } else {
+                d[(size_t)row * n_out + col] = (uint16_t)h;
+                amax_local = fmaxf(amax_local, fabsf(bf16_to_f32(h)));
+              }
+            }
+          } else {
+#pragma unroll
+            for (int j = 0; j < SUB_N; ++j) {
+              const int col = nt * C::BN + (wave * SUB_N + j) * 32 + lr;
+              if (col >= n_out) continue;
+              d[(size_t)row * n_out + col] = (uint16_t)f32_to_bf16(acc[i][j][v] * alpha);
             }
           }
-        } else {
+        }
+      }
+    } else {
+      // BF16 output, two rows at a time: rows (v, v + 1) of a lane's column
+      // become one BF16 pair, swapped with lane lr ^ 1 so that an even lane
+      // holds row v, columns (lr, lr + 1) and an odd lane row v + 1, columns
+      // (lr - 1, lr): one 4-byte store each. The store resource starts at
+      // the row tile's first row and ends at the group's last row, so rows
+      // past the group's end are dropped by the range check.
+      const int odd = lr & 1;
+      const uint32_t pair_sel = odd ? 0x03020706u : 0x05040100u;
+      const uint32_t row_bytes = (uint32_t)n_out * 2u;
+      const __amdgpu_buffer_rsrc_t rd =
+          make_rsrc(d + (size_t)r0 * n_out, (uint32_t)(r_end - r0) * row_bytes);
 #pragma unroll
-          for (int j = 0; j < SUB_N; ++j) {
-            const int col = nt * C::BN + (wave * SUB_N + j) * 32 + lr;
-            if (col >= n_out) continue;
-            d[(size_t)row * n_out + col] = (uint16_t)f32_to_bf16(acc[i][j][v] * alpha);
+      for (int j = 0; j < SUB_N; j += (kSilu ? 2 : 1)) {
+        const int ch = wave * SUB_N + j;  // with SiLU: even chunk gate, next chunk up
+        const int col0 = kSilu ? nt * (C::BN / 2) + (ch >> 1) * 32 : nt * C::BN + ch * 32;
+        if (col0 >= n_out) continue;  // the whole 32-column subtile is past N
+        const uint32_t lane_off = ((uint32_t)(4 * lg + odd) * (uint32_t)n_out + (uint32_t)(col0 + (lr & ~1))) * 2u;
+#pragma unroll
+        for (int i = 0; i < SUB_M; ++i) {
+#pragma unroll
+          for (int v = 0; v < 16; v += 2) {
+            uint32_t ha, hb;
+            if (kSilu) {
+              ha = silu_mul_bf16(acc[i][j][v], acc[i][j + 1][v], alpha, alpha_up);
+              hb = silu_mul_bf16(acc[i][j][v + 1], acc[i][j + 1][v + 1], alpha, alpha_up);
+              // rows past the group hold zeros (their activations read as zero)
+              amax_local = fmaxf(amax_local, fmaxf(fabsf(bf16_to_f32(ha)), fabsf(bf16_to_f32(hb))));
+            } else {
+              ha = f32_to_bf16(acc[i][j][v] * alpha);
+              hb = f32_to_bf16(acc[i][j][v + 1] * alpha);
+            }
+            const uint32_t p = ha | (hb << 16);
+            const uint32_t q = (uint32_t)__builtin_amdgcn_mov_dpp((int)p, 0xB1, 0xF, 0xF, false);  // lane lr ^ 1
+            const uint32_t row = (uint32_t)(i * 32 + 8 * (v >> 2) + (v & 3));
+            __builtin_amdgcn_raw_buffer_store_b32(__builtin_amdgcn_perm(q, p, pair_sel), rd, (int)lane_off,
+                                                  (int)(row * row_bytes), 0);
           }
         }
       }
