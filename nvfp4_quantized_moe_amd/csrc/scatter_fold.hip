@@ -17,7 +17,7 @@
 
 namespace nvfp4 {
 
-constexpr int kScatterBatch = 8;  // slot rows loaded together per 8-element chunk
+constexpr int kScatterChunks = 4;  // 8-element chunks per thread and round, their loads in flight together
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
 __global__ __launch_bounds__(256) void scatter_kernel(const uint16_t* __restrict__ y,
@@ -27,50 +27,68 @@ __global__ __launch_bounds__(256) void scatter_kernel(const uint16_t* __restrict
 #pragma clang fp contract(off)  // separate multiply and add roundings, in j order
   __shared__ int s_slot[64];
   __shared__ float s_w[64];
+  __shared__ int s_n;
   const int t = blockIdx.x;
-  if (threadIdx.x < k) {
-    s_slot[threadIdx.x] = token_slot[(size_t)t * k + threadIdx.x];
-    s_w[threadIdx.x] = topk_w[(size_t)t * k + threadIdx.x];
+  // the token's local slots, compacted in increasing j (lane j of wave 0
+  // takes entry j; its place is the number of local entries before it)
+  if (threadIdx.x < 64) {
+    const int j = threadIdx.x;
+    const int slot = j < k ? token_slot[(size_t)t * k + j] : -1;
+    const float w = j < k ? topk_w[(size_t)t * k + j] : 0.0f;
+    const uint64_t local = __ballot(slot >= 0);
+    if (slot >= 0) {
+      const int at = __popcll(local & ((1ull << j) - 1ull));
+      s_slot[at] = slot;
+      s_w[at] = w;
+    }
+    if (j == 0) s_n = __popcll(local);
   }
   __syncthreads();
-  // workgroup (t, y) takes every gridDim.y-th run of 256 8-element chunks of row t
+  const int n = s_n;
+  // workgroup (t, y) takes every gridDim.y-th run of 256 8-element chunks of
+  // row t; a thread's kScatterChunks chunks of a round lie one such step apart
   const int nchunk = H / 8;
-  for (int c = blockIdx.y * blockDim.x + threadIdx.x; c < nchunk; c += gridDim.y * blockDim.x) {
-    float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-    // up to 8 slots' loads in flight at once, then their adds in j order
-    for (int j0 = 0; j0 < k; j0 += kScatterBatch) {
-      uint4 v[kScatterBatch];
+  const int step = gridDim.y * blockDim.x;
+  for (int c0 = blockIdx.y * blockDim.x + threadIdx.x; c0 < nchunk; c0 += kScatterChunks * step) {
+    float acc[kScatterChunks][8];
 #pragma unroll
-      for (int jj = 0; jj < kScatterBatch; ++jj) {
-        const int j = j0 + jj;
-        const int s = j < k ? s_slot[j] : -1;
-        v[jj] = s >= 0 ? *reinterpret_cast<const uint4*>(y + (size_t)s * H + c * 8) : make_uint4(0, 0, 0, 0);
+    for (int g = 0; g < kScatterChunks; ++g)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[g][e] = 0.0f;
+    for (int jj = 0; jj < n; ++jj) {
+      const uint16_t* row = y + (size_t)s_slot[jj] * H;
+      const float w = s_w[jj];
+      uint4 v[kScatterChunks];
+#pragma unroll
+      for (int g = 0; g < kScatterChunks; ++g) {
+        const int c = c0 + g * step;
+        v[g] = c < nchunk ? *reinterpret_cast<const uint4*>(row + c * 8) : make_uint4(0, 0, 0, 0);
       }
 #pragma unroll
-      for (int jj = 0; jj < kScatterBatch; ++jj) {
-        const int j = j0 + jj;
-        if (j >= k || s_slot[j] < 0) continue;
-        const float w = s_w[j];
-        const uint32_t u[4] = {v[jj].x, v[jj].y, v[jj].z, v[jj].w};
+      for (int g = 0; g < kScatterChunks; ++g) {
+        const uint32_t u[4] = {v[g].x, v[g].y, v[g].z, v[g].w};
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
           const float p0 = w * bf16_to_f32(u[q] & 0xFFFFu);
           const float p1 = w * bf16_to_f32(u[q] >> 16);
-          acc[2 * q] = acc[2 * q] + p0;
-          acc[2 * q + 1] = acc[2 * q + 1] + p1;
+          acc[g][2 * q] = acc[g][2 * q] + p0;
+          acc[g][2 * q + 1] = acc[g][2 * q + 1] + p1;
         }
       }
     }
-    uint4 o;
-    o.x = f32_to_bf16(acc[0]) | (f32_to_bf16(acc[1]) << 16);
-    o.y = f32_to_bf16(acc[2]) | (f32_to_bf16(acc[3]) << 16);
-    o.z = f32_to_bf16(acc[4]) | (f32_to_bf16(acc[5]) << 16);
-    o.w = f32_to_bf16(acc[6]) | (f32_to_bf16(acc[7]) << 16);
-    // non-temporal: the output is not read again in the layer, and its lines
-    // would otherwise be written back from the caches during the next
-    // launches (the next layer step's amax pass ran 7 us longer for it)
-    const u32x4_t ov = {o.x, o.y, o.z, o.w};
-    __builtin_nontemporal_store(ov, reinterpret_cast<u32x4_t*>(out + (size_t)t * H + c * 8));
+#pragma unroll
+    for (int g = 0; g < kScatterChunks; ++g) {
+      const int c = c0 + g * step;
+      if (c >= nchunk) continue;
+      const u32x4_t ov = {f32_to_bf16(acc[g][0]) | (f32_to_bf16(acc[g][1]) << 16),
+                          f32_to_bf16(acc[g][2]) | (f32_to_bf16(acc[g][3]) << 16),
+                          f32_to_bf16(acc[g][4]) | (f32_to_bf16(acc[g][5]) << 16),
+                          f32_to_bf16(acc[g][6]) | (f32_to_bf16(acc[g][7]) << 16)};
+      // non-temporal: the output is not read again in the layer, and its
+      // lines would otherwise be written back from the caches during the next
+      // launches (the next layer step's amax pass ran 7 us longer for it)
+      __builtin_nontemporal_store(ov, reinterpret_cast<u32x4_t*>(out + (size_t)t * H + c * 8));
+    }
   }
 }
 
