@@ -22,10 +22,19 @@ constexpr int kXcds = 8;  // MI355X: 8 accelerator complex dies, one L2 each
 
 __device__ __forceinline__ float bf16_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
 
-// float32 -> BF16, nearest with ties to even (inputs are finite)
+// float32 -> BF16 bits, nearest with ties to even (inputs are finite): the
+// gfx950 conversion v_cvt_pk_bf16_f32, which equals the bit construction
+// (u + 0x7FFF + bit 16 of u) >> 16 on every finite float32 (all 2^32
+// patterns compared on MI355X)
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float float2_t __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ uint32_t f32_to_bf16(float f) {
-  uint32_t u = __float_as_uint(f);
-  return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+  return __builtin_bit_cast(uint16_t, (__bf16)f);
+}
+// two float32 -> a BF16 pair (a in the low half), one instruction
+__device__ __forceinline__ uint32_t f32x2_to_bf16x2(float a, float b) {
+  const float2_t v = {a, b};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
 }
 
 // Exact value of an E4M3 code (non-NaN) as float32.

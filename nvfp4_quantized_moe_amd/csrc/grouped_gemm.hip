@@ -135,8 +135,8 @@ __device__ __forceinline__ float silu_f32(float g) { return g * __builtin_amdgcn
 
 // h = BF16(SiLU(g) * u) with g = BF16(acc_gate * alpha) and u = BF16(acc_up * alpha_up), as BF16 bits
 __device__ __forceinline__ uint32_t silu_mul_bf16(float acc_gate, float acc_up, float alpha, float alpha_up) {
-  const float g = bf16_to_f32(f32_to_bf16(acc_gate * alpha));
-  const float u = bf16_to_f32(f32_to_bf16(acc_up * alpha_up));
+  const uint32_t gu = f32x2_to_bf16x2(acc_gate * alpha, acc_up * alpha_up);
+  const float g = __uint_as_float(gu << 16), u = __uint_as_float(gu & 0xFFFF0000u);
   return f32_to_bf16(silu_f32(g) * u);
 }
 
@@ -507,17 +507,16 @@ __global__ __launch_bounds__(64 * WAVES) void grouped_gemm_kernel(
         for (int i = 0; i < SUB_M; ++i) {
 #pragma unroll
           for (int v = 0; v < 16; v += 2) {
-            uint32_t ha, hb;
+            uint32_t p;
             if (kSilu) {
-              ha = silu_mul_bf16(acc[i][j][v], acc[i][j + 1][v], alpha, alpha_up);
-              hb = silu_mul_bf16(acc[i][j][v + 1], acc[i][j + 1][v + 1], alpha, alpha_up);
+              const uint32_t ha = silu_mul_bf16(acc[i][j][v], acc[i][j + 1][v], alpha, alpha_up);
+              const uint32_t hb = silu_mul_bf16(acc[i][j][v + 1], acc[i][j + 1][v + 1], alpha, alpha_up);
               // rows past the group hold zeros (their activations read as zero)
               amax_local = fmaxf(amax_local, fmaxf(fabsf(bf16_to_f32(ha)), fabsf(bf16_to_f32(hb))));
+              p = ha | (hb << 16);
             } else {
-              ha = f32_to_bf16(acc[i][j][v] * alpha);
-              hb = f32_to_bf16(acc[i][j][v + 1] * alpha);
+              p = f32x2_to_bf16x2(acc[i][j][v] * alpha, acc[i][j][v + 1] * alpha);
             }
-            const uint32_t p = ha | (hb << 16);
             const uint32_t q = (uint32_t)__builtin_amdgcn_mov_dpp((int)p, 0xB1, 0xF, 0xF, false);  // lane lr ^ 1
             const uint32_t row = (uint32_t)(i * 32 + 8 * (v >> 2) + (v & 3));
             __builtin_amdgcn_raw_buffer_store_b32(__builtin_amdgcn_perm(q, p, pair_sel), rd, (int)lane_off,

@@ -80,10 +80,8 @@ __global__ __launch_bounds__(256) void scatter_kernel(const uint16_t* __restrict
     for (int g = 0; g < kScatterChunks; ++g) {
       const int c = c0 + g * step;
       if (c >= nchunk) continue;
-      const u32x4_t ov = {f32_to_bf16(acc[g][0]) | (f32_to_bf16(acc[g][1]) << 16),
-                          f32_to_bf16(acc[g][2]) | (f32_to_bf16(acc[g][3]) << 16),
-                          f32_to_bf16(acc[g][4]) | (f32_to_bf16(acc[g][5]) << 16),
-                          f32_to_bf16(acc[g][6]) | (f32_to_bf16(acc[g][7]) << 16)};
+      const u32x4_t ov = {f32x2_to_bf16x2(acc[g][0], acc[g][1]), f32x2_to_bf16x2(acc[g][2], acc[g][3]),
+                          f32x2_to_bf16x2(acc[g][4], acc[g][5]), f32x2_to_bf16x2(acc[g][6], acc[g][7])};
       // non-temporal: the output is not read again in the layer, and its
       // lines would otherwise be written back from the caches during the next
       // launches (the next layer step's amax pass ran 7 us longer for it)
