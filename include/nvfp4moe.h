@@ -192,8 +192,8 @@ int nvfp4_pack_weights(const uint8_t* q, const uint8_t* sf, int64_t B, int64_t N
  *   = (gs_gate, gs_up) and the gate columns take alpha = RN_f32(a_gs[0] * b_gs[e][0]), the up
  *   columns RN_f32(a_gs[0] * b_gs[e][1]) (the alpha commit's global-scale treatment applied to
  *   each half, instead of the finalize_weights fold).
- * Activation row indices must satisfy (row + 1) * K/2 < 2^31, as must rows_cap * K/2
- * and N * K * 9/16 (32-bit buffer offsets).
+ * Activation row indices must satisfy (row + 1) * K/2 < 2^31, as must rows_cap * K/2,
+ * N * K * 9/16 and 256 * N (32-bit buffer offsets); NVFP4_ERR_SHAPE otherwise.
  * Only rows of listed tiles are written. Requires K % 128 == 0, N % 64 == 0
  * (N % 128 == 0 for NVFP4_EPI_SILU_MUL), 1 <= L, tile_m 32 (decode-shaped
  * batches), 64, 96 (prefill-shaped) or 128 (large groups).

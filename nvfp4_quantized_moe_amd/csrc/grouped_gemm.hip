@@ -690,8 +690,10 @@ extern "C" int nvfp4_grouped_gemm(const uint8_t* a_q, const uint8_t* a_sf, const
   if (silu && !amax_out) return NVFP4_ERR_NULL;
   if (!nvfp4_aligned16(a_q) || !nvfp4_aligned16(a_sf) || !nvfp4_aligned16(b_packed) || !nvfp4_aligned16(d))
     return NVFP4_ERR_ALIGN;
-  // buffer offsets are 32-bit: activation row offsets and one expert's packed weights stay below 2^31
+  // buffer offsets are 32-bit: activation row offsets, one expert's packed weights and one row tile of the
+  // output (at most 128 rows) stay below 2^31
   if ((int64_t)rows_cap * (K / 2) >= (1ll << 31) || (int64_t)N * K / 32 * 18 >= (1ll << 31)) return NVFP4_ERR_SHAPE;
+  if ((int64_t)N * 2 * 128 >= (1ll << 31)) return NVFP4_ERR_SHAPE;
   if (rows_cap == 0) return NVFP4_OK;
   return nvfp4_launch_grouped_gemm(a_q, a_sf, a_row_index, a_gs, b_packed, b_gs, offsets, tile_table, num_local,
                                    rows_cap, N, K, tile_m, epilogue, d, amax_out, (hipStream_t)stream);

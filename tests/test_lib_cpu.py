@@ -79,6 +79,7 @@ def test_invalid_arguments_are_rejected_before_launch():
     assert nv._gemm(*g, 8, 64, 256, 256, 32, 2, buf, null, s) == 1   # dual-scale SiLU also needs amax_out
     assert nv._gemm(*g, 8, 64, 256, 256, 48, 0, buf, null, s) == 2
     assert nv._gemm(*g, 8, 64, 256, 256, 32, 1, buf, null, s) == 1   # SiLU epilogue needs amax_out
+    assert nv._gemm(*g, 8, 64, 1 << 23, 128, 96, 0, buf, null, s) == 2  # a 128-row output tile past 2^31 bytes
     # packed size / pack: N not a multiple of 32, K not a multiple of 128, NULL input, misaligned output
     assert nv.nvfp4_packed_bytes(2, 64, 256) == 2 * 64 * 256 * 9 // 16
     assert nv.nvfp4_packed_bytes(1, 48, 256) == -1 and nv.nvfp4_packed_bytes(1, 64, 192) == -1
