@@ -258,7 +258,7 @@ int nvfp4_fold_scales(uint8_t* w1_sf, const float* gs_gate, const float* gs_up, 
  * out_bf16 [T, H] (tokens with no local expert get zeros).
  * ws: at least nvfp4_moe_ws_bytes(...) bytes; its regions (nvfp4_moe_ws_layout)
  * hold the intermediates after the call. Requires H % 128 == 0, I % 128 == 0,
- * T*k < 2^30, and T*H/2, T*k*I/2 and 2I*H*9/16 below 2^31.
+ * T*k < 2^30, and T*H/2, T*k*I/2, 2I*H*9/16, 512*I and 256*H below 2^31.
  */
 typedef struct {
   int32_t num_local, hidden, inter;

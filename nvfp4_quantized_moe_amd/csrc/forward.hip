@@ -82,9 +82,10 @@ static int check_forward_args(const nvfp4_moe_weights* w, const void* x_bf16, in
   if (T < 0 || k < 1 || k > 64 || L < 1 || L > 4096 || H <= 0 || I <= 0) return NVFP4_ERR_SHAPE;
   if (H % 128 != 0 || I % 128 != 0) return NVFP4_ERR_SHAPE;
   if ((int64_t)T * k >= (1ll << 30)) return NVFP4_ERR_SHAPE;
-  // the GEMMs address one expert's packed weights and the activation rows with 32-bit offsets
+  // the GEMMs address one expert's packed weights, the activation rows and one output row tile with 32-bit offsets
   if ((int64_t)2 * I * H / 32 * 18 >= (1ll << 31) || (int64_t)T * (H / 2) >= (1ll << 31) ||
-      (int64_t)T * k * (I / 2) >= (1ll << 31))
+      (int64_t)T * k * (I / 2) >= (1ll << 31) || (int64_t)2 * I * 256 >= (1ll << 31) ||
+      (int64_t)H * 256 >= (1ll << 31))
     return NVFP4_ERR_SHAPE;
   if (w->w1_dual_gs != 0 && w->w1_dual_gs != 1) return NVFP4_ERR_ARG;
   if (!w->w1 || !w->w1_gs || !w->w2 || !w->w2_gs || !ws) return NVFP4_ERR_NULL;

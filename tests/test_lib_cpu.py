@@ -108,6 +108,8 @@ def test_invalid_arguments_are_rejected_before_launch():
     assert nv._forward(ctypes.byref(big), buf, 1 << 27, buf, buf, 8, 96, buf, buf, 1 << 62, s) == 2   # T*k = 2^30
     huge = nv._Weights(8, 65536, 32768, 4096, 4096, 4096, 4096)                                  # 2I*H*9/16 >= 2^31
     assert nv._forward(ctypes.byref(huge), buf, 4, buf, buf, 2, 0, buf, buf, 1 << 62, s) == 2
+    wide = nv._Weights(8, 1 << 23, 128, 4096, 4096, 4096, 4096)                                  # 256*H = 2^31
+    assert nv._forward(ctypes.byref(wide), buf, 1, buf, buf, 1, 0, buf, buf, 1 << 62, s) == 2
     w = nv._Weights(8, 256, 128, 4096, 4096, 4096, 4096, 2)     # unknown gate/up scale mode
     assert nv._forward(ctypes.byref(w), buf, 4, buf, buf, 2, 0, buf, buf, 1 << 30, s) == 6
     # quantize without a workspace: more tensors than its array holds, bad K, NULL gs
