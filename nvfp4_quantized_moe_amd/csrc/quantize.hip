@@ -12,7 +12,7 @@
 // Kernels: amax (wave reductions, one partial maximum per workgroup on the
 // float bits, order-free) and quantize (each workgroup reduces the partials,
 // derives gs and builds the threshold table in LDS, then quantizes 16-element
-// blocks, one per thread, grid-stride over the tensor). With amax given (the
+// blocks, two per thread and round, grid-stride over the tensor). With amax given (the
 // h path) or with a fixed global scale (nvfp4_cutedsl.py history, static-scale
 // commit: gs measured once at warmup, then no max reduction) only the
 // quantize kernel runs.
