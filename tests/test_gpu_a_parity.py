@@ -158,7 +158,8 @@ def test_fold_bit_exact(nv):
 
 # ------------------------------------------------------------------- scatter
 
-@pytest.mark.parametrize("T,k,H", [(37, 3, 256), (5, 8, 7168), (64, 1, 64)])
+@pytest.mark.parametrize("T,k,H", [(37, 3, 256), (5, 8, 7168), (64, 1, 64), (6, 64, 512), (33, 8, 8320),
+                                   (2048, 8, 7168)])
 def test_scatter_bit_exact(nv, T, k, H):
     rng = np.random.default_rng(T * 131 + k)
     S = int(T * k * 0.6)
