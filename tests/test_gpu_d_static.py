@@ -70,6 +70,28 @@ def test_quantize_static_bit_exact(nv, case, factor):
     assert np.array_equal(q.cpu().numpy(), oq)
 
 
+@pytest.mark.parametrize("x_exp,gs", [
+    (-57, 2.0 ** -60), (-57, float(np.nextafter(np.float32(2.0 ** -60), np.float32(0)))), (-57, 2.0 ** -61),
+    (63, 2.0 ** 60), (63, float(np.nextafter(np.float32(2.0 ** 60), np.float32(np.inf)))), (63, 2.0 ** 61),
+    (0, 1e-25), (0, 1e25), (-130, 2.0 ** -135)])
+def test_quantize_static_extreme_scales(nv, x_exp, gs):
+    # global scales at and past the ends of the range where the block scale
+    # code comes from the float32 estimate (the others take the float64
+    # quotient), on inputs scaled to give codes across the E4M3 range; also
+    # every block saturated (1e-25), every block zero (1e25) and BF16
+    # subnormal inputs with a float32 subnormal scale
+    rng = np.random.default_rng(abs(x_exp) + 7)
+    x = (rng.standard_normal((24, 256)) * np.exp2(np.float64(x_exp))).astype(np.float32)
+    xb = W.bf16_bits(x)
+    g = np.float32(gs)
+    log(f"quantize_static extreme gs={float(g):.3e} x_exp={x_exp}")
+    q, sf = nv.nvfp4_quantize_static(to_bf16(xb), to_dev(np.array([g], np.float32)))
+    torch.cuda.synchronize()
+    oq, osf, _ = O.quantize(xb, gs=g)
+    assert np.array_equal(sf.cpu().numpy(), osf)
+    assert np.array_equal(q.cpu().numpy(), oq)
+
+
 def test_quantize_static_batched_and_zero_scale(nv):
     rng = np.random.default_rng(15)
     x = (rng.standard_normal((3, 40, 256)) * np.array([1.0, 300.0, 1e-3])[:, None, None]).astype(np.float32)
