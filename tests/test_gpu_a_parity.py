@@ -71,6 +71,23 @@ def test_quantize_bit_exact(nv, case):
     record(f"quantize:{case}", bit_exact_arrays=3)
 
 
+@pytest.mark.parametrize("x_exp", [-100, -52, -50, 70, -128])
+def test_quantize_tiny_and_huge_tensors(nv, x_exp):
+    # tensors whose own global scale amax/2688 lies outside [2^-60, 2^60] (the
+    # block scale codes then come from the float64 quotient: 2^-100, 2^-52,
+    # 2^70, and BF16 subnormals at 2^-128) or just inside it (2^-50)
+    rng = np.random.default_rng(x_exp + 200)
+    x = (rng.standard_normal((32, 512)) * np.exp2(np.float64(x_exp))).astype(np.float32)
+    xb = W.bf16_bits(x)
+    log(f"quantize scaled by 2^{x_exp}")
+    q, sf, gs = nv.nvfp4_quantize(to_bf16(xb))
+    torch.cuda.synchronize()
+    oq, osf, ogs = O.quantize(xb)
+    assert gs.cpu().numpy()[0] == ogs
+    assert np.array_equal(sf.cpu().numpy(), osf)
+    assert np.array_equal(q.cpu().numpy(), oq)
+
+
 def test_quantize_batched_and_amax_in(nv):
     rng = np.random.default_rng(5)
     x = (rng.standard_normal((3, 40, 256)) * np.array([1.0, 300.0, 1e-3])[:, None, None]).astype(np.float32)
