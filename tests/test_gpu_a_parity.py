@@ -439,6 +439,33 @@ def test_layer_duplicate_ids_in_a_token(nv):
     assert rel_err(got, ref) <= TOL
 
 
+def test_layers_on_two_streams(nv):
+    """Two different layers (their own weights, inputs and workspaces) issued
+    alternately on two streams with no synchronization between them: each
+    call's output equals that layer's output computed alone, bit for bit (the
+    library keeps no state between calls besides the caller's buffers)."""
+    runs = []
+    for name in ("mid", "mid_skew"):
+        cfg, ids, w, x, wg, wu, wd = _layer_inputs(name)
+        weights = nv.prepare_weights(to_bf16(wg), to_bf16(wu), to_bf16(wd))
+        args = (weights, to_bf16(x), to_dev(ids), to_dev(w), cfg.expert_start)
+        alone = nv.nvfp4_moe_forward(*args)
+        torch.cuda.synchronize()
+        runs.append((args, bits_of(alone)))
+    log("layers mid and mid_skew on two streams, 4 calls each")
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    outs = [[], []]
+    torch.cuda.synchronize()
+    for _ in range(4):
+        for i, (args, _) in enumerate(runs):
+            with torch.cuda.stream(streams[i]):
+                outs[i].append(nv.nvfp4_moe_forward(*args))
+    torch.cuda.synchronize()
+    for i, (_, ref) in enumerate(runs):
+        for o in outs[i]:
+            assert np.array_equal(bits_of(o), ref), i
+
+
 # ------------------------------------------------------- binding validation
 
 def test_binding_rejects_bad_buffers(nv):
