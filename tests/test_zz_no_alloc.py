@@ -2,7 +2,9 @@
 workspace (its amax partials in the library's own device array) gives the
 same q, sf and gs as nvfp4_quantize with a workspace, bit for bit, on two
 calls in a row (the second on a smaller input, after the first left its
-partials in the array), and it rejects more tensors than the array holds.
+partials in the array), and it rejects more tensors than the array holds;
+captured in a HIP graph, every replay equals the eager call, also with
+other no-alloc calls (which overwrite the array) between the replays.
 Collected last so that a failure here hides no other test."""
 import numpy as np
 import pytest
@@ -84,3 +86,34 @@ def test_noalloc_amax_in_and_limits(nv):
     nv.nvfp4_quantize_noalloc(big[:128], q[:128], sf[:128], gs[:128])
     torch.cuda.synchronize()
     assert not gs[:128].any().item() and not sf[:128].any().item()
+
+
+def test_noalloc_graph_replay(nv):
+    rng = np.random.default_rng(79)
+    bits = quant_case("t3_outliers")[None]                                      # [1, 256, 1024]
+    other = W.bf16_bits(rng.standard_normal((2, 64, 512)).astype(np.float32) * 40.0)
+    x, xo = _bf16(bits), _bf16(other)
+    q, sf, gs = _outputs(*bits.shape)
+    qo, sfo, gso = _outputs(*other.shape)
+    nv.nvfp4_quantize_noalloc(x, q, sf, gs)                   # eager reference (and the device array's set-up)
+    torch.cuda.synchronize()
+    ref = (q.clone(), sf.clone(), gs.clone())
+    log("capture nvfp4_quantize_noalloc in a graph")
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            nv.nvfp4_quantize_noalloc(x, q, sf, gs)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    for r in range(3):
+        q.fill_(0x5A)
+        sf.fill_(0x5A)
+        gs.fill_(-1.0)
+        nv.nvfp4_quantize_noalloc(xo, qo, sfo, gso)            # another call: new partials in the array
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(gs, ref[2]) and torch.equal(sf, ref[1]) and torch.equal(q, ref[0]), r
+    oq, osf, ogs = O.quantize(bits[0])
+    assert gs[0].item() == ogs and np.array_equal(q[0].cpu().numpy(), oq)
