@@ -466,6 +466,32 @@ def test_layers_on_two_streams(nv):
             assert np.array_equal(bits_of(o), ref), i
 
 
+@pytest.mark.parametrize("name", ["tiny", "mid_route3", "long_k1"])
+def test_layer_with_stage_events(nv, name):
+    """nvfp4_moe_forward_stage_events (the layer with events between its
+    launches, for timing) gives the plain call's output bit for bit; its events
+    are recorded in stage order (every span >= 0), with some of them left out
+    too."""
+    cfg, ids, w, x, wg, wu, wd = _layer_inputs(name)
+    weights = nv.prepare_weights(to_bf16(wg), to_bf16(wu), to_bf16(wd))
+    args = (weights, to_bf16(x), to_dev(ids), to_dev(w), cfg.expert_start)
+    ref = nv.nvfp4_moe_forward(*args)
+    torch.cuda.synchronize()
+    log(f"layer {name} with stage events")
+    for skip in ((), (2, 5)):
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(len(nv.STAGES) + 1)]
+        for e in ev:
+            e.record()
+        torch.cuda.synchronize()
+        events = [None if i in skip else e for i, e in enumerate(ev)]
+        out = nv.nvfp4_moe_forward_stage_events(*args, events)
+        torch.cuda.synchronize()
+        assert np.array_equal(bits_of(out), bits_of(ref))
+        kept = [e for e in events if e is not None]
+        for a, b in zip(kept, kept[1:]):
+            assert a.elapsed_time(b) >= 0.0
+
+
 # ------------------------------------------------------- binding validation
 
 def test_binding_rejects_bad_buffers(nv):
