@@ -1,10 +1,14 @@
-"""The quantizer's exact E2M1 rounding (two elements per 32-bit add, index
-read from the thermometer code of the seven midpoint tests) against plain
-counting of the thresholds passed, compiled for the host and run on the CPU:
-every low-half BF16 value against random non-decreasing threshold sets,
-including thresholds at and past the largest finite magnitude and the
-nothing-passes table of scale code 0; also the block maximum and the byte
-packing. No GPU is needed and no kernel is launched."""
+"""The quantizer's exact roundings (quant_block.h), compiled for the host and
+run on the CPU: the E2M1 index (two elements per 32-bit add, a three-test
+binary search, byte-permute packing) against plain counting of the thresholds
+passed, every BF16 value in every position of eight against random
+non-decreasing threshold sets, including thresholds at and past the largest
+finite magnitude and the nothing-passes table of scale code 0; the block
+maximum; the block scale code (a float32 estimate settled by two table tests)
+against counts of exact float64 midpoint comparisons for every finite block
+maximum at fixed, random and tie-making global scales; the threshold table's
+16-bit entries; and the threshold round-down against the float64 route. No
+GPU is needed and no kernel is launched."""
 import os
 import shutil
 import subprocess
